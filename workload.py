@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the W4A16 decode GEMV.
+
+This module is shared by the oracle side (tests, CPU baseline) and the HIP side
+(tests, bench, smoke). It holds only random draws and shapes: no dequantisation,
+no dot products, no packing. Everything the method computes lives elsewhere.
+
+Recipe (per GEMV, all draws from numpy's PCG64 keyed by
+``SeedSequence(ROOT_SEED, spawn_key=(workload, layer, projection, tensor))``):
+
+* codes: uniform random bytes ``uint8[N, K/2]``; a byte is two independent
+  uniform 4-bit codes (low nibble = even k, high nibble = odd k).
+* scale: uniform on [0.001, 0.01] in float64, rounded to IEEE binary16.
+* min:   uniform on [-0.08, 0] in float64, rounded to IEEE binary16.
+* x:     standard normal in float64; for the "outlier" workloads exactly
+  ``round(0.001 * K)`` distinct positions per activation row (uniform, without
+  replacement) are multiplied by 20; then rounded to binary16.
+
+Layer shapes are the public Llama-3-8B and Llama-3-70B decoder projections with
+the query/key/value and gate/up matrices fused, the fusion the core-modules
+page lists among the packer's operator rewrites (section 5.1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+ROOT_SEED = 0x57A4A16
+GROUP = 32
+
+# tensor ids inside a seed key
+_T_CODES, _T_SCALE, _T_MIN, _T_X, _T_OUTLIER = range(5)
+
+
+@dataclass(frozen=True)
+class Proj:
+    name: str
+    K: int  # input features (reduction length)
+    N: int  # output features (rows of the weight matrix)
+
+
+LLAMA8B_LAYER = (
+    Proj("qkv", 4096, 6144),
+    Proj("o", 4096, 4096),
+    Proj("gate_up", 4096, 28672),
+    Proj("down", 14336, 4096),
+)
+
+LLAMA70B_LAYER = (
+    Proj("qkv", 8192, 10240),
+    Proj("o", 8192, 8192),
+    Proj("gate_up", 8192, 57344),
+    Proj("down", 28672, 8192),
+)
+
+
+@dataclass(frozen=True)
+class Workload:
+    wid: int             # numeric id used in the seed key
+    name: str
+    layers: int
+    shapes: tuple        # tuple[Proj, ...] per layer
+    ms: tuple            # activation-row counts M exercised
+    outliers: bool       # 0.1 % x20 activation outliers
+
+
+WORKLOADS = {
+    # single 4096 x 4096 GEMV, M = 1, plain N(0,1) activations
+    "gemv4096": Workload(0, "gemv4096", 1, (Proj("square", 4096, 4096),), (1,), False),
+    # one Llama-3-8B-shaped decoder layer at M = 1, with activation outliers
+    "llama8b_layer": Workload(1, "llama8b_layer", 1, LLAMA8B_LAYER, (1,), True),
+    # 32 such layers with independent weights: one decode step, M = 1
+    "llama8b_step": Workload(2, "llama8b_step", 32, LLAMA8B_LAYER, (1,), True),
+    # speculative-verify batches on the 8B layer shapes, M = 4 and M = 8
+    "llama8b_verify": Workload(3, "llama8b_verify", 1, LLAMA8B_LAYER, (4, 8), False),
+    # 80 Llama-3-70B-shaped layers, M = 1 and M = 8, with activation outliers
+    "llama70b_step": Workload(4, "llama70b_step", 80, LLAMA70B_LAYER, (1, 8), True),
+}
+
+
+def _rng(wid: int, layer: int, proj: int, tensor: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(ROOT_SEED, spawn_key=(wid, layer, proj, tensor))
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def n_outliers(K: int) -> int:
+    """Outlier positions per activation row: round(0.001 * K)."""
+    return int(round(0.001 * K))
+
+
+def weights(wid: int, layer: int, proj: int, N: int, K: int):
+    """Seeded codes uint8[N, K/2], scale and min float16[N, K/32]."""
+    if K % GROUP or K <= 0 or N <= 0:
+        raise ValueError(f"bad shape N={N} K={K}")
+    codes = _rng(wid, layer, proj, _T_CODES).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scale = _rng(wid, layer, proj, _T_SCALE).uniform(0.001, 0.01, size=(N, K // GROUP)).astype(np.float16)
+    mn = _rng(wid, layer, proj, _T_MIN).uniform(-0.08, 0.0, size=(N, K // GROUP)).astype(np.float16)
+    return codes, scale, mn
+
+
+def activations(wid: int, layer: int, proj: int, M: int, K: int, outliers: bool) -> np.ndarray:
+    """Seeded x float16[M, K]: N(0,1), optionally with round(0.001 K) x20 outliers per row."""
+    x = _rng(wid, layer, proj, _T_X).standard_normal(size=(M, K))
+    if outliers:
+        r = _rng(wid, layer, proj, _T_OUTLIER)
+        cnt = n_outliers(K)
+        for m in range(M):
+            pos = r.choice(K, size=cnt, replace=False)
+            x[m, pos] *= 20.0
+    return x.astype(np.float16)
+
+
+def workload_gemvs(name: str, M: int | None = None):
+    """Yield (layer, proj_index, Proj, M) for every GEMV of a named workload."""
+    w = WORKLOADS[name]
+    ms = w.ms if M is None else (M,)
+    for m in ms:
+        for layer in range(w.layers):
+            for pi, p in enumerate(w.shapes):
+                yield layer, pi, p, m
+
+
+def gemv_inputs(name: str, layer: int, proj: int, M: int):
+    """All seeded inputs of one GEMV of a named workload: (x, codes, scale, min)."""
+    w = WORKLOADS[name]
+    p = w.shapes[proj]
+    codes, scale, mn = weights(w.wid, layer, proj, p.N, p.K)
+    # x seeds also depend on M so that the M = 4 and M = 8 batches are distinct
+    x = activations(w.wid, layer, proj + 16 * M, M, p.K, w.outliers)
+    return x, codes, scale, mn
+
+
+def random_problem(seed: int, M: int, N: int, K: int, outliers: bool = False):
+    """Seeded inputs for an arbitrary (M, N, K), used by edge-shape tests."""
+    codes, scale, mn = weights(1000 + seed, 0, 0, N, K)
+    x = activations(1000 + seed, 0, 0, M, K, outliers)
+    return x, codes, scale, mn
