@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Decode-step bench of the W4A16 GEMV on one MI355X.
+
+One step = the 128 GEMVs of 32 Llama-3-8B-shaped decoder layers at M = 1
+(fused QKV 4096->6144, O 4096->4096, fused gate-up 4096->28672, down
+14336->4096), each with its own seeded 4-bit group-32 weights, all resident in
+HBM (4.37 GB packed). The step is launched in stream order, the way a decode
+loop runs it (each GEMV starts after the previous one ends), captured once into
+a HIP graph and replayed.
+
+Printed: one JSON line with the whole-step throughput in algorithmic GB/s
+(N*K/2 code bytes + 4 bytes of scale/min per 32 weights + x + y, per GEMV),
+the roofline entry of the dominant kernel (event-timed per launch on the
+launch stream) and the fp64 oracle timed on this host's cores as a reported
+CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workload  # noqa: E402
+
+METRIC = "W4A16 decode GEMV µs/step and effective HBM GB/s (% of peak), 8B shapes"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "llama8b_step"
+
+
+def gemv_bytes(M, N, K):
+    return N * K // 2 + 4 * N * (K // 32) + 2 * M * K + 4 * M * N
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_inputs(torch, w4, M, dev, threads):
+    """Generate, pack and upload every GEMV of the step; returns a list of dicts."""
+    items = list(workload.workload_gemvs(WORKLOAD, M))
+
+    def make(item):
+        layer, pi, p, m = item
+        x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, layer, pi, m)
+        blob = w4.w4a16_pack(codes, scale, mn)
+        return item, x, blob
+
+    out = []
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for (layer, pi, p, m), x, blob in ex.map(make, items):
+            packed = w4.upload_packed(blob, dev)
+            xd = torch.from_numpy(x).to(dev)
+            y = torch.zeros((m, p.N), dtype=torch.float32, device=dev)
+            out.append(dict(layer=layer, proj=pi, name=p.name, M=m, N=p.N, K=p.K, x=xd, packed=packed, y=y,
+                            bytes=gemv_bytes(m, p.N, p.K),
+                            kernel=w4.w4a16_launch_shape(m, p.N, p.K)["kernel"]))
+            del blob
+    return out
+
+
+def launch_step(w4, gemvs, stream_handle):
+    for g in gemvs:
+        st = w4.w4a16_gemv_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], stream_handle)
+        if st != 0:
+            raise w4.W4A16Error(st, "w4a16_gemv")
+
+
+def spot_check(w4, gemvs, torch):
+    """Sampled rows of two GEMVs of the step against the oracle (sanity only)."""
+    import oracle
+
+    for g in (gemvs[2], gemvs[3]):
+        x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, g["layer"], g["proj"], g["M"])
+        rows = np.arange(0, g["N"], max(1, g["N"] // 64))
+        y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
+        y = g["y"].cpu().numpy()[:, rows].astype(np.float64)
+        if not oracle.within_tolerance(y, y_ref, B).all():
+            raise AssertionError(f"bench spot check failed on {g['name']} layer {g['layer']}")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle on whole GEMVs of the same step until ~budget_s of work."""
+    import threadpoolctl
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    done_bytes = 0
+    done = []
+    t_total = 0.0
+    with threadpoolctl.threadpool_limits(1):
+        for layer, pi, p, m in workload.workload_gemvs(WORKLOAD, 1):
+            x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, layer, pi, m)
+            t0 = time.perf_counter()
+            oracle.gemv(x, codes, scale, mn, threads=threads)
+            t_total += time.perf_counter() - t0
+            done_bytes += gemv_bytes(m, p.N, p.K)
+            done.append(f"L{layer}.{p.name}")
+            if t_total >= budget_s:
+                break
+    return {
+        "value": round(done_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 oracle on {len(done)} of the step's 128 GEMVs ({', '.join(done)}), "
+                  f"{done_bytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, "
+                  f"{threads} worker threads, BLAS threads limited to 1",
+        "us_per_step_extrapolated": round(t_total / done_bytes * sum(
+            gemv_bytes(m, p.N, p.K) for _, _, p, m in workload.workload_gemvs(WORKLOAD, 1)) * 1e6, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the W4A16 GEMV path has no multi-GPU code "
+              "(a sharded run would split N across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_quantized_w4a16_amd as w4
+
+    if not os.path.exists(w4.LIB_PATH):
+        from bit_weight_quantized_w4a16_amd import _build
+        _build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M = 1
+
+    t0 = time.time()
+    gemvs = build_inputs(torch, w4, M, dev, threads=min(16, len(os.sched_getaffinity(0))))
+    torch.cuda.synchronize()
+    for g in gemvs:
+        g["xp"], g["pp"], g["yp"] = g["x"].data_ptr(), g["packed"].data_ptr(), g["y"].data_ptr()
+    step_bytes = sum(g["bytes"] for g in gemvs)
+    log(f"[bench] {len(gemvs)} GEMVs, {step_bytes / 1e9:.3f} GB/step, inputs ready in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    # eager warm-up and a sanity spot check
+    with torch.cuda.stream(stream):
+        launch_step(w4, gemvs, sh)
+    stream.synchronize()
+    spot_check(w4, gemvs, torch)
+    log("[bench] spot check ok")
+
+    graph = None
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            launch_step(w4, gemvs, stream.cuda_stream)
+        torch.cuda.synchronize()
+
+    def run_steps(n):
+        with torch.cuda.stream(stream):
+            for _ in range(n):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    launch_step(w4, gemvs, sh)
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed / args.steps * 1e3
+    log(f"[bench] {args.mode}: {ms_per_step * 1e3:.1f} us/step")
+
+    # event timing of the same step: whole step, and every launch of each kernel
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e0, e1 = ev(), ev()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        run_steps(args.steps)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us_step_events = e0.elapsed_time(e1) / args.steps * 1e3
+
+    per_kernel = {}
+    ksteps = max(1, min(args.steps, 20))
+    with torch.cuda.stream(stream):
+        marks = []
+        for _ in range(ksteps):
+            for g in gemvs:
+                a, b = ev(), ev()
+                a.record(stream)
+                st = w4.w4a16_gemv_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], sh)
+                if st != 0:
+                    raise w4.W4A16Error(st, "w4a16_gemv")
+                b.record(stream)
+                marks.append((g, a, b))
+    torch.cuda.synchronize()
+    for g, a, b in marks:
+        k = per_kernel.setdefault(g["kernel"], {"launches": 0, "ms": 0.0, "bytes": 0})
+        k["launches"] += 1
+        k["ms"] += a.elapsed_time(b)
+        k["bytes"] += g["bytes"]
+    for name, k in per_kernel.items():
+        k["avg_us"] = k["ms"] / k["launches"] * 1e3
+        k["gbs"] = k["bytes"] / (k["ms"] * 1e-3) / 1e9
+        log(f"[bench] {name}: {k['launches']} launches, avg {k['avg_us']:.2f} us, {k['gbs']:.1f} GB/s")
+    dom_name = max(per_kernel, key=lambda n: per_kernel[n]["ms"])
+    dom = per_kernel[dom_name]
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4xf16->f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b_step: 32 Llama-3-8B-shaped layers x (qkv 4096->6144, o 4096->4096, "
+                        "gate_up 4096->28672, down 14336->4096), M=1, 4-bit codes, group 32, fp16 scale+min",
+            "gemvs_per_step": len(gemvs),
+            "bytes_per_step": step_bytes,
+            "launch": args.mode,
+            "us_per_step_events": round(us_step_events, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom_name,
+            "achieved": round(dom["gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dom["avg_us"], 3),
+            "bytes_per_launch": int(dom["bytes"] / dom["launches"]),
+            "per_kernel": {n: {"launches_per_step": k["launches"] // ksteps, "avg_us": round(k["avg_us"], 3),
+                               "gbs": round(k["gbs"], 1)} for n, k in per_kernel.items()},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on host cores ...")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+"""Thin ctypes binding of libw4a16 (the C ABI in include/w4a16.h).
+
+Argument marshalling only: every step of the product runs in the library's
+host repacker and gfx950 kernels. PyTorch, when used, only supplies device
+memory and the current stream. If the library is not built this module
+raises; it never falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_ERR_NULL = 1
+W4A16_ERR_SHAPE = 2
+W4A16_ERR_ALIGN = 3
+W4A16_ERR_SIZE = 4
+W4A16_ERR_OVERLAP = 5
+W4A16_ERR_HIP = 6
+
+# every symbol include/w4a16.h declares
+EXPORTS = (
+    "w4a16_abi_version",
+    "w4a16_max_k",
+    "w4a16_packed_bytes",
+    "w4a16_pack",
+    "w4a16_gemv",
+    "w4a16_launch_shape",
+    "w4a16_status_string",
+)
+
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {w4a16_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32, c_sz, c_vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    L.w4a16_abi_version.restype = c_i32
+    L.w4a16_abi_version.argtypes = []
+    L.w4a16_max_k.restype = c_i32
+    L.w4a16_max_k.argtypes = [c_i32]
+    L.w4a16_packed_bytes.restype = c_sz
+    L.w4a16_packed_bytes.argtypes = [c_i32, c_i32]
+    L.w4a16_pack.restype = c_i32
+    L.w4a16_pack.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_sz]
+    L.w4a16_gemv.restype = c_i32
+    L.w4a16_gemv.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp]
+    L.w4a16_launch_shape.restype = c_i32
+    L.w4a16_launch_shape.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_status_string.argtypes = [c_i32]
+    _lib = L
+    return L
+
+
+def w4a16_abi_version() -> int:
+    return int(lib().w4a16_abi_version())
+
+
+def w4a16_max_k(M: int) -> int:
+    return int(lib().w4a16_max_k(M))
+
+
+def w4a16_status_string(status: int) -> str:
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def w4a16_packed_bytes(N: int, K: int) -> int:
+    return int(lib().w4a16_packed_bytes(int(N), int(K)))
+
+
+def w4a16_pack(codes: np.ndarray, scale: np.ndarray, mn: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Host repack: codes uint8[N, K/2], scale/min float16[N, K/32] -> uint8 blob."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float16)
+    mn = np.ascontiguousarray(mn, dtype=np.float16)
+    N, Kh = codes.shape
+    K = 2 * Kh
+    nbytes = w4a16_packed_bytes(N, K)
+    if out is None:
+        out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    if scale.shape != (N, K // 32) or mn.shape != (N, K // 32):
+        raise ValueError("scale and min must be [N, K/32]")
+    st = lib().w4a16_pack(codes.ctypes.data, scale.ctypes.data, mn.ctypes.data, N, K,
+                          out.ctypes.data, out.nbytes)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_pack")
+    return out
+
+
+def w4a16_launch_shape(M: int, N: int, K: int) -> dict:
+    """(groups per lane, waves per workgroup, passes over K) w4a16_gemv would use."""
+    out = (ctypes.c_int32 * 3)()
+    st = lib().w4a16_launch_shape(M, N, K, out)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_launch_shape")
+    return {"groups_per_lane": out[0], "waves": out[1], "k_passes": out[2],
+            "kernel": f"gemv_kernel<{M}, {out[0]}>"}
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if hasattr(t, "data_ptr") else int(t)
+
+
+def w4a16_gemv_raw(x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Direct C call with raw pointers; returns the status code."""
+    return int(lib().w4a16_gemv(x_ptr, packed_ptr, y_ptr, M, N, K, stream))
+
+
+def w4a16_gemv(x, packed, y, stream=None) -> None:
+    """y[M, N] = x[M, K] @ w_hat.T on the GPU, enqueued on `stream`.
+
+    x: device float16 [M, K]; packed: device uint8 blob from w4a16_pack;
+    y: device float32 [M, N], overwritten. `stream` is a torch stream, a raw
+    hipStream_t integer, or None for torch's current stream.
+    """
+    if str(x.dtype) != "torch.float16" or str(y.dtype) != "torch.float32":
+        raise TypeError("x must be float16 and y float32")
+    if x.dim() != 2 or y.dim() != 2:
+        raise ValueError("x must be [M, K] and y [M, N]")
+    M, K = int(x.shape[0]), int(x.shape[1])
+    N = int(y.shape[-1])
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N] with the same M as x")
+    need = w4a16_packed_bytes(N, K)
+    if need == 0:
+        raise W4A16Error(W4A16_ERR_SHAPE, "w4a16_gemv")
+    if packed.numel() * packed.element_size() < need:
+        raise ValueError(f"packed blob has {packed.numel() * packed.element_size()} bytes, needs {need}")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and y must be contiguous")
+    if stream is None:
+        import torch  # only for the current stream handle
+
+        s = torch.cuda.current_stream(x.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        s = stream.cuda_stream
+    else:
+        s = int(stream)
+    st = w4a16_gemv_raw(_ptr(x), _ptr(packed), _ptr(y), M, N, K, s)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemv")
+
+
+def upload_packed(blob: np.ndarray, device="cuda"):
+    """Copy a host blob from w4a16_pack to a 256-byte-aligned device uint8 tensor."""
+    import torch
+
+    host = torch.from_numpy(np.ascontiguousarray(blob, dtype=np.uint8))
+    dev = torch.empty(host.numel() + 256, dtype=torch.uint8, device=device)
+    off = (-dev.data_ptr()) % 256
+    view = dev[off:off + host.numel()]
+    view.copy_(host)
+    return view

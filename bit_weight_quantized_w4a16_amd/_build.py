@@ -1,0 +1,51 @@
+"""Compile libw4a16.so in-tree with hipcc for gfx950 (no JIT, no cache outside the tree)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+LIB_NAME = "libw4a16.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = ["csrc/w4a16_gemv.hip", "csrc/w4a16_pack.cpp"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # no packed-fp32 VALU forms anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the W4A16 library needs ROCm's hipcc to build")
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompile; write the library atomically next to this file."""
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
+           *[os.path.join(PKG_DIR, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building %s" % LIB_NAME)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,131 @@
+// Host-side repacker: canonical nibbles + per-group binary16 scale/min ->
+// the packed blob the gfx950 kernel streams (layout in include/w4a16.h).
+//
+// The packer of the core-modules page (section 5.1) quantises and lays a model
+// out once, offline; doing the re-layout here keeps every run-time load a
+// full 16-byte, lane-contiguous chunk and lets the kernel unpack a nibble pair
+// with a single AND.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "w4a16.h"
+
+namespace {
+
+constexpr int64_t kGroup = 32;
+constexpr int64_t kTileRows = 4;
+constexpr int64_t kRegionAlign = 256;
+
+// Bytes b0..b3 (little-endian word v) hold k = 8d + 0..7 as (lo = even k,
+// hi = odd k) nibble pairs. Return the word with the four even k in the low
+// half-word and the four odd k in the high half-word, in increasing k.
+inline uint32_t split_even_odd(uint32_t v) {
+  uint32_t e = v & 0x0F0F0F0Fu;          // even k, one per byte
+  uint32_t o = (v >> 4) & 0x0F0F0F0Fu;   // odd k, one per byte
+  e = (e | (e >> 4)) & 0x00FF00FFu;      // squeeze nibbles pairwise
+  e = (e | (e >> 8)) & 0x0000FFFFu;
+  o = (o | (o >> 4)) & 0x00FF00FFu;
+  o = (o | (o >> 8)) & 0x0000FFFFu;
+  return e | (o << 16);
+}
+
+int64_t codes_region_bytes(int64_t N, int64_t K) {
+  int64_t c = N * K / 2;
+  return (c + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+}
+
+template <class F>
+void parallel_rows(int64_t rows, int64_t work_per_row, F&& body) {
+  int64_t total = rows * work_per_row;
+  unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  int64_t nthreads = std::min<int64_t>(hw, std::max<int64_t>(1, total >> 22));
+  nthreads = std::min<int64_t>(nthreads, rows);
+  if (nthreads <= 1) {
+    body(0, rows);
+    return;
+  }
+  std::vector<std::thread> pool;
+  int64_t per = (rows + nthreads - 1) / nthreads;
+  for (int64_t t = 0; t < nthreads; ++t) {
+    int64_t r0 = t * per, r1 = std::min(rows, r0 + per);
+    if (r0 >= r1) break;
+    pool.emplace_back([&body, r0, r1] { body(r0, r1); });
+  }
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" size_t w4a16_packed_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < kGroup || K % kGroup) return 0;
+  int64_t G = K / kGroup;
+  if (int64_t(N) * G > INT32_MAX) return 0;
+  int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
+  return size_t(codes_region_bytes(N, K) + T * G * 16);
+}
+
+extern "C" w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* min,
+                                   int32_t N, int32_t K, void* out, size_t out_bytes) {
+  if (!codes || !scale || !min || !out) return W4A16_ERR_NULL;
+  size_t need = w4a16_packed_bytes(N, K);
+  if (need == 0) return W4A16_ERR_SHAPE;
+  if (out_bytes < need) return W4A16_ERR_SIZE;
+
+  const int64_t G = K / kGroup;
+  const int64_t row_bytes = int64_t(K) / 2;
+  const int64_t S = codes_region_bytes(N, K);
+  const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
+  uint8_t* o = static_cast<uint8_t*>(out);
+
+  // codes: same byte footprint as the canonical array, words re-ordered in place
+  parallel_rows(N, row_bytes, [&](int64_t r0, int64_t r1) {
+    for (int64_t n = r0; n < r1; ++n) {
+      const uint8_t* src = codes + n * row_bytes;
+      uint8_t* dst = o + n * row_bytes;
+      for (int64_t b = 0; b < row_bytes; b += 4) {
+        uint32_t v;
+        std::memcpy(&v, src + b, 4);
+        v = split_even_odd(v);
+        std::memcpy(dst + b, &v, 4);
+      }
+    }
+  });
+  std::memset(o + int64_t(N) * row_bytes, 0, size_t(S - int64_t(N) * row_bytes));
+
+  // scale/min tiles of 4 rows x 1 group
+  uint8_t* sm = o + S;
+  parallel_rows(T, G * 16, [&](int64_t t0, int64_t t1) {
+    for (int64_t t = t0; t < t1; ++t) {
+      for (int64_t g = 0; g < G; ++g) {
+        uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int64_t r = 0; r < kTileRows; ++r) {
+          int64_t n = t * kTileRows + r;
+          if (n < N) {
+            e[2 * r] = scale[n * G + g];
+            e[2 * r + 1] = min[n * G + g];
+          }
+        }
+        std::memcpy(sm + (t * G + g) * 16, e, 16);
+      }
+    }
+  });
+  return W4A16_OK;
+}
+
+extern "C" int32_t w4a16_abi_version(void) { return 1; }
+
+extern "C" const char* w4a16_status_string(int32_t status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL: return "a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "M, N or K outside the supported range";
+    case W4A16_ERR_ALIGN: return "a pointer breaks its alignment rule";
+    case W4A16_ERR_SIZE: return "output buffer smaller than required";
+    case W4A16_ERR_OVERLAP: return "y overlaps x or the packed weights";
+    case W4A16_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,147 @@
+/*
+ * w4a16.h - C ABI of libw4a16: the decode-step matrix-vector product over
+ * 4-bit group-quantised weights and 16-bit activations (W4A16) on gfx950.
+ *
+ * Sources. The core-modules page (section 5.1, packer: quantisation) places
+ * edge decode in the 4-bit-weight / 16-bit-activation regime; its runtime
+ * table (section 5.2) names the K-quant Q4_K_M family; the Magnitude page
+ * (section 3.4, thread control) and the core-modules page (section 5.4,
+ * loading strategies) frame decode as memory-bandwidth bound, which is why the
+ * kernel streams each weight exactly once. Section 5.2's list of runtime
+ * traits (static shapes, an allocation-free decode loop, a plain tensor
+ * descriptor behind a backend table) sets the conventions below: plain
+ * pointers and sizes, caller-owned buffers, no allocation, no
+ * synchronisation. Section 5.7's contract table (a runtime refuses a model
+ * whose format it does not cover) is why every argument error is reported
+ * as a status instead of being run.
+ *
+ * Weight format (the plain reading of "group scale and min"; the pages never
+ * spell the format out):
+ *   codes  uint8 [N][K/2]  two unsigned 4-bit codes per byte, row n = output
+ *                          feature n; the LOW nibble of byte j is k = 2j, the
+ *                          HIGH nibble is k = 2j + 1.
+ *   scale  binary16 [N][K/32], min binary16 [N][K/32]: one pair per group of
+ *                          32 consecutive k of one row.
+ *   w_hat[n][k] = scale[n][k/32] * q[n][k] + min[n][k/32]
+ *   y[m][n]     = sum_k w_hat[n][k] * x[m][k]      (x binary16 [M][K], y fp32)
+ *
+ * Packed layout (what w4a16_pack writes and w4a16_gemv reads):
+ *   G  = K / 32 groups per row, T = ceil(N / 4) row tiles.
+ *   [0, N*K/2)           codes: row-major [N][G] chunks of 16 bytes; chunk
+ *                        (n, g) holds k = 32g .. 32g+31. Inside a chunk, the
+ *                        little-endian 32-bit word d (bytes 4d..4d+3) holds
+ *                        k = 32g + 8d + i, i = 0..7, with nibble slot p
+ *                        (bits 4p..4p+3) holding i = 2p for p < 4 and
+ *                        i = 2(p-4)+1 for p >= 4: the four even i in the low
+ *                        half-word, the four odd i in the high half-word,
+ *                        each in increasing order.
+ *   [S, S + T*G*16)      S = N*K/2 rounded up to a multiple of 256. Scale/min
+ *                        tiles: [T][G] entries of 16 bytes; entry (t, g) holds
+ *                        rows 4t .. 4t+3, row r in bytes 4r..4r+3 as
+ *                        (binary16 scale, binary16 min), little endian. Rows
+ *                        at or beyond N are zero.
+ *   Total size: w4a16_packed_bytes(N, K) = S + T*G*16.
+ *
+ * Status codes are returned, never raised; nothing aborts.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4a16_status {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL = 1,     /* a required pointer is NULL */
+  W4A16_ERR_SHAPE = 2,    /* M, N or K outside the supported range */
+  W4A16_ERR_ALIGN = 3,    /* a pointer breaks its alignment rule */
+  W4A16_ERR_SIZE = 4,     /* an output buffer is smaller than required */
+  W4A16_ERR_OVERLAP = 5,  /* y overlaps x or the packed weights */
+  W4A16_ERR_HIP = 6       /* the HIP runtime reported an error */
+} w4a16_status;
+
+/* Version of this ABI and of the packed layout; bumped on any change. */
+int32_t w4a16_abi_version(void);
+
+/* Largest K accepted by w4a16_gemv for a given M (0 if M is outside 1..8). */
+int32_t w4a16_max_k(int32_t M);
+
+/*
+ * Bytes of the packed blob for an N x K weight matrix (see "Packed layout").
+ * Returns 0 if N < 1, K < 32, K % 32 != 0, or N * K / 32 does not fit the
+ * kernels' 31-bit chunk index.
+ */
+size_t w4a16_packed_bytes(int32_t N, int32_t K);
+
+/*
+ * w4a16_pack - host-side repacker (init time; not on the per-token path).
+ * The packer's quantise-then-lay-out step of the core-modules page (section
+ * 5.1), done once so the run-time kernel only ever streams.
+ *
+ *   codes  host uint8 [N][K/2], layout as in "Weight format"   (read only)
+ *   scale  host binary16 bits [N][K/32]                         (read only)
+ *   min    host binary16 bits [N][K/32]                         (read only)
+ *   out    host buffer of at least w4a16_packed_bytes(N, K) bytes, owned
+ *          by the caller; written completely (padding is zeroed).
+ * The caller then copies `out` to device memory, 256-byte aligned.
+ * Uses worker threads for large inputs; touches no GPU.
+ * Errors: NULL pointer -> W4A16_ERR_NULL; bad N/K -> W4A16_ERR_SHAPE;
+ * out_bytes too small -> W4A16_ERR_SIZE (nothing written).
+ */
+w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* min,
+                        int32_t N, int32_t K, void* out, size_t out_bytes);
+
+/*
+ * w4a16_gemv - y[M][N] = x[M][K] * w_hat^T, one decode-step product (the
+ * per-token GEMV of every fused linear layer, core-modules page section 5.1's
+ * fused query/key/value and gate/up rewrites; M > 1 rows are a speculative
+ * verify batch, section 5.6).
+ *
+ *   x       device binary16 [M][K], row-major, 16-byte aligned (read only)
+ *   packed  device blob written by w4a16_pack for this N and K, 256-byte
+ *           aligned (read only)
+ *   y       device fp32 [M][N], row-major, 4-byte aligned; overwritten (no
+ *           accumulation into prior contents)
+ *   M       activation rows, 1..8
+ *   N       output features, >= 1
+ *   K       input features, multiple of 32, 32 <= K <= w4a16_max_k(M)
+ *   stream  hipStream_t to enqueue on (NULL = the device's null stream)
+ *
+ * All buffers are owned by the caller and must live until the work completes.
+ * The call only enqueues: it never allocates, frees or synchronises. Results
+ * are bitwise repeatable for the same inputs on the same device.
+ * Errors (checked on the host before anything is enqueued): NULL pointer ->
+ * W4A16_ERR_NULL; M, N or K out of range -> W4A16_ERR_SHAPE; misaligned
+ * pointer -> W4A16_ERR_ALIGN; y's byte range intersecting x's or the packed
+ * blob's -> W4A16_ERR_OVERLAP; a launch the HIP runtime rejects ->
+ * W4A16_ERR_HIP. Faults inside the kernel (e.g. a packed blob shorter than
+ * w4a16_packed_bytes) are not detectable here and surface at the caller's
+ * next synchronisation.
+ */
+w4a16_status w4a16_gemv(const void* x, const void* packed, float* y,
+                        int32_t M, int32_t N, int32_t K, void* stream);
+
+/*
+ * w4a16_launch_shape - how w4a16_gemv would run an (M, N, K) product, for
+ * profilers and benches that attribute kernel time to launches. Pure host
+ * logic: touches no GPU.
+ *   out[0] = groups of 32 k per lane (the kernel's template parameter),
+ *   out[1] = waves per workgroup, out[2] = passes over K.
+ * The kernel symbol is gemv_kernel<M, out[0]>.
+ * Errors: out NULL -> W4A16_ERR_NULL; shape outside w4a16_gemv's range ->
+ * W4A16_ERR_SHAPE (out untouched).
+ */
+w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int32_t out[3]);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* w4a16_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */
