@@ -111,7 +111,8 @@ def cpu_baseline(budget_s=12.0):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle on {len(done)} of the step's 128 GEMVs ({', '.join(done)}), "
+        "sample": f"fp64 oracle on the first {len(done)} of the step's 128 GEMVs (layer order, "
+                  f"{done[0]} .. {done[-1]}), "
                   f"{done_bytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, "
                   f"{threads} worker threads, BLAS threads limited to 1",
         "us_per_step_extrapolated": round(t_total / done_bytes * sum(

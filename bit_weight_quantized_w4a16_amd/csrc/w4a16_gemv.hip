@@ -46,6 +46,14 @@ constexpr int kMaxWaves = 16;
 constexpr int kMaxM = 8;
 constexpr uint32_t kOnes = 0x3C003C00u;  // binary16 pair (1.0, 1.0)
 
+// Element i of a 4 x u32 vector. Written as an explicit select rather than
+// v[i]: with ROCm 7.2's clang, v[i] on an unrolled index inside the tile loop
+// was folded to v[0] (the scale/min load shrank to one dword and every row of
+// a tile used row 0's scale), so vector elements are only ever read this way.
+__device__ __forceinline__ uint32_t elem(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
@@ -116,8 +124,8 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            xr[m][j][4 * q + e] = v[q][e];
-            s = dot2(v[q][e], kOnes, s);
+            xr[m][j][4 * q + e] = elem(v[q], e);
+            s = dot2(elem(v[q], e), kOnes, s);
           }
         }
         xs[m][j] = s;
@@ -154,7 +162,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
         for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint32_t w = c4[r][j][d];
+          const uint32_t w = elem(c4[r][j], d);
           const uint32_t w8 = w >> 8;
           const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
           const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
@@ -168,7 +176,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
             hi[m] = dot2(pd, xr[m][j][4 * d + 3], hi[m]);
           }
         }
-        const f16x2 h = __builtin_bit_cast(f16x2, s4[j][r]);
+        const f16x2 h = __builtin_bit_cast(f16x2, elem(s4[j], r));
         const float sc = float(h[0]) * 0x1p20f;
         const float mn = float(h[1]);
 #pragma unroll
@@ -277,31 +285,29 @@ struct LaunchShape {
   int nchunks;  // passes over K
 };
 
-// Prefer one pass over K with the fewest waves and at most a quarter of the
-// lanes idle; otherwise split K into the fewest passes of the widest shape.
+// Fewest passes over K; then avoid leaving more than a quarter of the lanes
+// idle; then the fewest waves per workgroup; then the fewest idle lanes.
 LaunchShape choose_shape(int M, int G) {
   LaunchShape best{-1, 0, 0};
-  long best_idle = 0;
+  long best_key[4] = {0, 0, 0, 0};
   for (int gi = kNumGpl - 1; gi >= 0; --gi) {
     const int gpl = kGplOptions[gi];
     if (!gpl_allowed(M, gpl)) continue;
-    const int waves = (G + 64 * gpl - 1) / (64 * gpl);
-    if (waves > max_waves(M, gpl)) continue;
-    const long idle = long(waves) * 64 * gpl - G;
-    if (waves > 1 && 4 * idle > long(waves) * 64 * gpl) continue;
-    if (best.gi < 0 || waves < best.waves || (waves == best.waves && idle < best_idle)) {
-      best = LaunchShape{gi, waves, 1};
-      best_idle = idle;
+    const int wmax = max_waves(M, gpl);
+    const int nchunks = (G + wmax * 64 * gpl - 1) / (wmax * 64 * gpl);
+    const int waves = (G + nchunks * 64 * gpl - 1) / (nchunks * 64 * gpl);
+    const long slots = long(nchunks) * waves * 64 * gpl;
+    const long idle = slots - G;
+    const long key[4] = {nchunks, 4 * idle > slots ? 1 : 0, waves, idle};
+    bool better = best.gi < 0;
+    for (int i = 0; i < 4 && !better; ++i) {
+      if (key[i] < best_key[i]) better = true;
+      if (key[i] > best_key[i]) break;
     }
-  }
-  if (best.gi >= 0) return best;
-  for (int gi = kNumGpl - 1; gi >= 0; --gi) {
-    const int gpl = kGplOptions[gi];
-    if (!gpl_allowed(M, gpl)) continue;
-    const int waves = max_waves(M, gpl);
-    const int per_chunk = waves * 64 * gpl;
-    const int nchunks = (G + per_chunk - 1) / per_chunk;
-    if (best.gi < 0 || nchunks < best.nchunks) best = LaunchShape{gi, waves, nchunks};
+    if (better) {
+      best = LaunchShape{gi, waves, nchunks};
+      for (int i = 0; i < 4; ++i) best_key[i] = key[i];
+    }
   }
   return best;
 }
