@@ -12,12 +12,15 @@
 //
 // Work decomposition
 //   * a lane owns GPL groups of 32 k along K (group g = (wave*GPL + j)*64 +
-//     lane) and keeps that slice of every activation row in VGPRs for the
-//     whole kernel, so x is read from memory once per workgroup;
-//   * the W waves of a workgroup together cover all G = K/32 groups;
-//   * a workgroup walks 4-row tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...
-//     For each tile a lane issues 4*GPL code loads and GPL scale/min loads
-//     (each 16 B, lane-contiguous, so one wave instruction moves 1 KiB);
+//     lane within one pass over K) and keeps that slice of every activation
+//     row in VGPRs, so x is read from memory once per workgroup and pass;
+//   * the W waves of a workgroup cover W*64*GPL groups per pass; K longer
+//     than that takes several passes, the partial sums carried in LDS;
+//   * a workgroup walks 4-row tiles; for each tile a lane issues 4*GPL code
+//     loads and GPL scale/min loads, each 16 B and lane-contiguous, so one
+//     wave instruction moves 1 KiB. The loads of the next tile are issued
+//     before the current tile is computed, and the first tile's loads go out
+//     before x is fetched, so the two start-up latencies overlap;
 //   * per group a lane computes sum_k q*x with v_dot2c_f32_f16 on binary16
 //     *subnormal* pairs: AND-ing a packed word with 0x000F000F gives two halfs
 //     whose bit patterns are the codes, i.e. the values q * 2^-24, and with
@@ -32,6 +35,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstdlib>
 
 #include "w4a16.h"
 
@@ -75,82 +79,102 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Waves per workgroup an instantiation may use: its VGPR estimate must fit
-// the 512-entry register file shared by the waves on one SIMD.
+// Up to four activation rows the next tile's loads are issued before the
+// current tile is computed (two load buffers); beyond that the kernel is
+// bound by VALU work and the registers go to the x slices instead.
+__host__ __device__ constexpr bool double_buffered(int M) { return M <= 4; }
+
+// Waves per workgroup an instantiation may use: its VGPR estimate (x slice,
+// tile loads in flight, accumulators) must fit the 512-entry register file
+// shared by the waves on one SIMD.
 __host__ __device__ constexpr int max_waves(int M, int GPL) {
-  return (16 * M * GPL + 20 * GPL + 6 * M + 30) <= 128 ? 16 : 8;
+  return (16 * M * GPL + (double_buffered(M) ? 40 : 20) * GPL + 6 * M + 30) <= 128 ? 16 : 8;
 }
 
-// Tiles of 4 rows handled between two workgroup barriers when partial sums
-// go through LDS.
+// Most tiles of 4 rows handled between two workgroup barriers when partial
+// sums go through LDS.
 constexpr int kTilesPerBlock = 8;
 
-template <int M, int GPL>
+// Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
+template <int GPL>
+struct TileLoads {
+  u32x4 sm[GPL];
+  u32x4 code[kTileRows][GPL];
+};
+
+// MULTI: K takes more than one pass of the workgroup, so x is re-fetched per
+// pass inside the tile loop; otherwise x is fetched once, before it.
+template <int M, int GPL, bool MULTI>
 __global__ void __launch_bounds__(64 * max_waves(M, GPL))
-gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
-            const u32x4* __restrict__ sm, float* __restrict__ y, int N, int G, int T, int nchunks) {
+gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
+            float* __restrict__ y, int N, int G, int T, int nchunks, int tpb) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values kept in scalar registers, so every load address is a
+  // scalar base plus the one per-lane offset `lane`
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
   const bool direct = (nwaves == 1 && nchunks == 1);
-  const int nblocks = direct ? T : (T + kTilesPerBlock - 1) / kTilesPerBlock;
-  const int tpb = direct ? 1 : kTilesPerBlock;
+  const int nblocks = (T + tpb - 1) / tpb;
 
-  uint32_t xr[M][GPL][16];
+  // first group of slot j of this wave in pass c; the lane adds its index
+  auto group_base = [&](int c, int j) { return c * chunk_groups + (wave * GPL + j) * 64; };
+
+  // issue the 16-byte non-temporal loads of tile t, pass c over K
+  auto fetch = [&](int t, int c, TileLoads<GPL>& L) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const int g0 = group_base(c, j);
+      const bool ok = lane < G - g0;
+      const u32x4* sp = sm + (size_t(t) * G + g0);
+      L.sm[j] = u32x4{0, 0, 0, 0};
+      if (ok) L.sm[j] = __builtin_nontemporal_load(sp + lane);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const int n = t * kTileRows + r;
+        const u32x4* cp = codes + (size_t(n) * G + g0);
+        L.code[r][j] = u32x4{0, 0, 0, 0};
+        if (ok && n < N) L.code[r][j] = __builtin_nontemporal_load(cp + lane);
+      }
+    }
+  };
+
+  // this lane's slice of pass c of every activation row (loaded straight
+  // into the registers that keep it), plus its group sums
+  u32x4 xv[M][GPL][4];
   float xs[M][GPL];
-  int grp[GPL];
-  bool ok[GPL];
-
-  // this lane's slice of chunk c of every activation row, plus its group sums
   auto load_x = [&](int c) {
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
-      grp[j] = c * chunk_groups + (wave * GPL + j) * 64 + lane;
-      ok[j] = grp[j] < G;
+      const int g = group_base(c, j) + lane;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[m][j][q] = u32x4{0, 0, 0, 0};
+        if (g < G) {
+          const u32x4* p = x + (size_t(m) * G + g) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xv[m][j][q] = p[q];
+        }
+      }
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
 #pragma unroll
       for (int j = 0; j < GPL; ++j) {
-        u32x4 v[4] = {};
-        if (ok[j]) {
-          const u32x4* p = x + (size_t(m) * G + grp[j]) * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = p[q];
-        }
         float s = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xr[m][j][4 * q + e] = elem(v[q], e);
-            s = dot2(elem(v[q], e), kOnes, s);
-          }
+          for (int e = 0; e < 4; ++e) s = dot2(elem(xv[m][j][q], e), kOnes, s);
         }
         xs[m][j] = s;
       }
     }
   };
 
-  // partial row sums of one tile over this lane's groups of the current chunk
-  auto tile = [&](int t, float (&acc)[kTileRows][M]) {
-    u32x4 s4[GPL];
-    u32x4 c4[kTileRows][GPL];
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      s4[j] = u32x4{0, 0, 0, 0};
-      if (ok[j]) s4[j] = __builtin_nontemporal_load(sm + size_t(t) * G + grp[j]);
-    }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-      const int n = t * kTileRows + r;
-#pragma unroll
-      for (int j = 0; j < GPL; ++j) {
-        c4[r][j] = u32x4{0, 0, 0, 0};
-        if (ok[j] && n < N) c4[r][j] = __builtin_nontemporal_load(codes + size_t(n) * G + grp[j]);
-      }
-    }
+  // wave-wide row sums of one tile over this wave's groups of the current pass
+  auto compute = [&](const TileLoads<GPL>& L, float (&acc)[kTileRows][M]) {
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
 #pragma unroll
@@ -162,7 +186,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
         for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint32_t w = elem(c4[r][j], d);
+          const uint32_t w = elem(L.code[r][j], d);
           const uint32_t w8 = w >> 8;
           const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
           const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
@@ -170,13 +194,14 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
           const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            lo[m] = dot2(pa, xr[m][j][4 * d + 0], lo[m]);
-            hi[m] = dot2(pb, xr[m][j][4 * d + 1], hi[m]);
-            lo[m] = dot2(pc, xr[m][j][4 * d + 2], lo[m]);
-            hi[m] = dot2(pd, xr[m][j][4 * d + 3], hi[m]);
+            const u32x4& xq = xv[m][j][d];  // x[8d .. 8d+7] of this group
+            lo[m] = dot2(pa, elem(xq, 0), lo[m]);
+            hi[m] = dot2(pb, elem(xq, 1), hi[m]);
+            lo[m] = dot2(pc, elem(xq, 2), lo[m]);
+            hi[m] = dot2(pd, elem(xq, 3), hi[m]);
           }
         }
-        const f16x2 h = __builtin_bit_cast(f16x2, elem(s4[j], r));
+        const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
         const float sc = float(h[0]) * 0x1p20f;
         const float mn = float(h[1]);
 #pragma unroll
@@ -196,47 +221,109 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
   // per-wave partials of one block of tiles: [tile][row][m][wave]
   __shared__ float part[kTilesPerBlock][kTileRows][M][kMaxWaves];
 
-  if (nchunks == 1) load_x(0);
-  for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
-    for (int c = 0; c < nchunks; ++c) {
-      if (nchunks > 1) load_x(c);
-      for (int tb = 0; tb < tpb; ++tb) {
-        const int t = b * tpb + tb;
-        if (t >= T) break;
-        float acc[kTileRows][M];
-        tile(t, acc);
-        if (direct) {
-          float v = 0.f;
-#pragma unroll
-          for (int i = 0; i < kTileRows * M; ++i)
-            if (lane == i) v = acc[i / M][i % M];
-          if (lane < kTileRows * M) {
-            const int n = t * kTileRows + lane / M;
-            if (n < N) y[size_t(lane % M) * N + n] = v;
-          }
-        } else if (lane == 0) {
-#pragma unroll
-          for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-              part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + acc[r][m];
-        }
+  // This workgroup walks items (block b, pass c, tile tb of the block) for
+  // b = blockIdx.x, blockIdx.x + gridDim.x, ...; the loads of the next item
+  // are in flight while the current one is computed (two load buffers used
+  // alternately). Every wave of the workgroup walks the same items, so the
+  // barriers below are uniform.
+  struct Item {
+    int b, c, tb;
+  };
+  auto next_item = [&](Item it) {
+    Item n{it.b, it.c, it.tb + 1};
+    if (n.tb >= tpb || n.b * tpb + n.tb >= T) {
+      n.tb = 0;
+      if (++n.c >= nchunks) {
+        n.c = 0;
+        n.b += gridDim.x;
       }
     }
-    if (!direct) {
+    return n;
+  };
+  // compute item `it` from its loads, emit or stage its results; `nb` is the
+  // block of the item after it (a new block closes block it.b)
+  auto finish = [&](const TileLoads<GPL>& L, Item it, int nb) {
+    const int t = it.b * tpb + it.tb;
+    float acc[kTileRows][M];
+    compute(L, acc);
+    if (direct) {
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < kTileRows * M; ++i)
+        if (lane == i) v = acc[i / M][i % M];
+      if (lane < kTileRows * M) {
+        const int n = t * kTileRows + lane / M;
+        if (n < N) y[size_t(lane % M) * N + n] = v;
+      }
+      return;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          part[it.tb][r][m][wave] = (it.c == 0 ? 0.f : part[it.tb][r][m][wave]) + acc[r][m];
+    }
+    if (nb != it.b) {  // every pass of block it.b is done: combine the waves
       __syncthreads();
-      for (int i = threadIdx.x; i < tpb * kTileRows * M; i += blockDim.x) {
-        const int tb = i / (kTileRows * M);
+      const int ntiles = min(tpb, T - it.b * tpb);
+      for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
+        const int ti = i / (kTileRows * M);
         const int r = (i / M) % kTileRows;
         const int m = i % M;
-        const int n = (b * tpb + tb) * kTileRows + r;
+        const int n = (it.b * tpb + ti) * kTileRows + r;
         if (n < N) {
           float s = 0.f;
-          for (int w = 0; w < nwaves; ++w) s += part[tb][r][m][w];
+          for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
           y[size_t(m) * N + n] = s;
         }
       }
       __syncthreads();
+    }
+  };
+
+  Item ia{int(blockIdx.x), 0, 0};
+  if (ia.b >= nblocks) return;
+  if constexpr (MULTI) {
+    // passes over K outermost within a block: x of pass c is fetched once at
+    // the top of the pass and stays in registers for the block's tiles
+    for (int b = ia.b; b < nblocks; b += gridDim.x) {
+      for (int c = 0; c < nchunks; ++c) {
+        load_x(c);
+        const int ntiles = min(tpb, T - b * tpb);
+        for (int tb = 0; tb < ntiles; ++tb) {
+          TileLoads<GPL> la;
+          fetch(b * tpb + tb, c, la);
+          const bool last = (c == nchunks - 1) && (tb == ntiles - 1);
+          finish(la, Item{b, c, tb}, last ? b + int(gridDim.x) : b);
+        }
+      }
+    }
+  } else if constexpr (double_buffered(M)) {
+    TileLoads<GPL> la, lb;
+    fetch(ia.b * tpb + ia.tb, ia.c, la);
+    load_x(0);  // after the first tile's loads, so both latencies overlap
+    while (true) {
+      const Item ib = next_item(ia);
+      if (ib.b < nblocks) fetch(ib.b * tpb + ib.tb, ib.c, lb);
+      finish(la, ia, ib.b);
+      if (ib.b >= nblocks) break;
+      ia = next_item(ib);
+      if (ia.b < nblocks) fetch(ia.b * tpb + ia.tb, ia.c, la);
+      finish(lb, ib, ia.b);
+      if (ia.b >= nblocks) break;
+    }
+  } else {
+    bool first = true;
+    while (true) {
+      TileLoads<GPL> la;
+      fetch(ia.b * tpb + ia.tb, ia.c, la);
+      if (first) load_x(0);
+      first = false;
+      const Item ib = next_item(ia);
+      finish(la, ia, ib.b);
+      if (ib.b >= nblocks) break;
+      ia = ib;
     }
   }
 }
@@ -245,36 +332,37 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes,
 // host side: instantiation table, launch-shape choice, validation
 // ---------------------------------------------------------------------------
 
-typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, float*, int, int, int, int);
+typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, float*, int, int, int, int, int);
 
 constexpr int kGplOptions[] = {1, 2, 4};
 constexpr int kNumGpl = 3;
 constexpr int32_t kMaxK = 1 << 20;
 
-// the x slice of one lane stays within 64 VGPRs (one group per lane always allowed)
-constexpr bool gpl_allowed(int M, int gpl) { return 16 * M * gpl <= 64 || gpl == 1; }
+// the x slice of one lane stays within 32 VGPRs (one group per lane always allowed)
+constexpr bool gpl_allowed(int M, int gpl) { return 16 * M * gpl <= 32 || gpl == 1; }
 
-template <int M, int GPL>
+template <int M, int GPL, bool MULTI>
 constexpr kernel_fn instance() {
-  if constexpr (gpl_allowed(M, GPL)) return &gemv_kernel<M, GPL>;
+  if constexpr (gpl_allowed(M, GPL)) return &gemv_kernel<M, GPL, MULTI>;
   return nullptr;
 }
 
-template <int M>
+template <int M, bool MULTI>
 constexpr kernel_fn pick(int gi) {
-  return gi == 0 ? instance<M, 1>() : gi == 1 ? instance<M, 2>() : instance<M, 4>();
+  return gi == 0 ? instance<M, 1, MULTI>() : gi == 1 ? instance<M, 2, MULTI>() : instance<M, 4, MULTI>();
 }
 
+template <bool MULTI>
 kernel_fn kernel_for(int M, int gi) {
   switch (M) {
-    case 1: return pick<1>(gi);
-    case 2: return pick<2>(gi);
-    case 3: return pick<3>(gi);
-    case 4: return pick<4>(gi);
-    case 5: return pick<5>(gi);
-    case 6: return pick<6>(gi);
-    case 7: return pick<7>(gi);
-    case 8: return pick<8>(gi);
+    case 1: return pick<1, MULTI>(gi);
+    case 2: return pick<2, MULTI>(gi);
+    case 3: return pick<3, MULTI>(gi);
+    case 4: return pick<4, MULTI>(gi);
+    case 5: return pick<5, MULTI>(gi);
+    case 6: return pick<6, MULTI>(gi);
+    case 7: return pick<7, MULTI>(gi);
+    case 8: return pick<8, MULTI>(gi);
     default: return nullptr;
   }
 }
@@ -285,27 +373,32 @@ struct LaunchShape {
   int nchunks;  // passes over K
 };
 
+LaunchShape shape_for_gpl(int M, int G, int gi) {
+  const int gpl = kGplOptions[gi];
+  const int wmax = max_waves(M, gpl);
+  const int nchunks = (G + wmax * 64 * gpl - 1) / (wmax * 64 * gpl);
+  const int waves = (G + nchunks * 64 * gpl - 1) / (nchunks * 64 * gpl);
+  return LaunchShape{gi, waves, nchunks};
+}
+
 // Fewest passes over K; then avoid leaving more than a quarter of the lanes
 // idle; then the fewest waves per workgroup; then the fewest idle lanes.
 LaunchShape choose_shape(int M, int G) {
   LaunchShape best{-1, 0, 0};
   long best_key[4] = {0, 0, 0, 0};
   for (int gi = kNumGpl - 1; gi >= 0; --gi) {
-    const int gpl = kGplOptions[gi];
-    if (!gpl_allowed(M, gpl)) continue;
-    const int wmax = max_waves(M, gpl);
-    const int nchunks = (G + wmax * 64 * gpl - 1) / (wmax * 64 * gpl);
-    const int waves = (G + nchunks * 64 * gpl - 1) / (nchunks * 64 * gpl);
-    const long slots = long(nchunks) * waves * 64 * gpl;
+    if (!gpl_allowed(M, kGplOptions[gi])) continue;
+    const LaunchShape s = shape_for_gpl(M, G, gi);
+    const long slots = long(s.nchunks) * s.waves * 64 * kGplOptions[gi];
     const long idle = slots - G;
-    const long key[4] = {nchunks, 4 * idle > slots ? 1 : 0, waves, idle};
+    const long key[4] = {s.nchunks, 4 * idle > slots ? 1 : 0, s.waves, idle};
     bool better = best.gi < 0;
     for (int i = 0; i < 4 && !better; ++i) {
       if (key[i] < best_key[i]) better = true;
       if (key[i] > best_key[i]) break;
     }
     if (better) {
-      best = LaunchShape{gi, waves, nchunks};
+      best = s;
       for (int i = 0; i < 4; ++i) best_key[i] = key[i];
     }
   }
@@ -324,6 +417,34 @@ int cu_count(int dev) {
   g_cu_count[dev].store(c, std::memory_order_relaxed);
   return c;
 }
+
+// Resident workgroups per CU of one instantiation at one block size, from the
+// runtime's occupancy calculator (cached; 0 = not yet queried). Every device
+// the library drives is a gfx950, so the answer does not depend on the device.
+std::atomic<int> g_occupancy[kMaxM + 1][kNumGpl][2][kMaxWaves + 1];
+
+int occupancy(int M, int gi, bool multi, int waves, kernel_fn fn) {
+  std::atomic<int>& slot = g_occupancy[M][gi][multi ? 1 : 0][waves];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), 64 * waves, 0) !=
+          hipSuccess ||
+      nb <= 0)
+    nb = 1;
+  slot.store(nb, std::memory_order_relaxed);
+  return nb;
+}
+
+#ifdef W4A16_TUNING
+// Sweep builds only: integer overrides from the environment (0 = unset).
+int tune(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+#else
+constexpr int tune(const char*) { return 0; }
+#endif
 
 bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; }
 
@@ -362,28 +483,34 @@ extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, 
     return W4A16_ERR_OVERLAP;
 
   const int G = K / kGroup;
-  const LaunchShape shape = choose_shape(M, G);
+  LaunchShape shape = choose_shape(M, G);
+  if (const int g = tune("W4A16_TUNE_GPL")) {  // sweep builds only
+    for (int gi = 0; gi < kNumGpl; ++gi)
+      if (kGplOptions[gi] == g && gpl_allowed(M, g)) shape = shape_for_gpl(M, G, gi);
+  }
   if (shape.gi < 0) return W4A16_ERR_SHAPE;
-  kernel_fn fn = kernel_for(M, shape.gi);
+  kernel_fn fn = shape.nchunks > 1 ? kernel_for<true>(M, shape.gi) : kernel_for<false>(M, shape.gi);
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int T = (N + kTileRows - 1) / kTileRows;
   const bool direct = shape.waves == 1 && shape.nchunks == 1;
-  const int units = direct ? T : (T + kTilesPerBlock - 1) / kTilesPerBlock;
-  const int cus = cu_count(dev);
-  // several workgroups per CU, each walking an equal share of the work units
-  const int waves_per_cu_target = 16;
-  const int max_grid = cus * ((waves_per_cu_target + shape.waves - 1) / shape.waves);
-  const int per = (units + max_grid - 1) / max_grid;
-  const int grid = (units + per - 1) / per;
+  // all workgroups resident at once, each walking an equal share of the tiles
+  int occ = occupancy(M, shape.gi, shape.nchunks > 1, shape.waves, fn);
+  if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
+  const int max_grid = cu_count(dev) * occ;
+  int tpb = direct ? 1 : T / max_grid;
+  tpb = tpb < 1 ? 1 : tpb > kTilesPerBlock ? kTilesPerBlock : tpb;
+  if (const int v = tune("W4A16_TUNE_TPB")) tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
+  const int units = (T + tpb - 1) / tpb;
+  const int grid = units < max_grid ? units : max_grid;
 
   const size_t codes_region = (size_t(N) * size_t(K) / 2 + 255) / 256 * 256;
   const u32x4* xp = static_cast<const u32x4*>(x);
   const u32x4* cp = static_cast<const u32x4*>(packed);
   const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(packed) + codes_region);
-  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks;
-  void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg};
+  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb;
+  void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg};
   if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return W4A16_ERR_HIP;
