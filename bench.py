@@ -4,15 +4,17 @@
 One step = the 128 GEMVs of 32 Llama-3-8B-shaped decoder layers at M = 1
 (fused QKV 4096->6144, O 4096->4096, fused gate-up 4096->28672, down
 14336->4096), each with its own seeded 4-bit group-32 weights, all resident in
-HBM (4.37 GB packed). The step is launched in stream order, the way a decode
-loop runs it (each GEMV starts after the previous one ends), captured once into
-a HIP graph and replayed.
+HBM (4.37 GB packed). The step runs as one w4a16_gemv_chain launch: the 128
+products in order, each one starting only after every earlier one's results
+are written (the ordering a decode loop needs), with the next product's weights
+streamed while that ordering point is reached. The same step as 128 separate
+launches replayed from a HIP graph is reported alongside.
 
 Printed: one JSON line with the whole-step throughput in algorithmic GB/s
 (N*K/2 code bytes + 4 bytes of scale/min per 32 weights + x + y, per GEMV),
-the roofline entry of the dominant kernel (event-timed per launch on the
-launch stream) and the fp64 oracle timed on this host's cores as a reported
-CPU baseline.
+the roofline entry of the chain kernel (event-timed per launch on the launch
+stream) and the fp64 oracle timed on this host's cores as a reported CPU
+baseline.
 """
 from __future__ import annotations
 
@@ -120,12 +122,25 @@ def cpu_baseline(budget_s=12.0):
     }
 
 
+def time_loop(torch, stream, fn, warmup, steps):
+    """Wall-clock seconds per call of fn() over `steps` calls after `warmup`."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -158,72 +173,64 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
 
-    # eager warm-up and a sanity spot check
+    # the decode step as one chained launch: plan and workspace made once
+    plan = torch.from_numpy(w4.w4a16_chain_plan(
+        [(g["x"], g["packed"], g["y"], g["N"], g["K"]) for g in gemvs], M)).to(dev)
+    workspace = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev)
+    plan_p, ws_p, count = plan.data_ptr(), workspace.data_ptr(), len(gemvs)
+
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    def chain_step():
+        st = w4.w4a16_gemv_chain_raw(plan_p, count, M, ws_p, ws_bytes, sh)
+        if st != 0:
+            raise w4.W4A16Error(st, "w4a16_gemv_chain")
+
+    # separate launches first (their outputs are the chain's reference), then the chain
     with torch.cuda.stream(stream):
         launch_step(w4, gemvs, sh)
     stream.synchronize()
     spot_check(w4, gemvs, torch)
-    log("[bench] spot check ok")
+    separate = [g["y"].clone() for g in gemvs]
+    for g in gemvs:
+        g["y"].fill_(float("nan"))
+    with torch.cuda.stream(stream):
+        chain_step()
+    stream.synchronize()
+    spot_check(w4, gemvs, torch)
+    worst = max(float(((g["y"] - r).abs() / (r.abs() + 1e-3)).max()) for g, r in zip(gemvs, separate))
+    if workspace.cpu().numpy().any():
+        raise AssertionError("chain workspace not clean after a call (counters, flags or error word)")
+    log(f"[bench] spot checks ok; chain vs separate launches: max rel diff {worst:.2e}")
 
-    graph = None
-    if args.mode == "graph":
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            launch_step(w4, gemvs, stream.cuda_stream)
-        torch.cuda.synchronize()
-
-    def run_steps(n):
-        with torch.cuda.stream(stream):
-            for _ in range(n):
-                if graph is not None:
-                    graph.replay()
-                else:
-                    launch_step(w4, gemvs, sh)
-
-    run_steps(args.warmup)
+    # separate launches, replayed from a HIP graph (reported alongside)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        launch_step(w4, gemvs, stream.cuda_stream)
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    run_steps(args.steps)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed / args.steps * 1e3
-    log(f"[bench] {args.mode}: {ms_per_step * 1e3:.1f} us/step")
+    sec_sep = time_loop(torch, stream, graph.replay, args.warmup, args.steps)
+    log(f"[bench] separate launches (graph): {sec_sep * 1e6:.1f} us/step")
 
-    # event timing of the same step: whole step, and every launch of each kernel
+    # the timed decode step: one chained launch per step
+    sec = time_loop(torch, stream, chain_step, args.warmup, args.steps)
+    ms_per_step = sec * 1e3
+    log(f"[bench] chain: {ms_per_step * 1e3:.1f} us/step")
+
+    # HIP events on the launch stream around every chain launch: its average
+    # duration, the figure rocprofv3 reports for the same kernel
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    e0, e1 = ev(), ev()
+    marks = []
     with torch.cuda.stream(stream):
-        e0.record(stream)
-        run_steps(args.steps)
-        e1.record(stream)
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            chain_step()
+            b.record(stream)
+            marks.append((a, b))
     torch.cuda.synchronize()
-    us_step_events = e0.elapsed_time(e1) / args.steps * 1e3
-
-    per_kernel = {}
-    ksteps = max(1, min(args.steps, 20))
-    with torch.cuda.stream(stream):
-        marks = []
-        for _ in range(ksteps):
-            for g in gemvs:
-                a, b = ev(), ev()
-                a.record(stream)
-                st = w4.w4a16_gemv_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], sh)
-                if st != 0:
-                    raise w4.W4A16Error(st, "w4a16_gemv")
-                b.record(stream)
-                marks.append((g, a, b))
-    torch.cuda.synchronize()
-    for g, a, b in marks:
-        k = per_kernel.setdefault(g["kernel"], {"launches": 0, "ms": 0.0, "bytes": 0})
-        k["launches"] += 1
-        k["ms"] += a.elapsed_time(b)
-        k["bytes"] += g["bytes"]
-    for name, k in per_kernel.items():
-        k["avg_us"] = k["ms"] / k["launches"] * 1e3
-        k["gbs"] = k["bytes"] / (k["ms"] * 1e-3) / 1e9
-        log(f"[bench] {name}: {k['launches']} launches, avg {k['avg_us']:.2f} us, {k['gbs']:.1f} GB/s")
-    dom_name = max(per_kernel, key=lambda n: per_kernel[n]["ms"])
-    dom = per_kernel[dom_name]
+    avg_us = sum(a.elapsed_time(b) for a, b in marks) / len(marks) * 1e3
+    achieved = step_bytes / (avg_us * 1e-6) / 1e9
+    log(f"[bench] chain kernel: avg {avg_us:.1f} us per launch, {achieved:.1f} GB/s")
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
@@ -246,21 +253,19 @@ def main():
                         "gate_up 4096->28672, down 14336->4096), M=1, 4-bit codes, group 32, fp16 scale+min",
             "gemvs_per_step": len(gemvs),
             "bytes_per_step": step_bytes,
-            "launch": args.mode,
-            "us_per_step_events": round(us_step_events, 2),
+            "launch": "chain: one w4a16_gemv_chain launch per step, products ordered on the device",
+            "separate_launches_us_per_step": round(sec_sep * 1e6, 2),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": dom_name,
-            "achieved": round(dom["gbs"], 2),
+            "kernel": "chain_kernel<1, 2, 4>",
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "avg_launch_us": round(dom["avg_us"], 3),
-            "bytes_per_launch": int(dom["bytes"] / dom["launches"]),
-            "per_kernel": {n: {"launches_per_step": k["launches"] // ksteps, "avg_us": round(k["avg_us"], 3),
-                               "gbs": round(k["gbs"], 1)} for n, k in per_kernel.items()},
+            "avg_launch_us": round(avg_us, 2),
+            "bytes_per_launch": step_bytes,
         },
     }
     if not args.no_cpu_baseline:

@@ -31,8 +31,20 @@ EXPORTS = (
     "w4a16_pack",
     "w4a16_gemv",
     "w4a16_launch_shape",
+    "w4a16_chain_plan_bytes",
+    "w4a16_chain_plan",
+    "w4a16_gemv_chain",
     "w4a16_status_string",
 )
+
+W4A16_CHAIN_WORKSPACE_BYTES = 69632
+W4A16_CHAIN_ERROR_OFFSET = 256  # uint32: nonzero once an ordering wait gave up
+
+
+class ChainEntry(ctypes.Structure):
+    """struct w4a16_chain_entry of include/w4a16.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32)]
 
 _lib = None
 
@@ -64,6 +76,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemv.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp]
     L.w4a16_launch_shape.restype = c_i32
     L.w4a16_launch_shape.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
+    L.w4a16_chain_plan_bytes.restype = c_sz
+    L.w4a16_chain_plan_bytes.argtypes = [c_i32]
+    L.w4a16_chain_plan.restype = c_i32
+    L.w4a16_chain_plan.argtypes = [ctypes.POINTER(ChainEntry), c_i32, c_i32, c_vp, c_sz]
+    L.w4a16_gemv_chain.restype = c_i32
+    L.w4a16_gemv_chain.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_status_string.argtypes = [c_i32]
     _lib = L
@@ -169,3 +187,48 @@ def upload_packed(blob: np.ndarray, device="cuda"):
     view = dev[off:off + host.numel()]
     view.copy_(host)
     return view
+
+
+def w4a16_chain_plan_bytes(count: int) -> int:
+    return int(lib().w4a16_chain_plan_bytes(int(count)))
+
+
+def w4a16_chain_plan(entries, M: int) -> np.ndarray:
+    """Host plan for w4a16_gemv_chain.
+
+    entries: sequence of (x, packed, y, N, K) where x/packed/y are device
+    tensors or raw device addresses. Returns the plan as a host uint8 array;
+    copy it to device memory (16-byte aligned) before calling the chain.
+    """
+    n = len(entries)
+    arr = (ChainEntry * max(n, 1))()
+    for i, (x, packed, y, N, K) in enumerate(entries):
+        arr[i] = ChainEntry(_ptr(x), _ptr(packed), _ptr(y), int(N), int(K))
+    nbytes = w4a16_chain_plan_bytes(n)
+    out = np.zeros(max(nbytes, 1), dtype=np.uint8)
+    st = lib().w4a16_chain_plan(arr, n, int(M), out.ctypes.data, out.nbytes if nbytes else 0)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_chain_plan")
+    return out
+
+
+def w4a16_gemv_chain_raw(plan_ptr: int, count: int, M: int, workspace_ptr: int, workspace_bytes: int,
+                         stream: int = 0) -> int:
+    """Direct C call with raw pointers; returns the status code."""
+    return int(lib().w4a16_gemv_chain(plan_ptr, int(count), int(M), workspace_ptr, int(workspace_bytes), stream))
+
+
+def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None) -> None:
+    """Enqueue a planned decode-step chain (plan and workspace are device tensors)."""
+    if stream is None:
+        import torch
+
+        s = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        s = stream.cuda_stream
+    else:
+        s = int(stream)
+    st = w4a16_gemv_chain_raw(_ptr(plan), count, M, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), s)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gemv_chain")

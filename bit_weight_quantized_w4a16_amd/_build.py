@@ -10,7 +10,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["csrc/w4a16_gemv.hip", "csrc/w4a16_pack.cpp"]
+SOURCES = ["csrc/w4a16_gemv.hip", "csrc/w4a16_chain.hip", "csrc/w4a16_pack.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

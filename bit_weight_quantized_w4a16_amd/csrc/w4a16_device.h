@@ -1,0 +1,203 @@
+// Device building blocks shared by the single-GEMV kernel and the chained
+// (whole decode step) kernel: the tile loads, the activation slice and the
+// per-tile dot products. Internal header of libw4a16.
+//
+// Notation: G = K/32 groups per row; a tile is 4 consecutive rows; a lane
+// owns GPL groups (group bases g0[j] are wave-uniform, the lane adds its
+// index); the packed layout is the one documented in include/w4a16.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace w4a16_dev {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 32;
+constexpr int kTileRows = 4;
+constexpr int kMaxWaves = 16;
+constexpr int kMaxM = 8;
+constexpr int kTilesPerBlock = 8;        // most tiles between two LDS reductions
+constexpr uint32_t kOnes = 0x3C003C00u;  // binary16 pair (1.0, 1.0)
+
+// Element i of a 4 x u32 vector. Written as an explicit select rather than
+// v[i]: with ROCm 7.2's clang, v[i] on an unrolled index inside the tile loop
+// was folded to v[0] (the scale/min load shrank to one dword and every row of
+// a tile used row 0's scale), so vector elements are only ever read this way.
+__device__ __forceinline__ uint32_t elem(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
+template <int GPL>
+struct TileLoads {
+  u32x4 sm[GPL];
+  u32x4 code[kTileRows][GPL];
+};
+
+// Issue the 16-byte non-temporal loads of tile t (rows 4t..4t+3) for the
+// groups g0[j] + lane. Lanes past G and rows past N load nothing (zeros).
+template <int GPL>
+__device__ __forceinline__ void fetch_tile(const u32x4* __restrict__ codes, const u32x4* __restrict__ sm, int N,
+                                           int G, int t, const int (&g0)[GPL], int lane, TileLoads<GPL>& L) {
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const bool ok = lane < G - g0[j];
+    const u32x4* sp = sm + (size_t(t) * G + g0[j]);
+    L.sm[j] = u32x4{0, 0, 0, 0};
+    if (ok) L.sm[j] = __builtin_nontemporal_load(sp + lane);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const int n = t * kTileRows + r;
+      const u32x4* cp = codes + (size_t(n) * G + g0[j]);
+      L.code[r][j] = u32x4{0, 0, 0, 0};
+      if (ok && n < N) L.code[r][j] = __builtin_nontemporal_load(cp + lane);
+    }
+  }
+}
+
+// This lane's slice x[m][32g .. 32g+31] of every activation row for the
+// groups g = g0[j] + lane, loaded straight into the registers that keep it,
+// plus the per-group sums used by the min term.
+template <int M, int GPL>
+__device__ __forceinline__ void load_x(const u32x4* __restrict__ x, int G, const int (&g0)[GPL], int lane,
+                                       u32x4 (&xv)[M][GPL][4], float (&xs)[M][GPL]) {
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int g = g0[j] + lane;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[m][j][q] = u32x4{0, 0, 0, 0};
+      if (g < G) {
+        const u32x4* p = x + (size_t(m) * G + g) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[m][j][q] = p[q];
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = dot2(elem(xv[m][j][q], e), kOnes, s);
+      }
+      xs[m][j] = s;
+    }
+  }
+}
+
+// Wave-wide partial row sums of one tile over this wave's groups:
+// acc[r][m] = sum over the wave's groups g of
+//   scale[4t+r][g] * sum_k q*x[m][k] + min[4t+r][g] * sum_k x[m][k].
+// sum_k q*x is formed with v_dot2c_f32_f16 on binary16 subnormal pairs: the
+// packed word AND 0x000F000F is a pair of halfs whose bit patterns are the
+// codes (values q * 2^-24), AND 0x00F000F0 gives q * 2^-20. Both are exact,
+// so are their products with x in fp32, and no offset is cancelled later.
+template <int M, int GPL>
+__device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const u32x4 (&xv)[M][GPL][4],
+                                             const float (&xs)[M][GPL], float (&acc)[kTileRows][M]) {
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float lo[M], hi[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = elem(L.code[r][j], d);
+        const uint32_t w8 = w >> 8;
+        const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
+        const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
+        const uint32_t pc = w8 & 0x000F000Fu;  // k = 8d+4, 8d+5  -> q * 2^-24
+        const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const u32x4& xq = xv[m][j][d];  // x[8d .. 8d+7] of this group
+          lo[m] = dot2(pa, elem(xq, 0), lo[m]);
+          hi[m] = dot2(pb, elem(xq, 1), hi[m]);
+          lo[m] = dot2(pc, elem(xq, 2), lo[m]);
+          hi[m] = dot2(pd, elem(xq, 3), hi[m]);
+        }
+      }
+      const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
+      const float sc = float(h[0]) * 0x1p20f;
+      const float mn = float(h[1]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[m], 16.f, hi[m]), acc[r][m]);
+        acc[r][m] = __builtin_fmaf(mn, xs[m][j], acc[r][m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kTileRows; ++r) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  }
+}
+
+// Store one result. COHERENT stores go through to device-coherent memory
+// (a relaxed agent-scope atomic store, "sc1"), so a later reader on any XCD
+// sees them after the usual ordering point without any L2 write-back.
+template <bool COHERENT>
+__device__ __forceinline__ void store_y(float* p, float v) {
+  if constexpr (COHERENT)
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), __builtin_bit_cast(unsigned, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// A wave that covers all of K for its tile writes the tile's 4*M results
+// itself: lane r*M + m stores y[m][4t + r].
+template <int M, bool COHERENT = false>
+__device__ __forceinline__ void store_tile(const float (&acc)[kTileRows][M], float* __restrict__ y, int N, int t,
+                                           int lane) {
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTileRows * M; ++i)
+    if (lane == i) v = acc[i / M][i % M];
+  if (lane < kTileRows * M) {
+    const int n = t * kTileRows + lane / M;
+    if (n < N) store_y<COHERENT>(y + size_t(lane % M) * N + n, v);
+  }
+}
+
+// Up to four activation rows the next tile's loads are issued before the
+// current tile is computed (two load buffers); beyond that the kernel is
+// bound by VALU work and the registers go to the x slices instead.
+__host__ __device__ constexpr bool double_buffered(int M) { return M <= 4; }
+
+}  // namespace w4a16_dev

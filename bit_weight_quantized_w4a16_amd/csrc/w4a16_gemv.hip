@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) kernels and C-ABI entry point of the W4A16 decode GEMV.
+// gfx950 (CDNA4) kernel and C-ABI entry point of one W4A16 decode GEMV.
 //
 // y[m][n] = sum_k (scale[n][k/32] * q[n][k] + min[n][k/32]) * x[m][k]
 //
@@ -8,7 +8,7 @@
 // therefore a streaming kernel, not a contraction: no MFMA (M <= 8 rows of
 // activations are far too few for a matrix-core tile to pay), every weight
 // byte is loaded once with a 128-bit non-temporal load, and the VALU work per
-// weight is kept to about 0.6 bitwise ops + M/2 packed dot products.
+// weight is about 0.6 bitwise ops + M/2 packed dot products.
 //
 // Work decomposition
 //   * a lane owns GPL groups of 32 k along K (group g = (wave*GPL + j)*64 +
@@ -21,13 +21,6 @@
 //     wave instruction moves 1 KiB. The loads of the next tile are issued
 //     before the current tile is computed, and the first tile's loads go out
 //     before x is fetched, so the two start-up latencies overlap;
-//   * per group a lane computes sum_k q*x with v_dot2c_f32_f16 on binary16
-//     *subnormal* pairs: AND-ing a packed word with 0x000F000F gives two halfs
-//     whose bit patterns are the codes, i.e. the values q * 2^-24, and with
-//     0x00F000F0 the values q * 2^-20. Both are exact, the products with x are
-//     exact in fp32, and no offset has to be cancelled later, so an all-zero
-//     weight row gives exactly zero. The group result is folded in fp32 as
-//     scale * 2^20 * (16*lo + hi) + min * sum_{k in g} x[k];
 //   * lane partials are summed across the wave with DPP and lane shuffles,
 //     across waves through LDS, in a fixed order: results are bitwise
 //     repeatable, no atomics are used and y is overwritten.
@@ -35,54 +28,14 @@
 
 #include <atomic>
 #include <cstdint>
-#include <cstdlib>
 
 #include "w4a16.h"
+#include "w4a16_device.h"
+#include "w4a16_host.h"
+
+using namespace w4a16_dev;
 
 namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kGroup = 32;
-constexpr int kTileRows = 4;
-constexpr int kMaxWaves = 16;
-constexpr int kMaxM = 8;
-constexpr uint32_t kOnes = 0x3C003C00u;  // binary16 pair (1.0, 1.0)
-
-// Element i of a 4 x u32 vector. Written as an explicit select rather than
-// v[i]: with ROCm 7.2's clang, v[i] on an unrolled index inside the tile loop
-// was folded to v[0] (the scale/min load shrank to one dword and every row of
-// a tile used row 0's scale), so vector elements are only ever read this way.
-__device__ __forceinline__ uint32_t elem(const u32x4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wave; every lane ends with the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-
-// Up to four activation rows the next tile's loads are issued before the
-// current tile is computed (two load buffers); beyond that the kernel is
-// bound by VALU work and the registers go to the x slices instead.
-__host__ __device__ constexpr bool double_buffered(int M) { return M <= 4; }
 
 // Waves per workgroup an instantiation may use: its VGPR estimate (x slice,
 // tile loads in flight, accumulators) must fit the 512-entry register file
@@ -91,19 +44,8 @@ __host__ __device__ constexpr int max_waves(int M, int GPL) {
   return (16 * M * GPL + (double_buffered(M) ? 40 : 20) * GPL + 6 * M + 30) <= 128 ? 16 : 8;
 }
 
-// Most tiles of 4 rows handled between two workgroup barriers when partial
-// sums go through LDS.
-constexpr int kTilesPerBlock = 8;
-
-// Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
-template <int GPL>
-struct TileLoads {
-  u32x4 sm[GPL];
-  u32x4 code[kTileRows][GPL];
-};
-
 // MULTI: K takes more than one pass of the workgroup, so x is re-fetched per
-// pass inside the tile loop; otherwise x is fetched once, before it.
+// pass; otherwise x is fetched once, after the first tile's loads.
 template <int M, int GPL, bool MULTI>
 __global__ void __launch_bounds__(64 * max_waves(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
@@ -117,115 +59,20 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
   const bool direct = (nwaves == 1 && nchunks == 1);
   const int nblocks = (T + tpb - 1) / tpb;
 
-  // first group of slot j of this wave in pass c; the lane adds its index
-  auto group_base = [&](int c, int j) { return c * chunk_groups + (wave * GPL + j) * 64; };
-
-  // issue the 16-byte non-temporal loads of tile t, pass c over K
-  auto fetch = [&](int t, int c, TileLoads<GPL>& L) {
+  auto bases = [&](int c, int (&g0)[GPL]) {
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const int g0 = group_base(c, j);
-      const bool ok = lane < G - g0;
-      const u32x4* sp = sm + (size_t(t) * G + g0);
-      L.sm[j] = u32x4{0, 0, 0, 0};
-      if (ok) L.sm[j] = __builtin_nontemporal_load(sp + lane);
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const int n = t * kTileRows + r;
-        const u32x4* cp = codes + (size_t(n) * G + g0);
-        L.code[r][j] = u32x4{0, 0, 0, 0};
-        if (ok && n < N) L.code[r][j] = __builtin_nontemporal_load(cp + lane);
-      }
-    }
+    for (int j = 0; j < GPL; ++j) g0[j] = c * chunk_groups + (wave * GPL + j) * 64;
   };
 
-  // this lane's slice of pass c of every activation row (loaded straight
-  // into the registers that keep it), plus its group sums
   u32x4 xv[M][GPL][4];
   float xs[M][GPL];
-  auto load_x = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const int g = group_base(c, j) + lane;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[m][j][q] = u32x4{0, 0, 0, 0};
-        if (g < G) {
-          const u32x4* p = x + (size_t(m) * G + g) * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) xv[m][j][q] = p[q];
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-#pragma unroll
-      for (int j = 0; j < GPL; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s = dot2(elem(xv[m][j][q], e), kOnes, s);
-        }
-        xs[m][j] = s;
-      }
-    }
-  };
-
-  // wave-wide row sums of one tile over this wave's groups of the current pass
-  auto compute = [&](const TileLoads<GPL>& L, float (&acc)[kTileRows][M]) {
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-#pragma unroll
-      for (int j = 0; j < GPL; ++j) {
-        float lo[M], hi[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = elem(L.code[r][j], d);
-          const uint32_t w8 = w >> 8;
-          const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
-          const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
-          const uint32_t pc = w8 & 0x000F000Fu;  // k = 8d+4, 8d+5  -> q * 2^-24
-          const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const u32x4& xq = xv[m][j][d];  // x[8d .. 8d+7] of this group
-            lo[m] = dot2(pa, elem(xq, 0), lo[m]);
-            hi[m] = dot2(pb, elem(xq, 1), hi[m]);
-            lo[m] = dot2(pc, elem(xq, 2), lo[m]);
-            hi[m] = dot2(pd, elem(xq, 3), hi[m]);
-          }
-        }
-        const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
-        const float sc = float(h[0]) * 0x1p20f;
-        const float mn = float(h[1]);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[m], 16.f, hi[m]), acc[r][m]);
-          acc[r][m] = __builtin_fmaf(mn, xs[m][j], acc[r][m]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
-    }
-  };
 
   // per-wave partials of one block of tiles: [tile][row][m][wave]
   __shared__ float part[kTilesPerBlock][kTileRows][M][kMaxWaves];
 
   // This workgroup walks items (block b, pass c, tile tb of the block) for
-  // b = blockIdx.x, blockIdx.x + gridDim.x, ...; the loads of the next item
-  // are in flight while the current one is computed (two load buffers used
-  // alternately). Every wave of the workgroup walks the same items, so the
-  // barriers below are uniform.
+  // b = blockIdx.x, blockIdx.x + gridDim.x, ... Every wave of the workgroup
+  // walks the same items, so the barriers below are uniform.
   struct Item {
     int b, c, tb;
   };
@@ -240,21 +87,24 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
     }
     return n;
   };
+  auto fetch = [&](Item it, TileLoads<GPL>& L) {
+    int g0[GPL];
+    bases(it.c, g0);
+    fetch_tile<GPL>(codes, sm, N, G, it.b * tpb + it.tb, g0, lane, L);
+  };
+  auto fetch_x = [&](int c) {
+    int g0[GPL];
+    bases(c, g0);
+    load_x<M, GPL>(x, G, g0, lane, xv, xs);
+  };
   // compute item `it` from its loads, emit or stage its results; `nb` is the
   // block of the item after it (a new block closes block it.b)
   auto finish = [&](const TileLoads<GPL>& L, Item it, int nb) {
     const int t = it.b * tpb + it.tb;
     float acc[kTileRows][M];
-    compute(L, acc);
+    compute_tile<M, GPL>(L, xv, xs, acc);
     if (direct) {
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < kTileRows * M; ++i)
-        if (lane == i) v = acc[i / M][i % M];
-      if (lane < kTileRows * M) {
-        const int n = t * kTileRows + lane / M;
-        if (n < N) y[size_t(lane % M) * N + n] = v;
-      }
+      store_tile<M>(acc, y, N, t, lane);
       return;
     }
     if (lane == 0) {
@@ -289,11 +139,11 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
     // the top of the pass and stays in registers for the block's tiles
     for (int b = ia.b; b < nblocks; b += gridDim.x) {
       for (int c = 0; c < nchunks; ++c) {
-        load_x(c);
+        fetch_x(c);
         const int ntiles = min(tpb, T - b * tpb);
         for (int tb = 0; tb < ntiles; ++tb) {
           TileLoads<GPL> la;
-          fetch(b * tpb + tb, c, la);
+          fetch(Item{b, c, tb}, la);
           const bool last = (c == nchunks - 1) && (tb == ntiles - 1);
           finish(la, Item{b, c, tb}, last ? b + int(gridDim.x) : b);
         }
@@ -301,15 +151,15 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
     }
   } else if constexpr (double_buffered(M)) {
     TileLoads<GPL> la, lb;
-    fetch(ia.b * tpb + ia.tb, ia.c, la);
-    load_x(0);  // after the first tile's loads, so both latencies overlap
+    fetch(ia, la);
+    fetch_x(0);  // after the first tile's loads, so both latencies overlap
     while (true) {
       const Item ib = next_item(ia);
-      if (ib.b < nblocks) fetch(ib.b * tpb + ib.tb, ib.c, lb);
+      if (ib.b < nblocks) fetch(ib, lb);
       finish(la, ia, ib.b);
       if (ib.b >= nblocks) break;
       ia = next_item(ib);
-      if (ia.b < nblocks) fetch(ia.b * tpb + ia.tb, ia.c, la);
+      if (ia.b < nblocks) fetch(ia, la);
       finish(lb, ib, ia.b);
       if (ia.b >= nblocks) break;
     }
@@ -317,8 +167,8 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
     bool first = true;
     while (true) {
       TileLoads<GPL> la;
-      fetch(ia.b * tpb + ia.tb, ia.c, la);
-      if (first) load_x(0);
+      fetch(ia, la);
+      if (first) fetch_x(0);
       first = false;
       const Item ib = next_item(ia);
       finish(la, ia, ib.b);
@@ -405,48 +255,19 @@ LaunchShape choose_shape(int M, int G) {
   return best;
 }
 
-// per-device cache of the compute-unit count (0 = not yet queried)
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];
-
-int cu_count(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return 256;
-  int c = g_cu_count[dev].load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-  g_cu_count[dev].store(c, std::memory_order_relaxed);
-  return c;
-}
-
-// Resident workgroups per CU of one instantiation at one block size, from the
-// runtime's occupancy calculator (cached; 0 = not yet queried). Every device
-// the library drives is a gfx950, so the answer does not depend on the device.
+// Resident workgroups per CU of one instantiation at one block size (cached;
+// 0 = not yet queried). Every device the library drives is a gfx950, so the
+// answer does not depend on the device.
 std::atomic<int> g_occupancy[kMaxM + 1][kNumGpl][2][kMaxWaves + 1];
 
 int occupancy(int M, int gi, bool multi, int waves, kernel_fn fn) {
   std::atomic<int>& slot = g_occupancy[M][gi][multi ? 1 : 0][waves];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), 64 * waves, 0) !=
-          hipSuccess ||
-      nb <= 0)
-    nb = 1;
-  slot.store(nb, std::memory_order_relaxed);
-  return nb;
+  v = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * waves);
+  slot.store(v, std::memory_order_relaxed);
+  return v;
 }
-
-#ifdef W4A16_TUNING
-// Sweep builds only: integer overrides from the environment (0 = unset).
-int tune(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-#else
-constexpr int tune(const char*) { return 0; }
-#endif
-
-bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; }
 
 }  // namespace
 
@@ -470,6 +291,8 @@ extern "C" w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int3
 
 extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, int32_t M, int32_t N,
                                    int32_t K, void* stream) {
+  using w4a16_host::ranges_overlap;
+  using w4a16_host::tune;
   if (!x || !packed || !y) return W4A16_ERR_NULL;
   if (M < 1 || M > kMaxM || N < 1 || K < kGroup || K % kGroup || K > w4a16_max_k(M)) return W4A16_ERR_SHAPE;
   const size_t packed_bytes = w4a16_packed_bytes(N, K);
@@ -498,7 +321,7 @@ extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, 
   // all workgroups resident at once, each walking an equal share of the tiles
   int occ = occupancy(M, shape.gi, shape.nchunks > 1, shape.waves, fn);
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
-  const int max_grid = cu_count(dev) * occ;
+  const int max_grid = w4a16_host::cu_count(dev) * occ;
   int tpb = direct ? 1 : T / max_grid;
   tpb = tpb < 1 ? 1 : tpb > kTilesPerBlock ? kTilesPerBlock : tpb;
   if (const int v = tune("W4A16_TUNE_TPB")) tpb = v > kTilesPerBlock ? kTilesPerBlock : v;

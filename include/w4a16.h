@@ -137,6 +137,79 @@ w4a16_status w4a16_gemv(const void* x, const void* packed, float* y,
  */
 w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int32_t out[3]);
 
+/*
+ * Decode-step chain: the GEMVs of a whole decode step in ONE kernel launch.
+ *
+ * The runtime traits of the core-modules page (section 5.2: a tight decode
+ * loop, static shapes fixed before the loop) and its scheduler enhancements
+ * (section 5.3: prefetch the next matrix product's weights while other work
+ * runs) motivate it: a decode step runs the same list of products every
+ * token, each product's input usually depends on the previous one's output,
+ * and on an MI355X a kernel boundary costs about as much as streaming 10 MB
+ * of weights. The chain runs the list in order inside one persistent launch;
+ * before each product it waits (on a device-side counter) until every
+ * earlier product's results are written, and while it waits the next
+ * product's weights are already being streamed, since weights never depend
+ * on earlier results.
+ */
+typedef struct w4a16_chain_entry {
+  const void* x;       /* device binary16 [M][K], 16-byte aligned */
+  const void* packed;  /* device blob from w4a16_pack for (N, K), 256-byte aligned */
+  float* y;            /* device fp32 [M][N], 4-byte aligned, overwritten */
+  int32_t N;           /* output features, >= 1 */
+  int32_t K;           /* input features, multiple of 32, 32 <= K <= w4a16_max_k(M) */
+} w4a16_chain_entry;
+
+/* Bytes of the device workspace of w4a16_gemv_chain. */
+#define W4A16_CHAIN_WORKSPACE_BYTES 69632
+
+/* Bytes of the plan for `count` entries (0 if count < 1 or too large). */
+size_t w4a16_chain_plan_bytes(int32_t count);
+
+/*
+ * w4a16_chain_plan - host only, init time: validate a list of products that
+ * share the activation-row count M and write the device-ready plan into the
+ * caller's host buffer `plan` (at least w4a16_chain_plan_bytes(count) bytes).
+ * The caller copies the plan to device memory (16-byte aligned) and keeps it
+ * for as many steps as the buffers it names stay put.
+ * Rules, each checked here: every entry is a valid w4a16_gemv call for M
+ * (shape, alignment, y disjoint from its own x and packed blob); no packed
+ * blob intersects any entry's y (weights are read ahead of the ordering
+ * point). An entry's x MAY overlap an earlier entry's y: that is the
+ * dependency the chain honours.
+ * Errors: NULL -> W4A16_ERR_NULL; bad count/M/shape -> W4A16_ERR_SHAPE;
+ * alignment -> W4A16_ERR_ALIGN; plan_bytes too small -> W4A16_ERR_SIZE;
+ * overlap -> W4A16_ERR_OVERLAP. Nothing is written on error. Touches no GPU.
+ */
+w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32_t count, int32_t M, void* plan,
+                              size_t plan_bytes);
+
+/*
+ * w4a16_gemv_chain - enqueue the planned products on `stream` as one kernel.
+ * The results are those of w4a16_gemv on each entry in order, up to the fp32
+ * summation order (within the same tolerance, and bitwise repeatable from
+ * run to run); entry i observes every y written by entries 0..i-1.
+ *   plan       device copy of a plan from w4a16_chain_plan(..., count, M, ...)
+ *   workspace  device buffer of workspace_bytes >= W4A16_CHAIN_WORKSPACE_BYTES,
+ *              16-byte aligned, zero-filled by the caller once before its first use;
+ *              every call leaves its counters at zero again. The uint32 at
+ *              byte offset 256 becomes nonzero if an ordering wait ever gave
+ *              up (waits bound their spin so a starved launch cannot hang
+ *              the GPU); results of such a call are invalid. Calls that
+ *              share a workspace must not run concurrently.
+ * The plan and workspace are owned by the caller. The call only enqueues.
+ * The launch keeps all of its workgroups resident (grid sized from the
+ * occupancy of the kernel); other work running concurrently on the device
+ * can delay it but not deadlock it.
+ * Errors (host side): NULL -> W4A16_ERR_NULL; count < 1 or M outside 1..8 ->
+ * W4A16_ERR_SHAPE; misaligned plan or workspace -> W4A16_ERR_ALIGN;
+ * workspace_bytes too small -> W4A16_ERR_SIZE; launch rejected ->
+ * W4A16_ERR_HIP. A plan whose header does not match (count, M)
+ * is detected on the device: the kernel then writes nothing.
+ */
+w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* w4a16_status_string(int32_t status);
 

@@ -127,3 +127,80 @@ def test_launch_shape_host_logic(w4a16_lib):
     with pytest.raises(w4.W4A16Error):
         shp(9, 5, 64)
     assert w4a16_lib.w4a16_launch_shape(1, 1, 64, None) == w4.W4A16_ERR_NULL
+
+
+# ------------------------------------------------------------ decode-step chain
+
+def _plan_fields(plan, count):
+    hdr = plan[:64].view("<u4")
+    ents = []
+    for i in range(count):
+        raw = plan[64 + 64 * i: 128 + 64 * i]
+        ptrs = raw[:32].view("<u8")
+        ints = raw[32:52].view("<i4")
+        ents.append((*[int(p) for p in ptrs], *[int(v) for v in ints]))
+    return hdr, ents
+
+
+def test_chain_plan_layout(w4a16_lib):
+    B = 0x7F0000000000
+    entries = [
+        (B, B + 2**24, B + 2**30, 6144, 4096),            # K = 4096: one wave per tile
+        (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # four waves per tile
+        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # four waves, two passes
+    ]
+    plan = w4.w4a16_chain_plan(entries, 1)
+    assert plan.size == w4.w4a16_chain_plan_bytes(3) == 64 + 3 * 64
+    hdr, ents = _plan_fields(plan, 3)
+    assert hdr[0] == 0x48433457 and hdr[1] == 2 and hdr[2] == 3 and hdr[3] == 1 and hdr[5] == 12
+    for (x, p, y, N, K), e in zip(entries, ents):
+        ex, ecodes, esm, ey, eN, eG, eT, wpr, passes = e
+        assert (ex, ecodes, ey, eN, eG, eT) == (x, p, y, N, K // 32, (N + 3) // 4)
+        assert esm == p + (N * K // 2 + 255) // 256 * 256
+        assert wpr * 128 * passes >= K // 32             # M = 1 uses two groups per lane
+    assert [e[7:] for e in ents] == [(1, 1), (4, 1), (6, 2)]        # teams divide 12 waves
+    plan8 = w4.w4a16_chain_plan(entries[:2], 8)
+    _, e8 = _plan_fields(plan8, 2)
+    assert [e[7:] for e in e8] == [(2, 1), (2, 4)]       # M = 8: 128 groups of x per LDS pass
+
+
+def test_chain_plan_errors(w4a16_lib):
+    L = w4a16_lib
+    B = 0x7F0000000000
+    good = (B, B + 2**24, B + 2**30, 64, 64)
+    buf = np.zeros(4096, np.uint8)
+
+    def plan(entries, M=1, nbytes=None):
+        arr = (w4.ChainEntry * len(entries))(*[w4.ChainEntry(*e) for e in entries])
+        return L.w4a16_chain_plan(arr, len(entries), M, buf.ctypes.data, buf.nbytes if nbytes is None else nbytes)
+
+    assert plan([good]) == w4.W4A16_OK
+    assert L.w4a16_chain_plan(None, 1, 1, buf.ctypes.data, buf.nbytes) == w4.W4A16_ERR_NULL
+    assert plan([(0, B + 2**24, B + 2**30, 64, 64)]) == w4.W4A16_ERR_NULL
+    assert plan([good], M=0) == w4.W4A16_ERR_SHAPE
+    assert plan([good], M=9) == w4.W4A16_ERR_SHAPE
+    assert plan([(B, B + 2**24, B + 2**30, 64, 48)]) == w4.W4A16_ERR_SHAPE
+    assert plan([(B, B + 2**24, B + 2**30, 0, 64)]) == w4.W4A16_ERR_SHAPE
+    assert plan([(B + 8, B + 2**24, B + 2**30, 64, 64)]) == w4.W4A16_ERR_ALIGN
+    assert plan([(B, B + 2**24 + 16, B + 2**30, 64, 64)]) == w4.W4A16_ERR_ALIGN
+    assert plan([good], nbytes=127) == w4.W4A16_ERR_SIZE
+    assert plan([(B, B + 2**24, B + 32, 64, 64)]) == w4.W4A16_ERR_OVERLAP          # y over its own x
+    # a later entry's y lands inside an earlier entry's weights
+    assert plan([good, (B + 2**20, B + 2**25, B + 2**24 + 512, 64, 64)]) == w4.W4A16_ERR_OVERLAP
+    # a later entry reading an earlier entry's y is the allowed dependency
+    assert plan([good, (B + 2**30, B + 2**25, B + 2**31, 64, 64)]) == w4.W4A16_OK
+    assert L.w4a16_chain_plan_bytes(0) == 0 and L.w4a16_chain_plan_bytes(-3) == 0
+
+
+def test_chain_call_rejects_before_any_hip_call(w4a16_lib):
+    L = w4a16_lib
+    B = 0x7F0000000000
+    W = w4.W4A16_CHAIN_WORKSPACE_BYTES
+    assert L.w4a16_gemv_chain(None, 1, 1, B, W, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemv_chain(B, 1, 1, None, W, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemv_chain(B, 0, 1, B + 4096, W, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemv_chain(B, 1, 9, B + 4096, W, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemv_chain(B + 8, 1, 1, B + 4096, W, None) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_gemv_chain(B, 1, 1, B + 4100, W, None) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_gemv_chain(B, 1, 1, B + 4096, W - 1, None) == w4.W4A16_ERR_SIZE
+    assert L.w4a16_gemv_chain(B, 1, 1, B + 4096, 256, None) == w4.W4A16_ERR_SIZE

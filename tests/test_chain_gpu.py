@@ -1,0 +1,165 @@
+"""GPU tests of the decode-step chain (w4a16_gemv_chain) through the C ABI.
+
+* parity with the fp64 oracle on mixed shapes, every M;
+* a real dependency: product 1 reads product 0's fp32 output as its binary16
+  input, so running it before product 0 finished would read stale memory;
+* agreement with separate w4a16_gemv launches (bitwise where the launch
+  shapes coincide);
+* the workspace is left zeroed and error-free after every call;
+* a plan whose header does not match the call writes nothing;
+* the chain captured in a HIP graph and replayed, with eager work and
+  synchronisation between replays, matches the eager result every time.
+"""
+import numpy as np
+import pytest
+
+import bit_weight_quantized_w4a16_amd as w4
+import oracle
+import workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+class Chain:
+    """Device buffers and plan for a list of (x, codes, scale, min) problems."""
+
+    def __init__(self, problems, M, y_fill=float("nan")):
+        self.M = M
+        self.items = []
+        for x, codes, scale, mn in problems:
+            packed = w4.upload_packed(w4.w4a16_pack(codes, scale, mn), DEV)
+            xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if x is not None else None
+            y = torch.full((M, codes.shape[0]), y_fill, dtype=torch.float32, device=DEV)
+            self.items.append(dict(x=xd, packed=packed, y=y, N=codes.shape[0], K=codes.shape[1] * 2))
+        self.workspace = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4, dtype=torch.int32, device=DEV)
+
+    def plan(self, M=None):
+        entries = [(it["x"], it["packed"], it["y"], it["N"], it["K"]) for it in self.items]
+        host = w4.w4a16_chain_plan(entries, self.M if M is None else M)
+        self.plan_dev = torch.from_numpy(host).to(DEV)
+        return self.plan_dev
+
+    def run(self, stream=None, M=None):
+        w4.w4a16_gemv_chain(self.plan_dev, len(self.items), self.M if M is None else M, self.workspace, stream)
+
+
+def check(y, y_ref, B, label):
+    ok = oracle.within_tolerance(y, y_ref, B)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        pytest.fail(f"{label}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. "
+                    f"{[(tuple(i), y[tuple(i)], y_ref[tuple(i)]) for i in bad]}")
+
+
+def assert_workspace_clean(ch):
+    ws = ch.workspace.cpu().numpy()
+    assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == 0, "an ordering wait gave up"
+    assert not ws.any(), f"counters or flags not reset: {np.flatnonzero(ws)[:8]}"
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_chain_mixed_shapes_vs_oracle(w4a16_lib, M):
+    shapes = [(4097, 4096), (3, 64), (130, 14336), (64, 8192), (21, 28672), (517, 96)]
+    problems = [workload.random_problem(300 + i * 7 + M, M, N, K, outliers=True) for i, (N, K) in enumerate(shapes)]
+    print(f"[chain] M={M} shapes={shapes}", flush=True)
+    ch = Chain(problems, M)
+    ch.plan()
+    ch.run()
+    torch.cuda.synchronize()
+    for it, (x, codes, scale, mn) in zip(ch.items, problems):
+        y_ref, B = oracle.gemv(x, codes, scale, mn)
+        check(it["y"].cpu().numpy().astype(np.float64), y_ref, B, f"M={M} N={it['N']} K={it['K']}")
+    assert_workspace_clean(ch)
+
+
+def _dependent_problems(seed):
+    """Product 0 gives small non-negative integers y0 (< 256, so their fp32 low
+    halves are zero); product 1 reads y0's bytes as 2*N0 binary16 values."""
+    rng = np.random.default_rng(seed)
+    N0, K0 = 96, 64
+    x0 = np.ones((1, K0), np.float16)
+    q0 = rng.integers(0, 8, size=(N0, K0))                  # sum of 64 codes < 8*64 = 512
+    q0[:, 32:] = 0                                          # keep y0 <= 7*32 = 224 < 256
+    codes0 = (q0[:, 0::2] | (q0[:, 1::2] << 4)).astype(np.uint8)
+    scale0 = np.ones((N0, K0 // 32), np.float16)
+    min0 = np.zeros((N0, K0 // 32), np.float16)
+    y0 = q0.sum(axis=1).astype(np.float32)[None, :]         # exact
+    x1 = y0.view(np.float16)                                # [1, 2*N0] = [1, 192]
+    K1 = x1.shape[1]
+    _, codes1, scale1, min1 = workload.random_problem(seed + 1, 1, 77, K1)
+    return (x0, codes0, scale0, min0), (x1, codes1, scale1, min1), y0
+
+
+def test_chain_honours_read_after_write(w4a16_lib):
+    p0, p1, y0_exact = _dependent_problems(5)
+    # product 1's x is product 0's y: build the chain by hand so that entry 1
+    # points its x at entry 0's output buffer; that buffer starts as garbage
+    ch = Chain([p0, (None, p1[1], p1[2], p1[3])], 1, y_fill=3.0)
+    ch.items[1]["x"] = ch.items[0]["y"]
+    ch.plan()
+    for rep in range(3):
+        ch.items[0]["y"].fill_(3.0)           # stale contents: 3.0f reads as binary16 (0, 2.125)
+        ch.items[1]["y"].fill_(float("nan"))
+        ch.run()
+        torch.cuda.synchronize()
+        y0 = ch.items[0]["y"].cpu().numpy()
+        assert np.array_equal(y0, y0_exact)
+        y_ref, B = oracle.gemv(p1[0], p1[1], p1[2], p1[3])
+        check(ch.items[1]["y"].cpu().numpy().astype(np.float64), y_ref, B, f"dependent product, rep {rep}")
+        assert_workspace_clean(ch)
+
+
+def test_chain_matches_separate_launches(w4a16_lib):
+    shapes = [(6144, 4096), (4096, 4096), (2048, 14336), (1000, 4096)]
+    problems = [workload.random_problem(400 + i, 1, N, K, outliers=True) for i, (N, K) in enumerate(shapes)]
+    ch = Chain(problems, 1)
+    ch.plan()
+    ch.run()
+    torch.cuda.synchronize()
+    for it in ch.items:
+        y = torch.empty_like(it["y"])
+        w4.w4a16_gemv(it["x"], it["packed"], y)
+        torch.cuda.synchronize()
+        a, b = it["y"].cpu().numpy(), y.cpu().numpy()
+        # K = 4096 (one wave per tile) and K = 14336 (four waves, one pass) use
+        # the same per-lane groups and reduction order in both paths
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"N={it['N']} K={it['K']}"
+
+
+def test_chain_header_mismatch_writes_nothing(w4a16_lib):
+    problems = [workload.random_problem(500, 1, 40, 128)]
+    ch = Chain(problems, 1, y_fill=-7.0)
+    ch.plan(M=1)
+    ch.run(M=2)                                             # plan says M = 1
+    torch.cuda.synchronize()
+    assert (ch.items[0]["y"].cpu().numpy() == -7.0).all()
+    assert_workspace_clean(ch)
+
+
+def test_chain_graph_replays_match_eager(w4a16_lib):
+    shapes = [(1024, 4096), (512, 14336), (300, 4096)]
+    problems = [workload.random_problem(600 + i, 1, N, K, outliers=True) for i, (N, K) in enumerate(shapes)]
+    ch = Chain(problems, 1)
+    ch.plan()
+    s = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(s):
+        ch.run(s)
+    s.synchronize()
+    eager = [it["y"].clone() for it in ch.items]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ch.run(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for it in ch.items:
+            it["y"].fill_(float("nan"))                     # eager work between replays
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        for it, e in zip(ch.items, eager):
+            assert torch.equal(it["y"], e), f"replay {rep} differs"
+        assert_workspace_clean(ch)
