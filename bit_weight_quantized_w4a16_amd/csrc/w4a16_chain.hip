@@ -44,7 +44,7 @@ constexpr int kXLdsBytes = 65536;              // LDS staging of one pass of x
 
 // One workgroup per CU, with as many waves as the register budget of the
 // instantiation allows per SIMD (x4 SIMDs).
-constexpr int chain_waves(int M) { return M == 1 ? 12 : 8; }
+constexpr int chain_waves(int M) { return 8; }
 // groups per lane (the x slice stays within 32 VGPRs)
 constexpr int chain_gpl(int M) { return M == 1 ? 2 : 1; }
 // groups of x one pass can stage in LDS
@@ -155,15 +155,17 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
     return n;
   };
   auto block_of = [&](const Geo& g, int k, int team) { return (k * nwg + int(blockIdx.x)) * g.teams + team; };
-  auto fetch = [&](const Geo& g, Item it, TileLoads<GPL>& L) {
+  // issue the loads of item `it`; a team with no tile in it (or `enable`
+  // false) issues out-of-range buffer loads that cost no memory traffic, so
+  // the fetch never sits behind a branch
+  auto fetch = [&](const Geo& g, Item it, TileLoads<GPL>& L, bool enable) {
     const int b = block_of(g, it.k, g.team);
     const int t = b * g.tpb + it.tb;
-    if (b < g.nblocks && t < g.T) {
-      int g0[GPL];
+    const bool valid = enable && b < g.nblocks && t < g.T;
+    int g0[GPL];
 #pragma unroll
-      for (int j = 0; j < GPL; ++j) g0[j] = it.c * g.pg + (g.wit * GPL + j) * 64;
-      fetch_tile<GPL>(g.codes, g.sm, g.N, g.G, t, g0, lane, L);
-    }
+    for (int j = 0; j < GPL; ++j) g0[j] = it.c * g.pg + (g.wit * GPL + j) * 64;
+    fetch_tile_rsrc<GPL>(g.codes, g.sm, g.N, g.G, valid ? t : 0, g0, lane, valid, L);
   };
 
   u32x4 xv[M][GPL][4];
@@ -178,7 +180,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   auto stage_x = [&](const Geo& g, int c) {
     const int g_first = c * g.pg;
     const int ng = min(g.pg, g.G - g_first);
-    __syncthreads();  // every wave is done with the previous pass's LDS copy
+    lds_barrier();  // every wave is done with the previous pass's LDS copy
     const int words = M * ng * 8;  // 8-byte words
     for (int w = threadIdx.x; w < words; w += blockDim.x) {
       const int m = w / (ng * 8);
@@ -188,7 +190,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
       const unsigned long long v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       reinterpret_cast<unsigned long long*>(xl)[size_t(m) * g.pg * 8 + r] = v;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
       const int gl = (g.wit * GPL + j) * 64 + lane;  // group within the pass
@@ -219,10 +221,11 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
 
   // this workgroup's results of product i are written: report to the tree;
   // the last report of a leaf climbs to the top, the last at the top raises
-  // every leaf's flag to i+1
+  // every leaf's flag to i+1. Called before the next tile is fetched, so the
+  // atomics' returns do not wait behind that prefetch (vmcnt is in order).
   auto arrive = [&](int i) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent y stores are complete
-    __syncthreads();                // ... and every other wave's
+    __builtin_amdgcn_s_barrier();   // ... and every other wave's
     if (threadIdx.x == 0) {
       const unsigned old = add_coherent(ws + leaf_word(leaf), 1u);
       if (old == unsigned(i + 1) * leaf_size - 1u) {
@@ -248,11 +251,11 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
       }
       s_abort = ab;
     }
-    __syncthreads();
+    lds_barrier();
     aborted = s_abort != 0;
   };
 
-  auto finish = [&](const Geo& g, Item it, const TileLoads<GPL>& L, bool last_of_product) {
+  auto finish = [&](const Geo& g, Item it, const TileLoads<GPL>& L) {
     if (it.tb == 0 && (it.i != x_i || it.c != x_c)) {  // this (product, pass) needs its x
       if (it.k == 0 && it.c == 0 && it.i > 0) wait_for(it.i);
       if (!aborted) stage_x(g, it.c);
@@ -275,7 +278,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
       }
     }
     if (!g.direct && it.c == g.passes - 1 && it.tb == g.tpb - 1) {  // block done: combine each team's waves
-      __syncthreads();
+      lds_barrier();
       if (!aborted) {
         const int per_team = g.tpb * kTileRows * M;
         for (int idx = threadIdx.x; idx < g.teams * per_team; idx += blockDim.x) {
@@ -293,38 +296,68 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
           }
         }
       }
+      lds_barrier();  // partials read before the next block writes them
     }
-    if (last_of_product) arrive(it.i);
   };
 
-  // two load buffers used alternately: the next item's tile is in flight
-  // while the current one is computed; across a product boundary the next
-  // tile is fetched right after this workgroup's report (so the report does
-  // not wait for it) and before the wait for the other workgroups
-  TileLoads<GPL> la, lb;
+  // Two load buffers used alternately: the next item's tile is in flight
+  // while the current one is computed. Inside a product the next fetch is
+  // issued first; at a product's last item the results are written and
+  // reported first, then the next product's first tile is fetched, and only
+  // then (at that product's first item) does the workgroup wait for the
+  // others, with the tile in flight. Every fetch is unconditional: a fetch
+  // behind a branch makes the compiler merge buffer contents with register
+  // moves that wait for the loads in flight.
   Item ia{0, 0, 0, 0};
   Geo ga = geo(0);
-  fetch(ga, ia, la);
-  while (true) {
-    const Item ib = next_item(ga, ia);
-    const bool more_b = ib.i < count;
-    const bool edge_b = ib.i != ia.i;
-    const Geo gb = (edge_b && more_b) ? geo(ib.i) : ga;
-    if (more_b && !edge_b) fetch(gb, ib, lb);
-    finish(ga, ia, la, edge_b);
-    if (!more_b || aborted) break;
-    if (edge_b) fetch(gb, ib, lb);
+  if constexpr (double_buffered(M)) {
+    TileLoads<GPL> la, lb;
+    fetch(ga, ia, la, true);
+    while (true) {
+      const Item ib = next_item(ga, ia);
+      const bool more_b = ib.i < count;
+      const bool edge_b = ib.i != ia.i;
+      const Geo gb = (edge_b && more_b) ? geo(ib.i) : ga;
+      if (!edge_b) {
+        fetch(gb, ib, lb, true);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(ga, ia, la);
+      } else {
+        finish(ga, ia, la);
+        arrive(ia.i);
+        fetch(gb, ib, lb, more_b);
+      }
+      if (!more_b || aborted) break;
 
-    const Item ic = next_item(gb, ib);
-    const bool more_c = ic.i < count;
-    const bool edge_c = ic.i != ib.i;
-    const Geo gc = (edge_c && more_c) ? geo(ic.i) : gb;
-    if (more_c && !edge_c) fetch(gc, ic, la);
-    finish(gb, ib, lb, edge_c);
-    if (!more_c || aborted) break;
-    if (edge_c) fetch(gc, ic, la);
-    ia = ic;
-    ga = gc;
+      const Item ic = next_item(gb, ib);
+      const bool more_c = ic.i < count;
+      const bool edge_c = ic.i != ib.i;
+      const Geo gc = (edge_c && more_c) ? geo(ic.i) : gb;
+      if (!edge_c) {
+        fetch(gc, ic, la, true);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(gb, ib, lb);
+      } else {
+        finish(gb, ib, lb);
+        arrive(ib.i);
+        fetch(gc, ic, la, more_c);
+      }
+      if (!more_c || aborted) break;
+      ia = ic;
+      ga = gc;
+    }
+  } else {
+    // more activation rows: VALU bound, registers go to the x slices
+    while (true) {
+      TileLoads<GPL> la;
+      fetch(ga, ia, la, true);
+      const Item ib = next_item(ga, ia);
+      finish(ga, ia, la);
+      if (ib.i != ia.i) arrive(ia.i);
+      if (ib.i >= count || aborted) break;
+      if (ib.i != ia.i) ga = geo(ib.i);
+      ia = ib;
+    }
   }
 
   // Count out. After an abort, first release every waiter (results of this

@@ -42,14 +42,22 @@ __device__ __forceinline__ float dpp(float v) {
 }
 
 // Sum over the 64 lanes of a wave; every lane ends with the same bits.
+// Within rows of 16 lanes: DPP butterflies. Across rows: gfx950's
+// v_permlane16_swap / v_permlane32_swap, which exchange whole rows between
+// two VGPRs inside the VALU (no LDS round trip as with ds_bpermute): after
+// swap(v, v) one register holds rows (0,0,2,2) and the other rows (1,1,3,3),
+// so their sum is the pairwise row sum in every lane, in the same order.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp<0x141>(v);  // row_half_mirror
   v += dpp<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const unsigned b = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = __builtin_bit_cast(float, unsigned(p[0])) + __builtin_bit_cast(float, unsigned(p[1]));
+  const unsigned c = __builtin_bit_cast(unsigned, v);
+  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_bit_cast(float, unsigned(q[0])) + __builtin_bit_cast(float, unsigned(q[1]));
 }
 
 // Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
@@ -60,24 +68,70 @@ struct TileLoads {
 };
 
 // Issue the 16-byte non-temporal loads of tile t (rows 4t..4t+3) for the
-// groups g0[j] + lane. Lanes past G and rows past N load nothing (zeros).
+// groups g0[j] + lane. Every load is unconditional: a lane past G reads group
+// G-1 instead (its activations are zero, so it adds exactly 0) and a row past
+// N reads row N-1 (its results are never stored). A conditional load would
+// make the compiler merge "zero or loaded" with a register move that waits
+// for the load, which serialises the prefetch of the next tile.
 template <int GPL>
 __device__ __forceinline__ void fetch_tile(const u32x4* __restrict__ codes, const u32x4* __restrict__ sm, int N,
                                            int G, int t, const int (&g0)[GPL], int lane, TileLoads<GPL>& L) {
 #pragma unroll
   for (int j = 0; j < GPL; ++j) {
-    const bool ok = lane < G - g0[j];
-    const u32x4* sp = sm + (size_t(t) * G + g0[j]);
-    L.sm[j] = u32x4{0, 0, 0, 0};
-    if (ok) L.sm[j] = __builtin_nontemporal_load(sp + lane);
+    const int last = G - 1 - g0[j];  // wave-uniform; < 0 when the whole slot is past G
+    const int gl = lane < last ? lane : (last > 0 ? last : 0);
+    const int base = last < 0 ? G - 1 - g0[j] : 0;  // pulls an all-idle slot back to group G-1
+    const u32x4* sp = sm + (size_t(t) * G + g0[j] + base);
+    L.sm[j] = __builtin_nontemporal_load(sp + gl);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      const int n = t * kTileRows + r;
-      const u32x4* cp = codes + (size_t(n) * G + g0[j]);
-      L.code[r][j] = u32x4{0, 0, 0, 0};
-      if (ok && n < N) L.code[r][j] = __builtin_nontemporal_load(cp + lane);
+      const int n = t * kTileRows + r < N ? t * kTileRows + r : N - 1;
+      const u32x4* cp = codes + (size_t(n) * G + g0[j] + base);
+      L.code[r][j] = __builtin_nontemporal_load(cp + gl);
     }
   }
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3:
+// 32-bit data format, the setting for untyped raw access). A load whose
+// offset falls outside the range returns zeros without touching memory.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kLoadNT = 2;  // buffer-load cache policy: non-temporal stream
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
+}
+
+// fetch_tile with buffer loads: when `valid` is false (a team with no tile
+// this round) every load is out of range and costs no memory traffic, so the
+// caller need not branch around the fetch. Lane and row clamping as above.
+template <int GPL>
+__device__ __forceinline__ void fetch_tile_rsrc(const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
+                                                int N, int G, int t, const int (&g0)[GPL], int lane, bool valid,
+                                                TileLoads<GPL>& L) {
+  const int lim = valid ? -1 : 0;  // -1: the whole 32-bit range
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + size_t(t) * kTileRows * G, lim);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sm + size_t(t) * G, lim);
+#pragma unroll
+  for (int j = 0; j < GPL; ++j) {
+    const int last = G - 1 - g0[j];
+    const int gl = lane < last ? lane : (last > 0 ? last : 0);
+    const int grp = g0[j] + (last < 0 ? last : 0) + gl;  // in [0, G-1]
+    L.sm[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, grp * 16, 0, kLoadNT);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const int rr = t * kTileRows + r < N ? r : N - 1 - t * kTileRows;  // row within the tile, clamped
+      L.code[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rc, (rr * G + grp) * 16, 0, kLoadNT);
+    }
+  }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads (a __syncthreads would also drain the
+// prefetched tile).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
 }
 
 // This lane's slice x[m][32g .. 32g+31] of every activation row for the

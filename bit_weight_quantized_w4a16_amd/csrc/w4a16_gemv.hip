@@ -44,9 +44,15 @@ __host__ __device__ constexpr int max_waves(int M, int GPL) {
   return (16 * M * GPL + (double_buffered(M) ? 40 : 20) * GPL + 6 * M + 30) <= 128 ? 16 : 8;
 }
 
-// MULTI: K takes more than one pass of the workgroup, so x is re-fetched per
-// pass; otherwise x is fetched once, after the first tile's loads.
-template <int M, int GPL, bool MULTI>
+// Launch modes of one GEMV.
+//   kDirect: one wave covers all of K for its tile and stores the results;
+//   kBlock:  the waves of a workgroup split K; per-wave partials of a block
+//            of tiles are combined through LDS;
+//   kMulti:  K also takes several passes of the workgroup (x re-fetched per
+//            pass, partials carried in LDS).
+constexpr int kDirect = 0, kBlock = 1, kMulti = 2;
+
+template <int M, int GPL, int MODE>
 __global__ void __launch_bounds__(64 * max_waves(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
             float* __restrict__ y, int N, int G, int T, int nchunks, int tpb) {
@@ -56,8 +62,8 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
-  const bool direct = (nwaves == 1 && nchunks == 1);
   const int nblocks = (T + tpb - 1) / tpb;
+  if (int(blockIdx.x) >= nblocks) return;
 
   auto bases = [&](int c, int (&g0)[GPL]) {
 #pragma unroll
@@ -66,114 +72,124 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
 
   u32x4 xv[M][GPL][4];
   float xs[M][GPL];
-
-  // per-wave partials of one block of tiles: [tile][row][m][wave]
-  __shared__ float part[kTilesPerBlock][kTileRows][M][kMaxWaves];
-
-  // This workgroup walks items (block b, pass c, tile tb of the block) for
-  // b = blockIdx.x, blockIdx.x + gridDim.x, ... Every wave of the workgroup
-  // walks the same items, so the barriers below are uniform.
-  struct Item {
-    int b, c, tb;
-  };
-  auto next_item = [&](Item it) {
-    Item n{it.b, it.c, it.tb + 1};
-    if (n.tb >= tpb || n.b * tpb + n.tb >= T) {
-      n.tb = 0;
-      if (++n.c >= nchunks) {
-        n.c = 0;
-        n.b += gridDim.x;
-      }
-    }
-    return n;
-  };
-  auto fetch = [&](Item it, TileLoads<GPL>& L) {
-    int g0[GPL];
-    bases(it.c, g0);
-    fetch_tile<GPL>(codes, sm, N, G, it.b * tpb + it.tb, g0, lane, L);
-  };
   auto fetch_x = [&](int c) {
     int g0[GPL];
     bases(c, g0);
     load_x<M, GPL>(x, G, g0, lane, xv, xs);
   };
-  // compute item `it` from its loads, emit or stage its results; `nb` is the
-  // block of the item after it (a new block closes block it.b)
-  auto finish = [&](const TileLoads<GPL>& L, Item it, int nb) {
-    const int t = it.b * tpb + it.tb;
-    float acc[kTileRows][M];
-    compute_tile<M, GPL>(L, xv, xs, acc);
-    if (direct) {
-      store_tile<M>(acc, y, N, t, lane);
-      return;
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          part[it.tb][r][m][wave] = (it.c == 0 ? 0.f : part[it.tb][r][m][wave]) + acc[r][m];
-    }
-    if (nb != it.b) {  // every pass of block it.b is done: combine the waves
-      __syncthreads();
-      const int ntiles = min(tpb, T - it.b * tpb);
-      for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
-        const int ti = i / (kTileRows * M);
-        const int r = (i / M) % kTileRows;
-        const int m = i % M;
-        const int n = (it.b * tpb + ti) * kTileRows + r;
-        if (n < N) {
-          float s = 0.f;
-          for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
-          y[size_t(m) * N + n] = s;
-        }
+
+  // per-wave partials of one block of tiles: [tile][row][m][wave]
+  __shared__ float part[MODE == kDirect ? 1 : kTilesPerBlock][kTileRows][M][MODE == kDirect ? 1 : kMaxWaves];
+
+  // combine the waves' partials of block b (all passes done) and store
+  auto reduce_block = [&](int b) {
+    __syncthreads();
+    const int ntiles = min(tpb, T - b * tpb);
+    for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
+      const int ti = i / (kTileRows * M);
+      const int r = (i / M) % kTileRows;
+      const int m = i % M;
+      const int n = (b * tpb + ti) * kTileRows + r;
+      if (n < N) {
+        float s = 0.f;
+        for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
+        y[size_t(m) * N + n] = s;
       }
-      __syncthreads();
     }
+    __syncthreads();
   };
 
-  Item ia{int(blockIdx.x), 0, 0};
-  if (ia.b >= nblocks) return;
-  if constexpr (MULTI) {
+  if constexpr (MODE == kMulti) {
     // passes over K outermost within a block: x of pass c is fetched once at
     // the top of the pass and stays in registers for the block's tiles
-    for (int b = ia.b; b < nblocks; b += gridDim.x) {
+    for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
+      const int ntiles = min(tpb, T - b * tpb);
       for (int c = 0; c < nchunks; ++c) {
         fetch_x(c);
-        const int ntiles = min(tpb, T - b * tpb);
+        int g0[GPL];
+        bases(c, g0);
         for (int tb = 0; tb < ntiles; ++tb) {
           TileLoads<GPL> la;
-          fetch(Item{b, c, tb}, la);
-          const bool last = (c == nchunks - 1) && (tb == ntiles - 1);
-          finish(la, Item{b, c, tb}, last ? b + int(gridDim.x) : b);
+          fetch_tile<GPL>(codes, sm, N, G, b * tpb + tb, g0, lane, la);
+          float acc[kTileRows][M];
+          compute_tile<M, GPL>(la, xv, xs, acc);
+          if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+              for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + acc[r][m];
+          }
         }
       }
+      reduce_block(b);
     }
-  } else if constexpr (double_buffered(M)) {
-    TileLoads<GPL> la, lb;
-    fetch(ia, la);
-    fetch_x(0);  // after the first tile's loads, so both latencies overlap
-    while (true) {
-      const Item ib = next_item(ia);
-      if (ib.b < nblocks) fetch(ib, lb);
-      finish(la, ia, ib.b);
-      if (ib.b >= nblocks) break;
-      ia = next_item(ib);
-      if (ia.b < nblocks) fetch(ia, la);
-      finish(lb, ib, ia.b);
-      if (ia.b >= nblocks) break;
-    }
+    return;
   } else {
-    bool first = true;
-    while (true) {
-      TileLoads<GPL> la;
-      fetch(ia, la);
-      if (first) fetch_x(0);
-      first = false;
-      const Item ib = next_item(ia);
-      finish(la, ia, ib.b);
-      if (ib.b >= nblocks) break;
-      ia = ib;
+    // Items e = 0 .. n_items-1 of this workgroup: tile tb = e % tpb of its
+    // (e / tpb)-th block. The item count is known up front and the loop's
+    // only exit is its condition, so every fetch inside the loop is
+    // unconditional (a fetch that might not happen would make the compiler
+    // merge buffer contents with register moves that wait for the loads in
+    // flight); tiles past T (in the matrix's last block only) fetch a clamped
+    // tile and are skipped. A scheduling barrier after each fetch keeps the
+    // next tile's loads ahead of the current tile's compute.
+    const int my_blocks = (nblocks - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+    const int n_items = my_blocks * tpb;
+    int g0[GPL];
+    bases(0, g0);
+    auto tile_of = [&](int e) { return (int(blockIdx.x) + (e / tpb) * int(gridDim.x)) * tpb + e % tpb; };
+    auto fetch = [&](int e, TileLoads<GPL>& L) {
+      const int t = tile_of(e);
+      fetch_tile<GPL>(codes, sm, N, G, t < T ? t : T - 1, g0, lane, L);
+    };
+    auto finish = [&](const TileLoads<GPL>& L, int e) {
+      const int t = tile_of(e);
+      if (t < T) {
+        float acc[kTileRows][M];
+        compute_tile<M, GPL>(L, xv, xs, acc);
+        if constexpr (MODE == kDirect) {
+          store_tile<M>(acc, y, N, t, lane);
+        } else if (lane == 0) {
+          const int tb = e % tpb;
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) part[tb][r][m][wave] = acc[r][m];
+        }
+      }
+      if constexpr (MODE == kBlock) {
+        if (e % tpb == tpb - 1) reduce_block(int(blockIdx.x) + (e / tpb) * int(gridDim.x));
+      }
+    };
+
+    TileLoads<GPL> la, lb;
+    fetch(0, la);
+    fetch_x(0);  // after the first tile's loads, so both latencies overlap
+    int e = 0;
+    if constexpr (double_buffered(M)) {
+      while (e + 2 < n_items) {
+        fetch(e + 1, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(la, e);
+        fetch(e + 2, la);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(lb, e + 1);
+        e += 2;
+      }
+      if (n_items - e == 2) {
+        fetch(e + 1, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(la, e);
+        finish(lb, e + 1);
+      } else {
+        finish(la, e);
+      }
+    } else {
+      finish(la, 0);
+      for (e = 1; e < n_items; ++e) {
+        fetch(e, la);
+        finish(la, e);
+      }
     }
   }
 }
@@ -191,30 +207,37 @@ constexpr int32_t kMaxK = 1 << 20;
 // the x slice of one lane stays within 32 VGPRs (one group per lane always allowed)
 constexpr bool gpl_allowed(int M, int gpl) { return 16 * M * gpl <= 32 || gpl == 1; }
 
-template <int M, int GPL, bool MULTI>
+template <int M, int GPL, int MODE>
 constexpr kernel_fn instance() {
-  if constexpr (gpl_allowed(M, GPL)) return &gemv_kernel<M, GPL, MULTI>;
+  if constexpr (gpl_allowed(M, GPL)) return &gemv_kernel<M, GPL, MODE>;
   return nullptr;
 }
 
-template <int M, bool MULTI>
+template <int M, int MODE>
 constexpr kernel_fn pick(int gi) {
-  return gi == 0 ? instance<M, 1, MULTI>() : gi == 1 ? instance<M, 2, MULTI>() : instance<M, 4, MULTI>();
+  return gi == 0 ? instance<M, 1, MODE>() : gi == 1 ? instance<M, 2, MODE>() : instance<M, 4, MODE>();
 }
 
-template <bool MULTI>
+template <int MODE>
 kernel_fn kernel_for(int M, int gi) {
   switch (M) {
-    case 1: return pick<1, MULTI>(gi);
-    case 2: return pick<2, MULTI>(gi);
-    case 3: return pick<3, MULTI>(gi);
-    case 4: return pick<4, MULTI>(gi);
-    case 5: return pick<5, MULTI>(gi);
-    case 6: return pick<6, MULTI>(gi);
-    case 7: return pick<7, MULTI>(gi);
-    case 8: return pick<8, MULTI>(gi);
+    case 1: return pick<1, MODE>(gi);
+    case 2: return pick<2, MODE>(gi);
+    case 3: return pick<3, MODE>(gi);
+    case 4: return pick<4, MODE>(gi);
+    case 5: return pick<5, MODE>(gi);
+    case 6: return pick<6, MODE>(gi);
+    case 7: return pick<7, MODE>(gi);
+    case 8: return pick<8, MODE>(gi);
     default: return nullptr;
   }
+}
+
+int mode_of(int waves, int nchunks) { return nchunks > 1 ? kMulti : waves > 1 ? kBlock : kDirect; }
+
+kernel_fn kernel_for_mode(int mode, int M, int gi) {
+  return mode == kMulti ? kernel_for<kMulti>(M, gi) : mode == kBlock ? kernel_for<kBlock>(M, gi)
+                                                                      : kernel_for<kDirect>(M, gi);
 }
 
 struct LaunchShape {
@@ -258,10 +281,10 @@ LaunchShape choose_shape(int M, int G) {
 // Resident workgroups per CU of one instantiation at one block size (cached;
 // 0 = not yet queried). Every device the library drives is a gfx950, so the
 // answer does not depend on the device.
-std::atomic<int> g_occupancy[kMaxM + 1][kNumGpl][2][kMaxWaves + 1];
+std::atomic<int> g_occupancy[kMaxM + 1][kNumGpl][3][kMaxWaves + 1];
 
-int occupancy(int M, int gi, bool multi, int waves, kernel_fn fn) {
-  std::atomic<int>& slot = g_occupancy[M][gi][multi ? 1 : 0][waves];
+int occupancy(int M, int gi, int mode, int waves, kernel_fn fn) {
+  std::atomic<int>& slot = g_occupancy[M][gi][mode][waves];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
   v = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * waves);
@@ -312,14 +335,15 @@ extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, 
       if (kGplOptions[gi] == g && gpl_allowed(M, g)) shape = shape_for_gpl(M, G, gi);
   }
   if (shape.gi < 0) return W4A16_ERR_SHAPE;
-  kernel_fn fn = shape.nchunks > 1 ? kernel_for<true>(M, shape.gi) : kernel_for<false>(M, shape.gi);
+  const int mode = mode_of(shape.waves, shape.nchunks);
+  kernel_fn fn = kernel_for_mode(mode, M, shape.gi);
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int T = (N + kTileRows - 1) / kTileRows;
-  const bool direct = shape.waves == 1 && shape.nchunks == 1;
+  const bool direct = mode == kDirect;
   // all workgroups resident at once, each walking an equal share of the tiles
-  int occ = occupancy(M, shape.gi, shape.nchunks > 1, shape.waves, fn);
+  int occ = occupancy(M, shape.gi, mode, shape.waves, fn);
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
   const int max_grid = w4a16_host::cu_count(dev) * occ;
   int tpb = direct ? 1 : T / max_grid;

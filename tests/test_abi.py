@@ -147,18 +147,18 @@ def test_chain_plan_layout(w4a16_lib):
     entries = [
         (B, B + 2**24, B + 2**30, 6144, 4096),            # K = 4096: one wave per tile
         (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # four waves per tile
-        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # four waves, two passes
+        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # eight waves, one pass
     ]
     plan = w4.w4a16_chain_plan(entries, 1)
     assert plan.size == w4.w4a16_chain_plan_bytes(3) == 64 + 3 * 64
     hdr, ents = _plan_fields(plan, 3)
-    assert hdr[0] == 0x48433457 and hdr[1] == 2 and hdr[2] == 3 and hdr[3] == 1 and hdr[5] == 12
+    assert hdr[0] == 0x48433457 and hdr[1] == 2 and hdr[2] == 3 and hdr[3] == 1 and hdr[5] == 8
     for (x, p, y, N, K), e in zip(entries, ents):
         ex, ecodes, esm, ey, eN, eG, eT, wpr, passes = e
         assert (ex, ecodes, ey, eN, eG, eT) == (x, p, y, N, K // 32, (N + 3) // 4)
         assert esm == p + (N * K // 2 + 255) // 256 * 256
         assert wpr * 128 * passes >= K // 32             # M = 1 uses two groups per lane
-    assert [e[7:] for e in ents] == [(1, 1), (4, 1), (6, 2)]        # teams divide 12 waves
+    assert [e[7:] for e in ents] == [(1, 1), (4, 1), (8, 1)]        # teams divide 8 waves
     plan8 = w4.w4a16_chain_plan(entries[:2], 8)
     _, e8 = _plan_fields(plan8, 2)
     assert [e[7:] for e in e8] == [(2, 1), (2, 4)]       # M = 8: 128 groups of x per LDS pass
