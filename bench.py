@@ -4,17 +4,24 @@
 One step = the 128 GEMVs of 32 Llama-3-8B-shaped decoder layers at M = 1
 (fused QKV 4096->6144, O 4096->4096, fused gate-up 4096->28672, down
 14336->4096), each with its own seeded 4-bit group-32 weights, all resident in
-HBM (4.37 GB packed). The step runs as one w4a16_gemv_chain launch: the 128
-products in order, each one starting only after every earlier one's results
-are written (the ordering a decode loop needs), with the next product's weights
-streamed while that ordering point is reached. The same step as 128 separate
-launches replayed from a HIP graph is reported alongside.
+HBM (4.37 GB packed). Products run in order, each one starting only after
+every earlier one's results are written (the ordering a decode loop needs).
+Two launch forms of the same step are timed:
 
-Printed: one JSON line with the whole-step throughput in algorithmic GB/s
-(N*K/2 code bytes + 4 bytes of scale/min per 32 weights + x + y, per GEMV),
-the roofline entry of the chain kernel (event-timed per launch on the launch
-stream) and the fp64 oracle timed on this host's cores as a reported CPU
-baseline.
+* chain: one w4a16_gemv_chain launch per step, the products ordered on the
+  device, the next product's weights streamed while that ordering point is
+  reached;
+* separate: 128 w4a16_gemv launches on one stream, replayed from a HIP graph.
+
+The faster one is the reported value. Printed: one JSON line with the whole-step
+throughput in algorithmic GB/s (N*K/2 code bytes + 4 bytes of scale/min per 32
+weights + x + y, per GEMV), the roofline entry of the dominant kernel of the
+reported form (its launches event-timed on the launch stream) and the fp64
+oracle timed on this host's cores as a reported CPU baseline.
+
+--only chain|separate times one form (for counter runs); --copy-calibration
+runs only a plain device copy of 1 GiB three times (the FETCH_SIZE /
+WRITE_SIZE scale of a kernel of known traffic).
 """
 from __future__ import annotations
 
@@ -39,6 +46,28 @@ WORKLOAD = "llama8b_step"
 
 def gemv_bytes(M, N, K):
     return N * K // 2 + 4 * N * (K // 32) + 2 * M * K + 4 * M * N
+
+
+# HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
+# only while the kernel is unchanged since the counters were taken.
+TRAFFIC = {
+    # (16,308.6 KiB FETCH_SIZE x 2.000 + 101.3 KiB WRITE_SIZE x 1.000) per dispatch
+    "gemv_kernel<1, 2, 0>": 33_503_787,
+    # (2,138,844.1 KiB x 2.000 + 11,401.1 KiB x 1.000) per dispatch
+    "chain_kernel<1, 2, 8>": 4_392_027_328,
+}
+
+
+def copy_calibration(torch, dev):
+    """Three plain device copies of 1 GiB (known traffic: 1 GiB read, 1 GiB written)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("[bench] copy calibration: 3 copies of 1 GiB done")
 
 
 def log(msg):
@@ -143,6 +172,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--only", choices=["chain", "separate"], default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time separate launches eagerly (counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -160,6 +192,9 @@ def main():
         _build.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     M = 1
 
     t0 = time.time()
@@ -203,34 +238,73 @@ def main():
         raise AssertionError("chain workspace not clean after a call (counters, flags or error word)")
     log(f"[bench] spot checks ok; chain vs separate launches: max rel diff {worst:.2e}")
 
-    # separate launches, replayed from a HIP graph (reported alongside)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        launch_step(w4, gemvs, stream.cuda_stream)
-    torch.cuda.synchronize()
-    sec_sep = time_loop(torch, stream, graph.replay, args.warmup, args.steps)
-    log(f"[bench] separate launches (graph): {sec_sep * 1e6:.1f} us/step")
-
-    # the timed decode step: one chained launch per step
-    sec = time_loop(torch, stream, chain_step, args.warmup, args.steps)
+    forms = {}
+    if args.only in (None, "separate"):
+        # separate launches, replayed from a HIP graph
+        if args.no_graph:
+            replay = lambda: launch_step(w4, gemvs, sh)  # noqa: E731
+        else:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                launch_step(w4, gemvs, stream.cuda_stream)
+            torch.cuda.synchronize()
+            replay = graph.replay
+        forms["separate"] = time_loop(torch, stream, replay, args.warmup, args.steps)
+        log(f"[bench] separate launches ({'eager' if args.no_graph else 'graph'}): "
+            f"{forms['separate'] * 1e6:.1f} us/step")
+    if args.only in (None, "chain"):
+        forms["chain"] = time_loop(torch, stream, chain_step, args.warmup, args.steps)
+        log(f"[bench] chain: {forms['chain'] * 1e6:.1f} us/step")
+    form = min(forms, key=forms.get)
+    sec = forms[form]
     ms_per_step = sec * 1e3
-    log(f"[bench] chain: {ms_per_step * 1e3:.1f} us/step")
 
-    # HIP events on the launch stream around every chain launch: its average
-    # duration, the figure rocprofv3 reports for the same kernel
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # The dominant kernel of the reported form: the chain kernel, or the
+    # w4a16_gemv instantiation that moves the most bytes per step. Its launches
+    # go through the *_timed entry points, which record the kernel's own start
+    # and end into two HIP events on the launch stream: the average of their
+    # elapsed times is the per-launch duration rocprofv3 reports for it.
+    def timed_events():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)   # creates the underlying HIP events
+        b.record(stream)
+        return a, b
+
     marks = []
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            a, b = ev(), ev()
-            a.record(stream)
-            chain_step()
-            b.record(stream)
-            marks.append((a, b))
+    if form == "chain":
+        kernel = w4.chain_launch_shape(M)["kernel"]
+        launch_bytes = [step_bytes]
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                a, b = timed_events()
+                st = w4.w4a16_gemv_chain_timed_raw(plan_p, count, M, ws_p, ws_bytes, sh, a.cuda_event, b.cuda_event)
+                if st != 0:
+                    raise w4.W4A16Error(st, "w4a16_gemv_chain_timed")
+                marks.append((a, b))
+    else:
+        by_kernel = {}
+        for g in gemvs:
+            by_kernel[g["kernel"]] = by_kernel.get(g["kernel"], 0) + g["bytes"]
+        kernel = max(by_kernel, key=by_kernel.get)
+        launch_bytes = [g["bytes"] for g in gemvs if g["kernel"] == kernel]
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, args.steps // 4)):
+                for g in gemvs:
+                    if g["kernel"] == kernel:
+                        a, b = timed_events()
+                        st = w4.w4a16_gemv_timed_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], sh,
+                                                     a.cuda_event, b.cuda_event)
+                        if st != 0:
+                            raise w4.W4A16Error(st, "w4a16_gemv_timed")
+                        marks.append((a, b))
+                    else:
+                        launch_step(w4, [g], sh)
     torch.cuda.synchronize()
     avg_us = sum(a.elapsed_time(b) for a, b in marks) / len(marks) * 1e3
-    achieved = step_bytes / (avg_us * 1e-6) / 1e9
-    log(f"[bench] chain kernel: avg {avg_us:.1f} us per launch, {achieved:.1f} GB/s")
+    per_launch = sum(launch_bytes) / len(launch_bytes)
+    achieved = per_launch / (avg_us * 1e-6) / 1e9
+    log(f"[bench] {kernel}: avg {avg_us:.2f} us per launch, {per_launch / 1e6:.2f} MB per launch, "
+        f"{achieved:.1f} GB/s")
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
@@ -253,19 +327,20 @@ def main():
                         "gate_up 4096->28672, down 14336->4096), M=1, 4-bit codes, group 32, fp16 scale+min",
             "gemvs_per_step": len(gemvs),
             "bytes_per_step": step_bytes,
-            "launch": "chain: one w4a16_gemv_chain launch per step, products ordered on the device",
-            "separate_launches_us_per_step": round(sec_sep * 1e6, 2),
+            "launch": {"chain": "one w4a16_gemv_chain launch per step, products ordered on the device",
+                       "separate": "128 w4a16_gemv launches per step, replayed from a HIP graph"}[form],
+            "us_per_step_by_launch_form": {k: round(v * 1e6, 2) for k, v in forms.items()},
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "chain_kernel<1, 2, 4>",
+            "kernel": kernel,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "avg_launch_us": round(avg_us, 2),
-            "bytes_per_launch": step_bytes,
+            "traffic": TRAFFIC.get(kernel),
+            "avg_launch_us": round(avg_us, 3),
+            "bytes_per_launch": round(per_launch),
         },
     }
     if not args.no_cpu_baseline:

@@ -33,6 +33,9 @@ EXPORTS = (
     "w4a16_launch_shape",
     "w4a16_chain_plan_bytes",
     "w4a16_chain_plan",
+    "w4a16_chain_launch_shape",
+    "w4a16_gemv_timed",
+    "w4a16_gemv_chain_timed",
     "w4a16_gemv_chain",
     "w4a16_status_string",
 )
@@ -80,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_chain_plan_bytes.argtypes = [c_i32]
     L.w4a16_chain_plan.restype = c_i32
     L.w4a16_chain_plan.argtypes = [ctypes.POINTER(ChainEntry), c_i32, c_i32, c_vp, c_sz]
+    L.w4a16_chain_launch_shape.restype = c_i32
+    L.w4a16_chain_launch_shape.argtypes = [c_i32, ctypes.POINTER(c_i32)]
+    L.w4a16_gemv_timed.restype = c_i32
+    L.w4a16_gemv_timed.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+    L.w4a16_gemv_chain_timed.restype = c_i32
+    L.w4a16_gemv_chain_timed.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp, c_vp]
     L.w4a16_gemv_chain.restype = c_i32
     L.w4a16_gemv_chain.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp]
     L.w4a16_status_string.restype = ctypes.c_char_p
@@ -129,8 +138,18 @@ def w4a16_launch_shape(M: int, N: int, K: int) -> dict:
     st = lib().w4a16_launch_shape(M, N, K, out)
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_launch_shape")
+    mode = 2 if out[2] > 1 else 1 if out[1] > 1 else 0     # direct / block / multi-pass kernel
     return {"groups_per_lane": out[0], "waves": out[1], "k_passes": out[2],
-            "kernel": f"gemv_kernel<{M}, {out[0]}>"}
+            "kernel": f"gemv_kernel<{M}, {out[0]}, {mode}>"}
+
+
+def chain_launch_shape(M: int) -> dict:
+    """Template arguments of the kernel w4a16_gemv_chain launches for M."""
+    out = (ctypes.c_int32 * 3)()
+    st = lib().w4a16_chain_launch_shape(M, out)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_chain_launch_shape")
+    return {"M": out[0], "gpl": out[1], "waves": out[2], "kernel": f"chain_kernel<{out[0]}, {out[1]}, {out[2]}>"}
 
 
 def _ptr(t) -> int:
@@ -140,6 +159,12 @@ def _ptr(t) -> int:
 def w4a16_gemv_raw(x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int, stream: int = 0) -> int:
     """Direct C call with raw pointers; returns the status code."""
     return int(lib().w4a16_gemv(x_ptr, packed_ptr, y_ptr, M, N, K, stream))
+
+
+def w4a16_gemv_timed_raw(x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int, stream: int,
+                         start_event: int, stop_event: int) -> int:
+    """w4a16_gemv_timed with raw pointers and hipEvent_t handles; returns the status code."""
+    return int(lib().w4a16_gemv_timed(x_ptr, packed_ptr, y_ptr, M, N, K, stream, start_event, stop_event))
 
 
 def w4a16_gemv(x, packed, y, stream=None) -> None:
@@ -216,6 +241,13 @@ def w4a16_gemv_chain_raw(plan_ptr: int, count: int, M: int, workspace_ptr: int, 
                          stream: int = 0) -> int:
     """Direct C call with raw pointers; returns the status code."""
     return int(lib().w4a16_gemv_chain(plan_ptr, int(count), int(M), workspace_ptr, int(workspace_bytes), stream))
+
+
+def w4a16_gemv_chain_timed_raw(plan_ptr: int, count: int, M: int, workspace_ptr: int, workspace_bytes: int,
+                               stream: int, start_event: int, stop_event: int) -> int:
+    """w4a16_gemv_chain_timed with raw pointers and hipEvent_t handles; returns the status code."""
+    return int(lib().w4a16_gemv_chain_timed(plan_ptr, int(count), int(M), workspace_ptr, int(workspace_bytes),
+                                            stream, start_event, stop_event))
 
 
 def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None) -> None:

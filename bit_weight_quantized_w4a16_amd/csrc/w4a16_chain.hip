@@ -21,6 +21,7 @@
 // the workspace and the workgroup stops computing but still counts in, so a
 // starved launch ends instead of hanging. The last workgroup out resets the
 // counters for the next call.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -486,8 +487,19 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
   return W4A16_OK;
 }
 
-extern "C" w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+extern "C" w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]) {
+  if (!out) return W4A16_ERR_NULL;
+  if (M < 1 || M > kMaxM) return W4A16_ERR_SHAPE;
+  out[0] = M;
+  out[1] = chain_gpl(M);
+  out[2] = chain_waves(M);
+  return W4A16_OK;
+}
+
+namespace {
+
+w4a16_status chain_enqueue(const void* plan, int32_t count, int32_t M, void* workspace, size_t workspace_bytes,
+                           void* stream, hipEvent_t start, hipEvent_t stop) {
   if (!plan || !workspace) return W4A16_ERR_NULL;
   if (count < 1 || count > kMaxChain || M < 1 || M > kMaxM) return W4A16_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(plan) % 16 || reinterpret_cast<uintptr_t>(workspace) % 16) return W4A16_ERR_ALIGN;
@@ -507,8 +519,23 @@ extern "C" w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_
   unsigned* wp = static_cast<unsigned*>(workspace);
   int n_arg = count;
   void* args[] = {&hp, &wp, &n_arg};
-  if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * chain_waves(M)), args, 0,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * chain_waves(M)), args, 0,
+                         static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return chain_enqueue(plan, count, M, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" w4a16_status w4a16_gemv_chain_timed(const void* plan, int32_t count, int32_t M, void* workspace,
+                                               size_t workspace_bytes, void* stream, void* start_event,
+                                               void* stop_event) {
+  if (!start_event || !stop_event) return W4A16_ERR_NULL;
+  return chain_enqueue(plan, count, M, workspace, workspace_bytes, stream, static_cast<hipEvent_t>(start_event),
+                       static_cast<hipEvent_t>(stop_event));
 }

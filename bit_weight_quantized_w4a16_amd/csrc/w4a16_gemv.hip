@@ -24,6 +24,7 @@
 //   * lane partials are summed across the wave with DPP and lane shuffles,
 //     across waves through LDS, in a fixed order: results are bitwise
 //     repeatable, no atomics are used and y is overwritten.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -312,8 +313,12 @@ extern "C" w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int3
   return W4A16_OK;
 }
 
-extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, int32_t M, int32_t N,
-                                   int32_t K, void* stream) {
+namespace {
+
+// Both entry points: validate, choose the launch and enqueue; with events,
+// they take the kernel's own start and end times.
+w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M, int32_t N, int32_t K,
+                          void* stream, hipEvent_t start, hipEvent_t stop) {
   using w4a16_host::ranges_overlap;
   using w4a16_host::tune;
   if (!x || !packed || !y) return W4A16_ERR_NULL;
@@ -358,8 +363,22 @@ extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, 
   const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(packed) + codes_region);
   int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb;
   void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg};
-  if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
+                         static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, int32_t M, int32_t N,
+                                   int32_t K, void* stream) {
+  return gemv_enqueue(x, packed, y, M, N, K, stream, nullptr, nullptr);
+}
+
+extern "C" w4a16_status w4a16_gemv_timed(const void* x, const void* packed, float* y, int32_t M, int32_t N,
+                                         int32_t K, void* stream, void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) return W4A16_ERR_NULL;
+  return gemv_enqueue(x, packed, y, M, N, K, stream, static_cast<hipEvent_t>(start_event),
+                      static_cast<hipEvent_t>(stop_event));
 }

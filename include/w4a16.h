@@ -138,6 +138,18 @@ w4a16_status w4a16_gemv(const void* x, const void* packed, float* y,
 w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int32_t out[3]);
 
 /*
+ * w4a16_gemv_timed - w4a16_gemv, with the kernel's own start and end times
+ * recorded into two caller-owned HIP events (hipEvent_t, created with timing
+ * enabled, e.g. by hipEventCreate): their elapsed time is the kernel's
+ * execution alone, the duration a profiler reports for it, without the
+ * launch latency that events recorded around the call would also include.
+ * Arguments, results and errors are those of w4a16_gemv; either event NULL
+ * -> W4A16_ERR_NULL.
+ */
+w4a16_status w4a16_gemv_timed(const void* x, const void* packed, float* y, int32_t M, int32_t N, int32_t K,
+                              void* stream, void* start_event, void* stop_event);
+
+/*
  * Decode-step chain: the GEMVs of a whole decode step in ONE kernel launch.
  *
  * The runtime traits of the core-modules page (section 5.2: a tight decode
@@ -209,6 +221,23 @@ w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32_t count, i
  */
 w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * w4a16_gemv_chain_timed - w4a16_gemv_chain, with the kernel's own start and
+ * end times recorded into two caller-owned HIP events, as w4a16_gemv_timed.
+ * Either event NULL -> W4A16_ERR_NULL; otherwise as w4a16_gemv_chain.
+ */
+w4a16_status w4a16_gemv_chain_timed(const void* plan, int32_t count, int32_t M, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
+/*
+ * w4a16_chain_launch_shape - host only: the three template arguments of the
+ * kernel w4a16_gemv_chain launches for M, as profilers print its name
+ * chain_kernel<out[0], out[1], out[2]>: activation rows, groups of 32 weights
+ * per lane, waves per workgroup.
+ * Errors: NULL out -> W4A16_ERR_NULL; M outside 1..8 -> W4A16_ERR_SHAPE.
+ */
+w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* w4a16_status_string(int32_t status);

@@ -97,6 +97,20 @@ BASE = 0x7F0000000000   # fake, never dereferenced
 def test_gemv_rejects_before_any_hip_call(w4a16_lib, args, status):
     x, p, y, M, N, K = args
     assert w4a16_lib.w4a16_gemv(x or None, p or None, y or None, M, N, K, None) == status
+    # the timed variant validates the same way (fake event handles, never used on error)
+    assert w4a16_lib.w4a16_gemv_timed(x or None, p or None, y or None, M, N, K, None, BASE, BASE) == status
+
+
+def test_timed_entry_points_need_both_events(w4a16_lib):
+    L = w4a16_lib
+    good = (BASE, BASE + 2**20, BASE + 2**30, 1, 64, 64)
+    assert L.w4a16_gemv_timed(*good, None, None, BASE) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemv_timed(*good, None, BASE, None) == w4.W4A16_ERR_NULL
+    ws = w4.W4A16_CHAIN_WORKSPACE_BYTES
+    assert L.w4a16_gemv_chain_timed(BASE, 1, 1, BASE, ws, None, None, BASE) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemv_chain_timed(BASE, 1, 1, BASE, ws, None, BASE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemv_chain_timed(BASE, 0, 1, BASE, ws, None, BASE, BASE) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemv_chain_timed(BASE, 1, 1, BASE, ws - 4, None, BASE, BASE) == w4.W4A16_ERR_SIZE
 
 
 def test_binding_checks(w4a16_lib):
@@ -127,6 +141,23 @@ def test_launch_shape_host_logic(w4a16_lib):
     with pytest.raises(w4.W4A16Error):
         shp(9, 5, 64)
     assert w4a16_lib.w4a16_launch_shape(1, 1, 64, None) == w4.W4A16_ERR_NULL
+    # the kernel name carries the mode: one wave per tile / waves split K / passes over K
+    assert shp(1, 6144, 4096)["kernel"] == "gemv_kernel<1, 2, 0>"
+    assert shp(1, 4096, 14336)["kernel"] == "gemv_kernel<1, 2, 1>"
+
+
+def test_chain_launch_shape(w4a16_lib):
+    for M in range(1, 9):
+        s = w4.chain_launch_shape(M)
+        assert s["M"] == M and s["gpl"] in (1, 2) and 1 <= s["waves"] <= 16
+        assert s["kernel"] == f"chain_kernel<{M}, {s['gpl']}, {s['waves']}>"
+        plan = w4.w4a16_chain_plan([(0x7F0000000000, 0x7F0001000000, 0x7F0040000000, 64, 64)], M)
+        hdr = plan[:64].view("<i4")
+        assert (hdr[4], hdr[5]) == (s["gpl"], s["waves"])   # the plan is made for that kernel
+    for M in (0, 9):
+        with pytest.raises(w4.W4A16Error):
+            w4.chain_launch_shape(M)
+    assert w4a16_lib.w4a16_chain_launch_shape(1, None) == w4.W4A16_ERR_NULL
 
 
 # ------------------------------------------------------------ decode-step chain

@@ -143,6 +143,26 @@ def test_bitwise_repeatable_and_stream_ordered(w4a16_lib):
     check(a.astype(np.float64), y_ref, B, "stream")
 
 
+def test_timed_launch_matches_and_times_the_kernel(w4a16_lib):
+    M, N, K = 1, 4096, 14336
+    x, codes, scale, mn = workload.random_problem(16, M, N, K, outliers=True)
+    xd, packed = _device_inputs(x, codes, scale, mn)
+    s = torch.cuda.Stream(device=DEV)
+    y0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        a.record(s)
+        b.record(s)
+        w4.w4a16_gemv(xd, packed, y0, s)
+        st = w4.w4a16_gemv_timed_raw(xd.data_ptr(), packed.data_ptr(), y1.data_ptr(), M, N, K, s.cuda_stream,
+                                     a.cuda_event, b.cuda_event)
+    assert st == w4.W4A16_OK
+    s.synchronize()
+    assert torch.equal(y0, y1)
+    assert 0.0 < a.elapsed_time(b) < 100.0        # ms: the kernel itself, a few microseconds
+
+
 def test_y_is_overwritten_not_accumulated(w4a16_lib):
     M, N, K = 2, 50, 1024
     x, codes, scale, mn = workload.random_problem(16, M, N, K)
