@@ -51,12 +51,7 @@ def gemv_bytes(M, N, K):
 # HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
 # only while the kernel is unchanged since the counters were taken.
-TRAFFIC = {
-    # (16,308.6 KiB FETCH_SIZE x 2.000 + 101.3 KiB WRITE_SIZE x 1.000) per dispatch
-    "gemv_kernel<1, 2, 0>": 33_503_787,
-    # (2,138,844.1 KiB x 2.000 + 11,401.1 KiB x 1.000) per dispatch
-    "chain_kernel<1, 2, 8>": 4_392_027_328,
-}
+TRAFFIC = {}
 
 
 def copy_calibration(torch, dev):

@@ -8,25 +8,42 @@
 // launch gap plus the ramp of the next kernel, about as long as streaming
 // 10 MB of weights; a 32-layer 8B step has 128 such boundaries.
 //
-// How: every workgroup walks the whole list. Product i's 4-row tiles are
-// spread over all workgroups; a workgroup's waves form teams of `wpr` waves,
-// a team covering all of K for its tile (wpr = 1 for K <= 4096 at M = 1).
-// Ordering between products is a device-wide counter in the caller's
-// workspace: a workgroup adds 1 (release) after writing its part of product
-// i, and before touching product i's x it waits (acquire) until the counter
-// reaches i * gridDim.x, i.e. every workgroup has finished products 0..i-1.
-// The first tile of product i is fetched BEFORE that wait: weights never
-// depend on earlier results, so HBM keeps streaming across the ordering
-// point. The wait spins a bounded number of times; if it gives up it flags
-// the workspace and the workgroup stops computing but still counts in, so a
-// starved launch ends instead of hanging. The last workgroup out resets the
-// counters for the next call.
+// How: one workgroup per CU, eight waves with two roles.
+//
+// * Seven compute waves only stream weights and do arithmetic. Product i's
+//   4-row tiles are split evenly over the workgroups; inside a workgroup a
+//   unit of work is (tile, K segment of 64*GPL groups), handed to the compute
+//   waves round-robin. Each wave keeps RING units' loads in registers and
+//   issues the loads of unit e+RING-1 before computing unit e, across product
+//   boundaries: weights never depend on earlier results, so HBM keeps
+//   streaming while the products' ordering points are reached. A unit's
+//   result (4 rows x M partial sums) goes to LDS; a compute wave never
+//   stores to global memory and never waits for its own stores, which on
+//   gfx9 would also wait for every weight load it has in flight.
+//
+// * One sync wave does everything that has to wait on memory: it stages each
+//   product's activations into LDS (coherent loads, since an earlier product
+//   of the same launch may have written them on another XCD), publishes them
+//   to the compute waves through an LDS counter, sums the segment partials in
+//   a fixed order and writes y with coherent stores, and takes part in the
+//   device-wide ordering between products.
+//
+// Ordering between products: after its y stores have completed, a
+// workgroup's sync wave adds 1 to its leaf of a two-level counter tree in the
+// caller's workspace; the last arrival at a leaf climbs to the top counter,
+// the last arrival at the top raises every leaf's flag to i+1. A sync wave
+// stages product i+1's x only after its leaf flag reaches i+1. Every wait is
+// bounded: a wait that gives up flags the workspace's error word, releases
+// the other workgroups and ends the launch (its results are then invalid),
+// so a launch whose workgroups cannot all be resident ends instead of
+// hanging. The last workgroup out resets the counters for the next call.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "w4a16.h"
 #include "w4a16_device.h"
@@ -37,23 +54,31 @@ using namespace w4a16_dev;
 namespace {
 
 constexpr uint32_t kChainMagic = 0x48433457u;  // "W4CH"
-constexpr uint32_t kChainVersion = 2;
-constexpr unsigned kSpinLimit = 1u << 20;      // polls before an ordering wait gives up (~1 s)
+constexpr uint32_t kChainVersion = 3;
+constexpr unsigned kSpinLimit = 1u << 20;      // global polls before an ordering wait gives up (~1 s)
+constexpr unsigned kLdsSpinLimit = 1u << 26;   // LDS polls before a wave gives up (several s)
 constexpr int kLeaves = 16;                    // leaf counters of the ordering tree
 constexpr int kLineWords = 1024;               // 4 KiB between counters (separate memory pages)
+constexpr int kWaves = 8;                      // per workgroup
+constexpr int kComputeWaves = kWaves - 1;      // wave kWaves-1 is the sync wave
 constexpr int kXLdsBytes = 65536;              // LDS staging of one pass of x
+constexpr int kYLdsBytes = 65536;              // LDS partial sums of one block of tiles
+constexpr int kLoadCoherent = 16;              // buffer-load cache policy: device-coherent (sc1)
 
-// One workgroup per CU, with as many waves as the register budget of the
-// instantiation allows per SIMD (x4 SIMDs).
-constexpr int chain_waves(int M) { return 8; }
-// groups per lane (the x slice stays within 32 VGPRs)
+// groups per lane (the x slice stays within 32 VGPRs at M = 1 and 2)
 constexpr int chain_gpl(int M) { return M == 1 ? 2 : 1; }
-// groups of x one pass can stage in LDS
-constexpr int chain_lds_groups(int M) { return kXLdsBytes / (64 * M); }
+// groups of one K segment (one unit of work covers one segment of one tile)
+constexpr int chain_seg_groups(int M) { return 64 * chain_gpl(M); }
+// segments of x one LDS pass holds, and the LDS row stride of x in groups
+constexpr int chain_pass_segs(int M) { return kXLdsBytes / (64 * M) / chain_seg_groups(M); }
+constexpr int chain_x_groups(int M) { return chain_pass_segs(M) * chain_seg_groups(M); }
+// units whose loads a compute wave keeps in registers (register budget: two
+// waves per SIMD, 256 VGPRs each)
+constexpr int chain_ring(int M) { return M == 1 ? 4 : M == 2 ? 8 : M <= 4 ? 6 : M == 5 ? 4 : 3; }
 
 struct ChainHeader {
   uint32_t magic, version;
-  int32_t count, M, gpl, ww;
+  int32_t count, M, gpl, ring;
   int32_t pad[10];
 };
 static_assert(sizeof(ChainHeader) == 64, "plan header is 64 bytes");
@@ -63,10 +88,21 @@ struct ChainEntry {
   const u32x4* codes;
   const u32x4* sm;
   float* y;
-  int32_t N, G, T, wpr, passes;
-  int32_t pad[3];
+  int32_t N, G, T;  // rows, groups per row, 4-row tiles
+  int32_t S;        // K segments per tile
+  int32_t passes;   // LDS passes of x over the segments
+  int32_t TB;       // tiles per block (the LDS partials of one block fit kYLdsBytes)
+  int32_t pad[2];
 };
 static_assert(sizeof(ChainEntry) == 64, "plan entry is 64 bytes");
+
+// The plan never changes during a launch: it is read through the constant
+// address space, which the compiler always serves with scalar loads. Through
+// a global pointer, the y stores and the ordering operations of the kernel
+// would make it assume the plan may have changed and read it with vector
+// loads, whose completion shares the in-order counter of the weight loads in
+// flight and would drain them at every product boundary.
+typedef const __attribute__((address_space(4))) ChainEntry* EntryPtr;
 
 // Workspace words: the tree's top counter, the exit counter and the error
 // word share the first page; leaf g's counter and flag sit on page 1 + g.
@@ -85,297 +121,403 @@ __device__ __forceinline__ void st_coherent(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int M, int GPL, int WW>
-__global__ void __launch_bounds__(64 * WW)
+// Product p as one workgroup sees it, walked stage by stage: a stage is
+// (block b of this workgroup's tiles, LDS pass c over K); its units are
+// (tile, segment) pairs, tile-major. All fields are wave-uniform.
+struct Walk {
+  int p, b, c, s;  // product, block, pass, running stage number
+  EntryPtr e;
+  int t0, ntile, nb;     // this workgroup's tiles of product p, blocks
+  int tb0, nt, sg0, ns;  // the stage's first tile and count, first segment and count
+};
+
+__device__ __forceinline__ void walk_product(Walk& w, EntryPtr ents, int p, int nwg, int wg) {
+  w.p = p;
+  w.e = ents + p;
+  const int T = w.e->T, TB = w.e->TB;
+  const int q = T / nwg, rem = T - q * nwg;
+  w.t0 = wg * q + (wg < rem ? wg : rem);
+  w.ntile = q + (wg < rem ? 1 : 0);
+  w.nb = w.ntile > 0 ? (w.ntile + TB - 1) / TB : 1;  // a workgroup with no tiles still walks one empty stage
+  w.b = 0;
+  w.c = 0;
+}
+
+template <int M>
+__device__ __forceinline__ void walk_stage(Walk& w) {
+  constexpr int SP = chain_pass_segs(M);
+  const int TB = w.e->TB, S = w.e->S;
+  w.tb0 = w.t0 + w.b * TB;
+  const int left = w.ntile - w.b * TB;
+  w.nt = left < TB ? (left > 0 ? left : 0) : TB;
+  w.sg0 = w.c * SP;
+  w.ns = S - w.sg0 < SP ? S - w.sg0 : SP;
+}
+
+// next stage; false past the last product
+template <int M>
+__device__ __forceinline__ bool walk_next(Walk& w, EntryPtr ents, int count, int nwg, int wg) {
+  ++w.s;
+  if (++w.c == w.e->passes) {
+    w.c = 0;
+    if (++w.b == w.nb) {
+      if (w.p + 1 >= count) {
+        w.p = count;
+        return false;
+      }
+      walk_product(w, ents, w.p + 1, nwg, wg);
+    }
+  }
+  walk_stage<M>(w);
+  return true;
+}
+
+// A compute wave's position: a stage, and unit ti * ns + si of it, i.e. tile
+// tb0 + ti and segment sg0 + si (wave v takes units v, v + 7, ... of every
+// stage). Kept as (ti, si) and moved with scalar adds: an integer division
+// here would be emulated in vector registers right next to the weight loads.
+struct Cursor {
+  Walk w;
+  int ti, si;
+};
+
+// unit index (ti, si) + n within a stage of ns segments per tile
+__device__ __forceinline__ void unit_add(int& ti, int& si, int ns, int n) {
+  si += n;
+  if (ns == 1) {
+    ti += si;
+    si = 0;
+  } else {
+    while (si >= ns) {
+      si -= ns;
+      ++ti;
+    }
+  }
+}
+
+// move past stages where this wave has no unit
+template <int M>
+__device__ __forceinline__ void cursor_settle(Cursor& u, EntryPtr ents, int count, int nwg, int wg,
+                                              int wave) {
+  while (u.w.p < count && u.ti >= u.w.nt) {
+    if (!walk_next<M>(u.w, ents, count, nwg, wg)) break;
+    u.ti = 0;
+    u.si = 0;
+    unit_add(u.ti, u.si, u.w.ns, wave);
+  }
+}
+
+// Activations read from LDS as they are used: chunk d of row m's group at
+// pass-local index gl[j], and that group's sum (written by the sync wave).
+template <int M, int GPL, int XG>
+struct LdsX {
+  const u32x4* xl;
+  const float* xsl;
+  int gl[GPL];
+  __device__ __forceinline__ u32x4 x(int m, int j, int d) const { return xl[(m * XG + gl[j]) * 4 + d]; }
+  __device__ __forceinline__ float sum(int m, int j) const { return xsl[m * XG + gl[j]]; }
+};
+
+// step(k) for k = K .. RING-1 with k a compile-time constant (the ring's
+// buffer indices must be constants; a pragma cannot unroll a loop this size
+// with an exit in it); false as soon as one step ends the walk
+template <int K, int RING, class Step>
+__device__ __forceinline__ bool ring_steps(Step& step) {
+  if constexpr (K == RING) {
+    return true;
+  } else {
+    if (!step(std::integral_constant<int, K>{})) return false;
+    return ring_steps<K + 1, RING>(step);
+  }
+}
+
+template <int M, int GPL, int RING>
+__global__ void __launch_bounds__(64 * kWaves)
 chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int count) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwg = gridDim.x;
+  const int wg = blockIdx.x;
   if (hdr->magic != kChainMagic || hdr->version != kChainVersion || hdr->count != count || hdr->M != M ||
-      hdr->gpl != GPL || hdr->ww != WW)
+      hdr->gpl != GPL || hdr->ring != RING)
     return;  // every workgroup sees the same header, so all leave together
-  const ChainEntry* __restrict__ ents = reinterpret_cast<const ChainEntry*>(hdr + 1);
+  const EntryPtr ents = (EntryPtr)(reinterpret_cast<uintptr_t>(hdr + 1));
 
-  __shared__ u32x4 xl[kXLdsBytes / 16];                      // x of the current pass: [m][group][32 halfs]
-  __shared__ float part[kTilesPerBlock][kTileRows][M][WW];  // [tile][row][m][wave]
+  constexpr int SG = chain_seg_groups(M);
+  constexpr int XG = chain_x_groups(M);
+  __shared__ u32x4 xl[kXLdsBytes / 16];  // x of the current pass: [m][XG groups][32 halfs]
+  __shared__ float xsl[kXLdsBytes / 64];  // the pass's group sums: [m][XG groups]
+  __shared__ float ys[kYLdsBytes / 4];   // partials of the current block: [tile][segment][row][m]
+  __shared__ int x_epoch;                // stages whose x is in xl
+  __shared__ int units_done;             // units written to ys so far
   __shared__ int s_abort;
 
-  // ordering tree: workgroup b reports to leaf b % leaves
-  const int leaves = nwg < kLeaves ? nwg : kLeaves;
-  const int leaf = int(blockIdx.x) % leaves;
-  const unsigned leaf_size = unsigned((nwg - leaf + leaves - 1) / leaves);
-
-  // product i as seen by this wave (all fields wave-uniform)
-  struct Geo {
-    const u32x4* x;
-    const u32x4* codes;
-    const u32x4* sm;
-    float* y;
-    int N, G, T, wpr, passes, pg, teams, team, wit, tpb, nblocks, rounds;
-    bool direct;
-  };
-  auto geo = [&](int i) {
-    const ChainEntry e = ents[i];
-    Geo g;
-    g.x = e.x;
-    g.codes = e.codes;
-    g.sm = e.sm;
-    g.y = e.y;
-    g.N = e.N;
-    g.G = e.G;
-    g.T = e.T;
-    g.wpr = e.wpr;
-    g.passes = e.passes;
-    g.pg = g.wpr * 64 * GPL;  // groups per pass
-    g.teams = WW / g.wpr;
-    g.team = wave / g.wpr;
-    g.wit = wave % g.wpr;
-    g.direct = g.wpr == 1 && g.passes == 1;
-    const int units = nwg * g.teams;
-    const int tpb = g.direct ? 1 : g.T / units;
-    g.tpb = tpb < 1 ? 1 : (tpb > kTilesPerBlock ? kTilesPerBlock : tpb);
-    g.nblocks = (g.T + g.tpb - 1) / g.tpb;
-    g.rounds = (g.nblocks + units - 1) / units;
-    return g;
-  };
-
-  // an item is (product i, round k, pass c over K, tile tb of the block);
-  // in round k team `team` of this workgroup owns block (k*nwg + wg)*teams + team
-  struct Item {
-    int i, k, c, tb;
-  };
-  auto next_item = [&](const Geo& g, Item it) {
-    Item n = it;
-    if (++n.tb < g.tpb) return n;
-    n.tb = 0;
-    if (++n.c < g.passes) return n;
-    n.c = 0;
-    if (++n.k < g.rounds) return n;
-    n.k = 0;
-    ++n.i;
-    return n;
-  };
-  auto block_of = [&](const Geo& g, int k, int team) { return (k * nwg + int(blockIdx.x)) * g.teams + team; };
-  // issue the loads of item `it`; a team with no tile in it (or `enable`
-  // false) issues out-of-range buffer loads that cost no memory traffic, so
-  // the fetch never sits behind a branch
-  auto fetch = [&](const Geo& g, Item it, TileLoads<GPL>& L, bool enable) {
-    const int b = block_of(g, it.k, g.team);
-    const int t = b * g.tpb + it.tb;
-    const bool valid = enable && b < g.nblocks && t < g.T;
-    int g0[GPL];
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) g0[j] = it.c * g.pg + (g.wit * GPL + j) * 64;
-    fetch_tile_rsrc<GPL>(g.codes, g.sm, g.N, g.G, valid ? t : 0, g0, lane, valid, L);
-  };
-
-  u32x4 xv[M][GPL][4];
-  float xs[M][GPL];
-  bool aborted = false;
-  int arrived = 0;
-  int x_i = -1, x_c = -1;  // product and pass whose x is in registers
-
-  // pass c of product g's activations: global -> LDS (coherent loads, since
-  // an earlier product of this launch may have written them on another XCD),
-  // then this wave's slice LDS -> VGPRs
-  auto stage_x = [&](const Geo& g, int c) {
-    const int g_first = c * g.pg;
-    const int ng = min(g.pg, g.G - g_first);
-    lds_barrier();  // every wave is done with the previous pass's LDS copy
-    const int words = M * ng * 8;  // 8-byte words
-    for (int w = threadIdx.x; w < words; w += blockDim.x) {
-      const int m = w / (ng * 8);
-      const int r = w - m * ng * 8;  // word within row m's slice
-      const unsigned long long* src =
-          reinterpret_cast<const unsigned long long*>(g.x + (size_t(m) * g.G + g_first) * 4) + r;
-      const unsigned long long v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      reinterpret_cast<unsigned long long*>(xl)[size_t(m) * g.pg * 8 + r] = v;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const int gl = (g.wit * GPL + j) * 64 + lane;  // group within the pass
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[m][j][q] = u32x4{0, 0, 0, 0};
-        if (gl < ng) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) xv[m][j][q] = xl[(size_t(m) * g.pg + gl) * 4 + q];
-        }
+  // Poll an LDS counter until it reaches v; false: the launch is being
+  // abandoned. Every lane reads the same word; taking lane 0's value keeps the
+  // loop's exit (and so everything after it) wave-uniform in the compiler's
+  // eyes, which keeps the walk in scalar registers and its plan reads scalar.
+  auto lds_wait_ge = [&](const int* p, int v) __attribute__((always_inline)) -> bool {
+    unsigned spins = 0;
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < v) {
+      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&s_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
+        return false;
+      if (++spins > kLdsSpinLimit) {
+        __hip_atomic_store(&s_abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return false;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-#pragma unroll
-      for (int j = 0; j < GPL; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s = dot2(elem(xv[m][j][q], e), kOnes, s);
-        }
-        xs[m][j] = s;
-      }
-    }
+    return true;
   };
 
-  // this workgroup's results of product i are written: report to the tree;
-  // the last report of a leaf climbs to the top, the last at the top raises
-  // every leaf's flag to i+1. Called before the next tile is fetched, so the
-  // atomics' returns do not wait behind that prefetch (vmcnt is in order).
-  auto arrive = [&](int i) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent y stores are complete
-    __builtin_amdgcn_s_barrier();   // ... and every other wave's
-    if (threadIdx.x == 0) {
-      const unsigned old = add_coherent(ws + leaf_word(leaf), 1u);
-      if (old == unsigned(i + 1) * leaf_size - 1u) {
-        const unsigned top = add_coherent(ws + kTopWord, 1u);
-        if (top == unsigned(i + 1) * unsigned(leaves) - 1u)
-          for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(i + 1));
-      }
-    }
-    ++arrived;
-  };
-  // wait until products 0..i-1 are complete everywhere
-  auto wait_for = [&](int i) {
-    if (threadIdx.x == 0) {
-      unsigned spins = 0;
-      int ab = 0;
-      while (ld_coherent(ws + flag_word(leaf)) < unsigned(i)) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          ab = 1;
-          add_coherent(ws + kErrorWord, 1u);
-          break;
-        }
-      }
-      s_abort = ab;
-    }
-    lds_barrier();
-    aborted = s_abort != 0;
-  };
+  if (wave < kComputeWaves) {
+    // ------------------------------------------------------------ compute wave
+    const int voff = lane * 16;  // this lane's byte offset in every weight descriptor
+    auto fetch = [&](const Cursor& u, TileLoads<GPL>& L) __attribute__((always_inline)) {
+      // -1 inside the walk, 0 past its end (every load then out of range)
+      const int valid = ~((count - 1 - u.w.p) >> 31);
+      const int seg = u.w.sg0 + u.si;
+      int g0[GPL];
+#pragma unroll
+      for (int k = 0; k < GPL; ++k) g0[k] = seg * SG + k * 64;
+      const EntryPtr e = u.w.e;
+      fetch_tile_rows<GPL>(e->codes, e->sm, e->N, e->G, (u.w.tb0 + u.ti) & valid, g0, voff, valid, L);
+    };
 
-  auto finish = [&](const Geo& g, Item it, const TileLoads<GPL>& L) {
-    if (it.tb == 0 && (it.i != x_i || it.c != x_c)) {  // this (product, pass) needs its x
-      if (it.k == 0 && it.c == 0 && it.i > 0) wait_for(it.i);
-      if (!aborted) stage_x(g, it.c);
-      x_i = it.i;
-      x_c = it.c;
-    }
-    const int b = block_of(g, it.k, g.team);
-    const int t = b * g.tpb + it.tb;
-    if (!aborted && b < g.nblocks && t < g.T) {
+    int cur_s = -1;
+
+    // compute unit u from its loads; false when the walk is over
+    auto consume = [&](const Cursor& u, const TileLoads<GPL>& L) __attribute__((always_inline)) -> bool {
+      if (u.w.p >= count) return false;
+      if (u.w.s != cur_s) {
+        if (!lds_wait_ge(&x_epoch, u.w.s + 1)) return false;
+        cur_s = u.w.s;
+      }
+      const int ti = u.ti;
+      const int seg = u.w.sg0 + u.si;
+      LdsX<M, GPL, XG> xa{xl, xsl, {}};
+#pragma unroll
+      for (int k = 0; k < GPL; ++k) xa.gl[k] = (seg - u.w.sg0) * SG + k * 64 + lane;
       float acc[kTileRows][M];
-      compute_tile<M, GPL>(L, xv, xs, acc);
-      if (g.direct) {
-        store_tile<M, true>(acc, g.y, g.N, t, lane);
-      } else if (lane == 0) {
+      compute_tile<M, GPL>(L, xa, acc);
+      // lane r*M + m writes the partial of row r, activation row m
+      float v = 0.f;
 #pragma unroll
-        for (int r = 0; r < kTileRows; ++r)
+      for (int i = 0; i < kTileRows * M; ++i)
+        if (lane == i) v = acc[i / M][i % M];
+      if (lane < kTileRows * M) ys[(ti * u.w.e->S + seg) * kTileRows * M + lane] = v;
+      if (lane == 0) __hip_atomic_fetch_add(&units_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return true;
+    };
+
+    Cursor F;
+    F.w.s = 0;
+    walk_product(F.w, ents, 0, nwg, wg);
+    walk_stage<M>(F.w);
+    F.ti = 0;
+    F.si = 0;
+    unit_add(F.ti, F.si, F.w.ns, wave);
+    cursor_settle<M>(F, ents, count, nwg, wg, wave);
+    Cursor C = F;
+    auto advance = [&](Cursor& u) __attribute__((always_inline)) {
+      unit_add(u.ti, u.si, u.w.ns, kComputeWaves);
+      cursor_settle<M>(u, ents, count, nwg, wg, wave);
+    };
+
+    // Ring of RING load buffers in a fixed rotation: the loads of the unit
+    // RING-1 ahead are issued before each unit is computed, so RING-1 units
+    // stay in flight while one is computed. Every fetch is unconditional
+    // (past the end it reads nothing), so no buffer is merged behind a branch.
+    TileLoads<GPL> L[RING];
 #pragma unroll
-          for (int m = 0; m < M; ++m)
-            part[it.tb][r][m][wave] = (it.c == 0 ? 0.f : part[it.tb][r][m][wave]) + acc[r][m];
-      }
+    for (int k = 0; k < RING - 1; ++k) {
+      fetch(F, L[k]);
+      advance(F);
     }
-    if (!g.direct && it.c == g.passes - 1 && it.tb == g.tpb - 1) {  // block done: combine each team's waves
-      lds_barrier();
-      if (!aborted) {
-        const int per_team = g.tpb * kTileRows * M;
-        for (int idx = threadIdx.x; idx < g.teams * per_team; idx += blockDim.x) {
-          const int m = idx % M;
-          const int r = (idx / M) % kTileRows;
-          const int tb = (idx / (M * kTileRows)) % g.tpb;
-          const int team = idx / per_team;
-          const int bb = block_of(g, it.k, team);
-          const int tt = bb * g.tpb + tb;
-          const int n = tt * kTileRows + r;
-          if (bb < g.nblocks && tt < g.T && n < g.N) {
-            float s = 0.f;
-            for (int w = 0; w < g.wpr; ++w) s += part[tb][r][m][team * g.wpr + w];
-            store_y<true>(g.y + size_t(m) * g.N + n, s);
+    lds_barrier();  // the sync wave has initialised the LDS counters
+    auto step = [&](auto kc) __attribute__((always_inline)) -> bool {
+      constexpr int k = decltype(kc)::value % RING;
+      fetch(F, L[(k + RING - 1) % RING]);
+      advance(F);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!consume(C, L[k])) return false;
+      advance(C);
+      return true;
+    };
+    // two rotations per loop trip: the compiler's wait counts at the top of
+    // the loop are conservative (one unit in flight instead of RING-1)
+    while (ring_steps<0, 2 * RING>(step)) {
+    }
+  } else {
+    // --------------------------------------------------------------- sync wave
+    // ordering tree: workgroup b reports to leaf b % leaves
+    const int leaves = nwg < kLeaves ? nwg : kLeaves;
+    const int leaf = wg % leaves;
+    const unsigned leaf_size = unsigned((nwg - leaf + leaves - 1) / leaves);
+    if (lane == 0) {
+      x_epoch = 0;
+      units_done = 0;
+      s_abort = 0;
+    }
+    lds_barrier();
+
+    bool aborted = false;
+    int arrived = 0;
+    auto give_up = [&]() {
+      aborted = true;
+      if (lane == 0) {
+        add_coherent(ws + kErrorWord, 1u);
+        __hip_atomic_store(&s_abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+    // wait until products 0..i-1 are complete everywhere; false: give up
+    auto wait_for = [&](int i) -> bool {
+      int ok = 1;
+      if (lane == 0) {
+        unsigned spins = 0;
+        while (ld_coherent(ws + flag_word(leaf)) < unsigned(i)) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kSpinLimit) {
+            ok = 0;
+            break;
           }
         }
       }
-      lds_barrier();  // partials read before the next block writes them
-    }
-  };
+      return __builtin_amdgcn_readfirstlane(ok) != 0;
+    };
+    // this workgroup's results of product i are written: report to the tree;
+    // the last report of a leaf climbs to the top, the last at the top raises
+    // every leaf's flag to i+1
+    auto arrive = [&](int i) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent y stores are complete
+      if (lane == 0) {
+        const unsigned old = add_coherent(ws + leaf_word(leaf), 1u);
+        if (old == unsigned(i + 1) * leaf_size - 1u) {
+          const unsigned top = add_coherent(ws + kTopWord, 1u);
+          if (top == unsigned(i + 1) * unsigned(leaves) - 1u)
+            for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(i + 1));
+        }
+      }
+      ++arrived;
+    };
+    // the stage's pass of activations, global -> LDS, with each group's sum;
+    // groups of the pass's last segment past G read as zeros. All loads of a
+    // batch are issued before the first is used: staging sits between an
+    // ordering point and the compute of the next product. The first product's
+    // activations were written before the launch and are read through the
+    // caches; every later product's may have been written by an earlier
+    // product of this launch on another XCD and are read device-coherently.
+    auto stage_x = [&](const Walk& w, auto policy) {
+      constexpr int kPolicy = decltype(policy)::value;
+      const EntryPtr e = w.e;
+      const int G = e->G;
+      const int gb = w.sg0 * SG;                               // first group of the pass
+      const int ng = G - gb < w.ns * SG ? G - gb : w.ns * SG;  // groups of x in the pass
+      const int chunks = ng * 4;                               // 16-byte chunks per activation row
+      const int total = M * chunks;
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(e->x, M * G * 64);
+      constexpr int kBatch = 16;
+      for (int base = 0; base < total; base += 64 * kBatch) {
+        u32x4 v[kBatch];
+        int mk[kBatch], rk[kBatch];
+        int m = (base + lane) / chunks, r = base + lane - m * chunks;  // chunk r of activation row m
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          mk[k] = m;
+          rk[k] = r;
+          // past the end: an offset beyond the buffer reads zeros and no memory
+          const int off = m < M ? ((m * G + gb) * 4 + r) * 16 : M * G * 64;
+          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kPolicy);
+          r += 64;
+          while (r >= chunks) {
+            r -= chunks;
+            ++m;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          // lanes 4g..4g+3 hold group g's four chunks: its sum in the fixed tree
+          float t = chunk_sum(v[k]);
+          t += dpp<0xB1>(t);  // (c0 + c1), (c2 + c3)
+          t += dpp<0x4E>(t);  // (c0 + c1) + (c2 + c3)
+          if (mk[k] < M) {
+            xl[mk[k] * XG * 4 + rk[k]] = v[k];
+            if ((lane & 3) == 0) xsl[mk[k] * XG + rk[k] / 4] = t;
+          }
+        }
+      }
+      const int pad = w.ns * SG - ng;  // groups past G in the last segment
+      for (int idx = lane; idx < M * pad * 4; idx += 64) {
+        const int m = idx / (pad * 4), r = idx - m * (pad * 4);
+        xl[m * XG * 4 + chunks + r] = u32x4{0, 0, 0, 0};
+        if ((r & 3) == 0) xsl[m * XG + ng + r / 4] = 0.f;
+      }
+    };
+    // the block's partials, summed over segments in order, to y
+    auto flush = [&](const Walk& w) {
+      const EntryPtr e = w.e;
+      const int S = e->S, N = e->N;
+      for (int idx = lane; idx < w.nt * kTileRows * M; idx += 64) {
+        const int ti = idx / (kTileRows * M);
+        const int rm = idx - ti * (kTileRows * M);
+        const int n = (w.tb0 + ti) * kTileRows + rm / M;
+        float s = 0.f;
+        for (int seg = 0; seg < S; ++seg) s += ys[(ti * S + seg) * kTileRows * M + rm];
+        if (n < N) store_y<true>(e->y + size_t(rm % M) * N + n, s);
+      }
+    };
 
-  // Two load buffers used alternately: the next item's tile is in flight
-  // while the current one is computed. Inside a product the next fetch is
-  // issued first; at a product's last item the results are written and
-  // reported first, then the next product's first tile is fetched, and only
-  // then (at that product's first item) does the workgroup wait for the
-  // others, with the tile in flight. Every fetch is unconditional: a fetch
-  // behind a branch makes the compiler merge buffer contents with register
-  // moves that wait for the loads in flight.
-  Item ia{0, 0, 0, 0};
-  Geo ga = geo(0);
-  if constexpr (double_buffered(M)) {
-    TileLoads<GPL> la, lb;
-    fetch(ga, ia, la, true);
+    Walk w;
+    w.s = 0;
+    walk_product(w, ents, 0, nwg, wg);
+    walk_stage<M>(w);
+    int units = 0;
+    int staged_p = -1, staged_c = -1;
     while (true) {
-      const Item ib = next_item(ga, ia);
-      const bool more_b = ib.i < count;
-      const bool edge_b = ib.i != ia.i;
-      const Geo gb = (edge_b && more_b) ? geo(ib.i) : ga;
-      if (!edge_b) {
-        fetch(gb, ib, lb, true);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(ga, ia, la);
-      } else {
-        finish(ga, ia, la);
-        arrive(ia.i);
-        fetch(gb, ib, lb, more_b);
+      const int p = w.p;
+      if (w.b == 0 && w.c == 0 && p > 0) {  // a new product: every earlier one must be complete
+        if (!wait_for(p)) {
+          give_up();
+          break;
+        }
       }
-      if (!more_b || aborted) break;
-
-      const Item ic = next_item(gb, ib);
-      const bool more_c = ic.i < count;
-      const bool edge_c = ic.i != ib.i;
-      const Geo gc = (edge_c && more_c) ? geo(ic.i) : gb;
-      if (!edge_c) {
-        fetch(gc, ic, la, true);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(gb, ib, lb);
-      } else {
-        finish(gb, ib, lb);
-        arrive(ib.i);
-        fetch(gc, ic, la, more_c);
+      if (w.nt > 0 && (p != staged_p || w.c != staged_c)) {
+        if (p == 0)
+          stage_x(w, std::integral_constant<int, 0>{});
+        else
+          stage_x(w, std::integral_constant<int, kLoadCoherent>{});
+        staged_p = p;
+        staged_c = w.c;
       }
-      if (!more_c || aborted) break;
-      ia = ic;
-      ga = gc;
+      units += w.nt * w.ns;
+      if (lane == 0) __hip_atomic_store(&x_epoch, w.s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (!lds_wait_ge(&units_done, units)) {
+        give_up();
+        break;
+      }
+      const bool block_done = w.c == w.e->passes - 1;
+      const bool product_done = block_done && w.b == w.nb - 1;
+      if (block_done && w.nt > 0) flush(w);
+      if (!walk_next<M>(w, ents, count, nwg, wg)) break;
+      if (product_done) arrive(p);
     }
-  } else {
-    // more activation rows: VALU bound, registers go to the x slices
-    while (true) {
-      TileLoads<GPL> la;
-      fetch(ga, ia, la, true);
-      const Item ib = next_item(ga, ia);
-      finish(ga, ia, la);
-      if (ib.i != ia.i) arrive(ia.i);
-      if (ib.i >= count || aborted) break;
-      if (ib.i != ia.i) ga = geo(ib.i);
-      ia = ib;
-    }
-  }
 
-  // Count out. After an abort, first release every waiter (results of this
-  // call are then invalid and the error word says so). The last workgroup
-  // out resets every counter and flag for the next call.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (arrived < count)
-      for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(count));
-    const unsigned prev = add_coherent(ws + kExitWord, 1u);
-    if (prev == unsigned(nwg) - 1u) {
-      st_coherent(ws + kTopWord, 0u);
-      for (int l = 0; l < leaves; ++l) {
-        st_coherent(ws + leaf_word(l), 0u);
-        st_coherent(ws + flag_word(l), 0u);
+    // Count out. After giving up, first release every waiter (results of this
+    // call are then invalid and the error word says so). The last workgroup
+    // out resets every counter and flag for the next call. A single product
+    // touches no counter and skips this.
+    if (lane == 0 && count > 1) {
+      if (aborted || arrived < count - 1)
+        for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(count));
+      const unsigned prev = add_coherent(ws + kExitWord, 1u);
+      if (prev == unsigned(nwg) - 1u) {
+        st_coherent(ws + kTopWord, 0u);
+        for (int l = 0; l < leaves; ++l) {
+          st_coherent(ws + leaf_word(l), 0u);
+          st_coherent(ws + flag_word(l), 0u);
+        }
+        st_coherent(ws + kExitWord, 0u);
       }
-      st_coherent(ws + kExitWord, 0u);
     }
   }
 }
@@ -384,7 +526,7 @@ typedef void (*chain_fn)(const ChainHeader*, unsigned*, int);
 
 template <int M>
 constexpr chain_fn chain_instance() {
-  return &chain_kernel<M, chain_gpl(M), chain_waves(M)>;
+  return &chain_kernel<M, chain_gpl(M), chain_ring(M)>;
 }
 
 chain_fn chain_for(int M) {
@@ -399,21 +541,6 @@ chain_fn chain_for(int M) {
     case 8: return chain_instance<8>();
     default: return nullptr;
   }
-}
-
-// waves per team for a product of G groups: the fewest that divide the
-// workgroup and cover K in one pass, within the LDS staging limit; otherwise
-// the widest such team and several passes
-void team_shape(int M, int G, int* wpr_out, int* passes_out) {
-  const int ww = chain_waves(M), gpl = chain_gpl(M), cap = chain_lds_groups(M);
-  int best = 0;
-  for (int w = 1; w <= ww; ++w) {
-    if (ww % w || w * 64 * gpl > cap) continue;
-    best = w;
-    if (w * 64 * gpl >= G) break;
-  }
-  *wpr_out = best;
-  *passes_out = (G + best * 64 * gpl - 1) / (best * 64 * gpl);
 }
 
 std::atomic<int> g_chain_occupancy[kMaxM + 1];
@@ -434,7 +561,6 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
   if (count < 1 || count > kMaxChain || M < 1 || M > kMaxM) return W4A16_ERR_SHAPE;
   const size_t need = w4a16_chain_plan_bytes(count);
   if (plan_bytes < need) return W4A16_ERR_SIZE;
-  const int gpl = chain_gpl(M);
   for (int32_t i = 0; i < count; ++i) {
     const w4a16_chain_entry& e = entries[i];
     if (!e.x || !e.packed || !e.y) return W4A16_ERR_NULL;
@@ -461,15 +587,14 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
   h.version = kChainVersion;
   h.count = count;
   h.M = M;
-  h.gpl = gpl;
-  h.ww = chain_waves(M);
+  h.gpl = chain_gpl(M);
+  h.ring = chain_ring(M);
+  const int sg = chain_seg_groups(M), sp = chain_pass_segs(M);
   uint8_t* out = static_cast<uint8_t*>(plan);
   std::memcpy(out, &h, sizeof(h));
   for (int32_t i = 0; i < count; ++i) {
     const w4a16_chain_entry& e = entries[i];
     const int G = e.K / kGroup;
-    int wpr = 0, passes = 0;
-    team_shape(M, G, &wpr, &passes);
     const size_t codes_region = (size_t(e.N) * size_t(e.K) / 2 + 255) / 256 * 256;
     ChainEntry c;
     std::memset(&c, 0, sizeof(c));
@@ -480,8 +605,10 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
     c.N = e.N;
     c.G = G;
     c.T = (e.N + kTileRows - 1) / kTileRows;
-    c.wpr = wpr;
-    c.passes = passes;
+    c.S = (G + sg - 1) / sg;
+    c.passes = (c.S + sp - 1) / sp;
+    // one tile's partials fit: S * 4 * M floats <= kYLdsBytes for every K <= w4a16_max_k
+    c.TB = kYLdsBytes / (c.S * kTileRows * M * int(sizeof(float)));
     std::memcpy(out + sizeof(ChainHeader) + size_t(i) * sizeof(ChainEntry), &c, sizeof(c));
   }
   return W4A16_OK;
@@ -492,7 +619,7 @@ extern "C" w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]) {
   if (M < 1 || M > kMaxM) return W4A16_ERR_SHAPE;
   out[0] = M;
   out[1] = chain_gpl(M);
-  out[2] = chain_waves(M);
+  out[2] = chain_ring(M);
   return W4A16_OK;
 }
 
@@ -509,17 +636,16 @@ w4a16_status chain_enqueue(const void* plan, int32_t count, int32_t M, void* wor
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   int occ = g_chain_occupancy[M].load(std::memory_order_relaxed);
   if (occ <= 0) {
-    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * chain_waves(M));
+    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * kWaves);
     g_chain_occupancy[M].store(occ, std::memory_order_relaxed);
   }
-  if (const int o = w4a16_host::tune("W4A16_TUNE_CHAIN_OCC")) occ = o < occ ? o : occ;  // sweep builds only
   // every workgroup must be resident at once: the grid is the occupancy limit
   const int grid = w4a16_host::cu_count(dev) * occ;
   const ChainHeader* hp = static_cast<const ChainHeader*>(plan);
   unsigned* wp = static_cast<unsigned*>(workspace);
   int n_arg = count;
   void* args[] = {&hp, &wp, &n_arg};
-  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * chain_waves(M)), args, 0,
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * kWaves), args, 0,
                          static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;

@@ -102,26 +102,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
 }
 
-// fetch_tile with buffer loads: when `valid` is false (a team with no tile
-// this round) every load is out of range and costs no memory traffic, so the
-// caller need not branch around the fetch. Lane and row clamping as above.
+// fetch_tile with buffer loads and no per-lane address arithmetic: every
+// (row, group slot) gets its own descriptor, based at the slot's first group
+// and sized to the groups left in the row, and lane l reads at byte offset
+// voff = 16 * l (computed once by the caller). Lanes past the end of the row
+// fall outside the descriptor and read zeros without touching memory (their
+// activations are zero too, so they add exactly 0). `valid` = 0 sizes every
+// descriptor to 0 (a team with no tile, or a fetch past the end: no traffic,
+// and no branch around the fetch); it must be -1 otherwise, formed by integer
+// arithmetic on scalar values (a select of a comparison would be built in a
+// vector register). All address arithmetic is scalar: a vector temporary
+// here can be placed by the register allocator in a buffer whose previous
+// load the compiler cannot prove complete, and it then waits for it. A row
+// past N reads row N-1 (its results are never stored).
 template <int GPL>
-__device__ __forceinline__ void fetch_tile_rsrc(const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
-                                                int N, int G, int t, const int (&g0)[GPL], int lane, bool valid,
+__device__ __forceinline__ void fetch_tile_rows(const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
+                                                int N, int G, int t, const int (&g0)[GPL], int voff, int valid,
                                                 TileLoads<GPL>& L) {
-  const int lim = valid ? -1 : 0;  // -1: the whole 32-bit range
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + size_t(t) * kTileRows * G, lim);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sm + size_t(t) * G, lim);
 #pragma unroll
   for (int j = 0; j < GPL; ++j) {
-    const int last = G - 1 - g0[j];
-    const int gl = lane < last ? lane : (last > 0 ? last : 0);
-    const int grp = g0[j] + (last < 0 ? last : 0) + gl;  // in [0, G-1]
-    L.sm[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, grp * 16, 0, kLoadNT);
+    const int left = G - g0[j];  // groups of the slot inside the row (may be <= 0)
+    const int bytes = (left > 0 ? left * 16 : 0) & valid;
+    L.sm[j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(sm + (size_t(t) * G + g0[j]), bytes), voff, 0,
+                                                    kLoadNT);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      const int rr = t * kTileRows + r < N ? r : N - 1 - t * kTileRows;  // row within the tile, clamped
-      L.code[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rc, (rr * G + grp) * 16, 0, kLoadNT);
+      const int n = t * kTileRows + r < N ? t * kTileRows + r : N - 1;
+      L.code[r][j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(codes + (size_t(n) * G + g0[j]), bytes),
+                                                           voff, 0, kLoadNT);
     }
   }
 }
@@ -132,6 +140,21 @@ __device__ __forceinline__ void fetch_tile_rsrc(const u32x4* __restrict__ codes,
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
   __builtin_amdgcn_s_barrier();
+}
+
+// Sum of the 32 binary16 activations of one group held as four 16-byte
+// chunks, in a fixed tree: each chunk's 8 values in one v_dot2 chain from 0,
+// then (c0 + c1) + (c2 + c3). Every path that needs a group sum forms it this
+// way (a wave holding the four chunks in four lanes adds them with two DPP
+// steps in the same order), so results do not depend on who formed it.
+__device__ __forceinline__ float chunk_sum(const u32x4& q) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s = dot2(elem(q, e), kOnes, s);
+  return s;
+}
+__device__ __forceinline__ float group_sum(const u32x4 (&q)[4]) {
+  return (chunk_sum(q[0]) + chunk_sum(q[1])) + (chunk_sum(q[2]) + chunk_sum(q[3]));
 }
 
 // This lane's slice x[m][32g .. 32g+31] of every activation row for the
@@ -155,19 +178,20 @@ __device__ __forceinline__ void load_x(const u32x4* __restrict__ x, int G, const
     }
   }
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
+  for (int m = 0; m < M; ++m)
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = dot2(elem(xv[m][j][q], e), kOnes, s);
-      }
-      xs[m][j] = s;
-    }
-  }
+    for (int j = 0; j < GPL; ++j) xs[m][j] = group_sum(xv[m][j]);
 }
+
+// Activations held in registers (the single-GEMV kernel): chunk d of the
+// lane's group j of row m, and that group's sum.
+template <int M, int GPL>
+struct RegX {
+  const u32x4 (&xv)[M][GPL][4];
+  const float (&xs)[M][GPL];
+  __device__ __forceinline__ u32x4 x(int m, int j, int d) const { return xv[m][j][d]; }
+  __device__ __forceinline__ float sum(int m, int j) const { return xs[m][j]; }
+};
 
 // Wave-wide partial row sums of one tile over this wave's groups:
 // acc[r][m] = sum over the wave's groups g of
@@ -176,20 +200,29 @@ __device__ __forceinline__ void load_x(const u32x4* __restrict__ x, int G, const
 // packed word AND 0x000F000F is a pair of halfs whose bit patterns are the
 // codes (values q * 2^-24), AND 0x00F000F0 gives q * 2^-20. Both are exact,
 // so are their products with x in fp32, and no offset is cancelled later.
-template <int M, int GPL>
-__device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const u32x4 (&xv)[M][GPL][4],
-                                             const float (&xs)[M][GPL], float (&acc)[kTileRows][M]) {
+// The activations come from an accessor (registers or LDS) chunk by chunk,
+// as they are used; the arithmetic per (row, activation row) is the same
+// sequence whatever the accessor.
+template <int M, int GPL, class XA>
+__device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
 #pragma unroll
-  for (int r = 0; r < kTileRows; ++r) {
+  for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 #pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      float lo[M], hi[M];
+  for (int j = 0; j < GPL; ++j) {
+    float lo[kTileRows][M], hi[kTileRows][M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.f;
+    for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u32x4 xq[M];  // x[m][8d .. 8d+7] of this group
+#pragma unroll
+      for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
         const uint32_t w = elem(L.code[r][j], d);
         const uint32_t w8 = w >> 8;
         const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
@@ -198,20 +231,22 @@ __device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const u32x
         const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          const u32x4& xq = xv[m][j][d];  // x[8d .. 8d+7] of this group
-          lo[m] = dot2(pa, elem(xq, 0), lo[m]);
-          hi[m] = dot2(pb, elem(xq, 1), hi[m]);
-          lo[m] = dot2(pc, elem(xq, 2), lo[m]);
-          hi[m] = dot2(pd, elem(xq, 3), hi[m]);
+          lo[r][m] = dot2(pa, elem(xq[m], 0), lo[r][m]);
+          hi[r][m] = dot2(pb, elem(xq[m], 1), hi[r][m]);
+          lo[r][m] = dot2(pc, elem(xq[m], 2), lo[r][m]);
+          hi[r][m] = dot2(pd, elem(xq[m], 3), hi[r][m]);
         }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
       const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
       const float sc = float(h[0]) * 0x1p20f;
       const float mn = float(h[1]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[m], 16.f, hi[m]), acc[r][m]);
-        acc[r][m] = __builtin_fmaf(mn, xs[m][j], acc[r][m]);
+        acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+        acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
       }
     }
   }

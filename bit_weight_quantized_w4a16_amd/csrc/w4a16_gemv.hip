@@ -113,7 +113,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
           TileLoads<GPL> la;
           fetch_tile<GPL>(codes, sm, N, G, b * tpb + tb, g0, lane, la);
           float acc[kTileRows][M];
-          compute_tile<M, GPL>(la, xv, xs, acc);
+          compute_tile<M, GPL>(la, RegX<M, GPL>{xv, xs}, acc);
           if (lane == 0) {
 #pragma unroll
             for (int r = 0; r < kTileRows; ++r)
@@ -147,7 +147,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
       const int t = tile_of(e);
       if (t < T) {
         float acc[kTileRows][M];
-        compute_tile<M, GPL>(L, xv, xs, acc);
+        compute_tile<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
         if constexpr (MODE == kDirect) {
           store_tile<M>(acc, y, N, t, lane);
         } else if (lane == 0) {

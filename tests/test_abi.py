@@ -149,11 +149,11 @@ def test_launch_shape_host_logic(w4a16_lib):
 def test_chain_launch_shape(w4a16_lib):
     for M in range(1, 9):
         s = w4.chain_launch_shape(M)
-        assert s["M"] == M and s["gpl"] in (1, 2) and 1 <= s["waves"] <= 16
-        assert s["kernel"] == f"chain_kernel<{M}, {s['gpl']}, {s['waves']}>"
+        assert s["M"] == M and s["gpl"] in (1, 2) and 1 <= s["ring"] <= 16
+        assert s["kernel"] == f"chain_kernel<{M}, {s['gpl']}, {s['ring']}>"
         plan = w4.w4a16_chain_plan([(0x7F0000000000, 0x7F0001000000, 0x7F0040000000, 64, 64)], M)
         hdr = plan[:64].view("<i4")
-        assert (hdr[4], hdr[5]) == (s["gpl"], s["waves"])   # the plan is made for that kernel
+        assert (hdr[4], hdr[5]) == (s["gpl"], s["ring"])    # the plan is made for that kernel
     for M in (0, 9):
         with pytest.raises(w4.W4A16Error):
             w4.chain_launch_shape(M)
@@ -168,7 +168,7 @@ def _plan_fields(plan, count):
     for i in range(count):
         raw = plan[64 + 64 * i: 128 + 64 * i]
         ptrs = raw[:32].view("<u8")
-        ints = raw[32:52].view("<i4")
+        ints = raw[32:56].view("<i4")
         ents.append((*[int(p) for p in ptrs], *[int(v) for v in ints]))
     return hdr, ents
 
@@ -176,23 +176,28 @@ def _plan_fields(plan, count):
 def test_chain_plan_layout(w4a16_lib):
     B = 0x7F0000000000
     entries = [
-        (B, B + 2**24, B + 2**30, 6144, 4096),            # K = 4096: one wave per tile
-        (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # four waves per tile
-        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # eight waves, one pass
+        (B, B + 2**24, B + 2**30, 6144, 4096),                    # one segment of 128 groups
+        (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # four segments
+        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # seven segments, one LDS pass
     ]
     plan = w4.w4a16_chain_plan(entries, 1)
     assert plan.size == w4.w4a16_chain_plan_bytes(3) == 64 + 3 * 64
     hdr, ents = _plan_fields(plan, 3)
-    assert hdr[0] == 0x48433457 and hdr[1] == 2 and hdr[2] == 3 and hdr[3] == 1 and hdr[5] == 8
+    shape = w4.chain_launch_shape(1)
+    assert (hdr[0], hdr[1], hdr[2], hdr[3]) == (0x48433457, 3, 3, 1)
+    assert (hdr[4], hdr[5]) == (shape["gpl"], shape["ring"]) == (2, 4)
     for (x, p, y, N, K), e in zip(entries, ents):
-        ex, ecodes, esm, ey, eN, eG, eT, wpr, passes = e
+        ex, ecodes, esm, ey, eN, eG, eT, S, passes, TB = e
         assert (ex, ecodes, ey, eN, eG, eT) == (x, p, y, N, K // 32, (N + 3) // 4)
         assert esm == p + (N * K // 2 + 255) // 256 * 256
-        assert wpr * 128 * passes >= K // 32             # M = 1 uses two groups per lane
-    assert [e[7:] for e in ents] == [(1, 1), (4, 1), (8, 1)]        # teams divide 8 waves
+        assert S * 128 >= K // 32 > (S - 1) * 128             # M = 1: segments of 64 lanes x 2 groups
+        assert TB * S * 4 * 4 <= 65536 < (TB + 1) * S * 4 * 4  # one block's partials fill the LDS stage
+    assert [e[7:] for e in ents] == [(1, 1, 4096), (4, 1, 1024), (7, 1, 585)]
     plan8 = w4.w4a16_chain_plan(entries[:2], 8)
-    _, e8 = _plan_fields(plan8, 2)
-    assert [e[7:] for e in e8] == [(2, 1), (2, 4)]       # M = 8: 128 groups of x per LDS pass
+    hdr8, e8 = _plan_fields(plan8, 2)
+    assert (hdr8[4], hdr8[5]) == (1, w4.chain_launch_shape(8)["ring"])
+    # M = 8: segments of 64 groups, 2 per 64 KiB pass of x, partials of 4 x 8 per segment
+    assert [e[7:] for e in e8] == [(2, 1, 256), (7, 4, 73)]
 
 
 def test_chain_plan_errors(w4a16_lib):
