@@ -256,24 +256,27 @@ LaunchShape shape_for_gpl(int M, int G, int gi) {
 }
 
 // Fewest passes over K; then avoid leaving more than a quarter of the lanes
-// idle; then the fewest waves per workgroup; then the fewest idle lanes.
+// idle; then, at M = 1, one group per lane (a tile's K split over more waves:
+// each wave loads less of x and more waves share the streaming; measured
+// faster on every decode-step shape); then the fewest waves per workgroup;
+// then the fewest idle lanes.
 LaunchShape choose_shape(int M, int G) {
   LaunchShape best{-1, 0, 0};
-  long best_key[4] = {0, 0, 0, 0};
+  long best_key[5] = {0, 0, 0, 0, 0};
   for (int gi = kNumGpl - 1; gi >= 0; --gi) {
     if (!gpl_allowed(M, kGplOptions[gi])) continue;
     const LaunchShape s = shape_for_gpl(M, G, gi);
     const long slots = long(s.nchunks) * s.waves * 64 * kGplOptions[gi];
     const long idle = slots - G;
-    const long key[4] = {s.nchunks, 4 * idle > slots ? 1 : 0, s.waves, idle};
+    const long key[5] = {s.nchunks, 4 * idle > slots ? 1 : 0, M == 1 ? kGplOptions[gi] : 0, s.waves, idle};
     bool better = best.gi < 0;
-    for (int i = 0; i < 4 && !better; ++i) {
+    for (int i = 0; i < 5 && !better; ++i) {
       if (key[i] < best_key[i]) better = true;
       if (key[i] > best_key[i]) break;
     }
     if (better) {
       best = s;
-      for (int i = 0; i < 4; ++i) best_key[i] = key[i];
+      for (int i = 0; i < 5; ++i) best_key[i] = key[i];
     }
   }
   return best;
@@ -351,7 +354,11 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   int occ = occupancy(M, shape.gi, mode, shape.waves, fn);
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
   const int max_grid = w4a16_host::cu_count(dev) * occ;
-  int tpb = direct ? 1 : T / max_grid;
+  // tiles per block: a workgroup reads its x slices once per block, so wide
+  // workgroups (long K split over four or more waves, a large x) take enough
+  // tiles per block for about one workgroup per CU; narrower ones fill the
+  // resident slots first
+  int tpb = direct ? 1 : shape.waves >= 4 ? T / w4a16_host::cu_count(dev) : T / max_grid;
   tpb = tpb < 1 ? 1 : tpb > kTilesPerBlock ? kTilesPerBlock : tpb;
   if (const int v = tune("W4A16_TUNE_TPB")) tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
   const int units = (T + tpb - 1) / tpb;

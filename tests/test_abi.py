@@ -142,8 +142,10 @@ def test_launch_shape_host_logic(w4a16_lib):
         shp(9, 5, 64)
     assert w4a16_lib.w4a16_launch_shape(1, 1, 64, None) == w4.W4A16_ERR_NULL
     # the kernel name carries the mode: one wave per tile / waves split K / passes over K
-    assert shp(1, 6144, 4096)["kernel"] == "gemv_kernel<1, 2, 0>"
-    assert shp(1, 4096, 14336)["kernel"] == "gemv_kernel<1, 2, 1>"
+    assert shp(1, 4096, 2048)["kernel"] == "gemv_kernel<1, 1, 0>"
+    assert shp(1, 6144, 4096)["kernel"] == "gemv_kernel<1, 1, 1>"
+    assert shp(1, 4096, 14336)["kernel"] == "gemv_kernel<1, 1, 1>"
+    assert shp(1, 64, 2**20)["kernel"].endswith(", 2>")
 
 
 def test_chain_launch_shape(w4a16_lib):

@@ -112,21 +112,27 @@ def test_chain_honours_read_after_write(w4a16_lib):
         assert_workspace_clean(ch)
 
 
-def test_chain_matches_separate_launches(w4a16_lib):
+@pytest.mark.parametrize("M", [1, 2])
+def test_chain_matches_separate_launches(w4a16_lib, M):
     shapes = [(6144, 4096), (4096, 4096), (2048, 14336), (1000, 4096)]
-    problems = [workload.random_problem(400 + i, 1, N, K, outliers=True) for i, (N, K) in enumerate(shapes)]
-    ch = Chain(problems, 1)
+    problems = [workload.random_problem(400 + i, M, N, K, outliers=True) for i, (N, K) in enumerate(shapes)]
+    ch = Chain(problems, M)
     ch.plan()
     ch.run()
     torch.cuda.synchronize()
-    for it in ch.items:
+    for it, (x, codes, scale, mn) in zip(ch.items, problems):
         y = torch.empty_like(it["y"])
         w4.w4a16_gemv(it["x"], it["packed"], y)
         torch.cuda.synchronize()
         a, b = it["y"].cpu().numpy(), y.cpu().numpy()
-        # K = 4096 (one wave per tile) and K = 14336 (four waves, one pass) use
-        # the same per-lane groups and reduction order in both paths
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"N={it['N']} K={it['K']}"
+        if M == 2:
+            # both split K into 64-group segments and add the segments' wave
+            # sums in order: the same bits
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"N={it['N']} K={it['K']}"
+        else:
+            # different segment widths: only the fp32 summation order differs
+            _, B = oracle.gemv(x, codes, scale, mn)
+            assert (np.abs(a.astype(np.float64) - b) <= 1e-5 * B + 1e-6).all(), f"N={it['N']} K={it['K']}"
 
 
 def test_chain_header_mismatch_writes_nothing(w4a16_lib):
