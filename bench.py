@@ -51,7 +51,12 @@ def gemv_bytes(M, N, K):
 # HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
 # only while the kernel is unchanged since the counters were taken.
-TRAFFIC = {}
+TRAFFIC = {
+    # (16,753.25 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    "gemv_kernel<1, 1, 1>": 34_363_904,
+    # (2,137,259.6 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
+    "chain_kernel<1, 2, 4>": 4_383_792_435,
+}
 
 
 def copy_calibration(torch, dev):
