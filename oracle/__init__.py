@@ -17,3 +17,4 @@ from .w4a16_ref import (  # noqa: F401
     unpack_codes,
     within_tolerance,
 )
+from . import codecs_ref  # noqa: F401,E402  (weight-code variants)

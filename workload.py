@@ -130,6 +130,48 @@ def gemv_inputs(name: str, layer: int, proj: int, M: int):
     return x, codes, scale, mn
 
 
+# Weight-code variants (see the codec definitions in the library header): the
+# canonical code array per codec is
+#   "q4", "q4_sym": uniform random bytes uint8[N, K/2] (two uniform 4-bit codes);
+#   "q5":           uniform integers 0..31, uint8[N, K] (one code per byte);
+#   "q8_sym":       uniform integers -128..127, int8[N, K].
+# Scale and min are the same draws as for the 4-bit code; the symmetric codecs
+# take no min (None). Codes of the variants use their own seed keys.
+CODECS = ("q4", "q4_sym", "q5", "q8_sym")
+
+
+def codec_weights(codec: str, wid: int, layer: int, proj: int, N: int, K: int):
+    """Seeded (codes, scale, min-or-None) of one matrix in a codec's canonical layout."""
+    if codec not in CODECS:
+        raise ValueError(f"unknown codec {codec!r}")
+    codes, scale, mn = weights(wid, layer, proj, N, K)
+    ci = CODECS.index(codec)
+    r = _rng(wid, layer, proj, _T_CODES + 8 * ci)
+    if codec == "q5":
+        codes = r.integers(0, 32, size=(N, K), dtype=np.uint8)
+    elif codec == "q8_sym":
+        codes = r.integers(-128, 128, size=(N, K), dtype=np.int8)
+    elif codec == "q4_sym":
+        codes = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    return codes, scale, (None if codec in ("q4_sym", "q8_sym") else mn)
+
+
+def codec_gemv_inputs(codec: str, name: str, layer: int, proj: int, M: int):
+    """Seeded (x, codes, scale, min-or-None) of one GEMV of a named workload in a codec."""
+    w = WORKLOADS[name]
+    p = w.shapes[proj]
+    codes, scale, mn = codec_weights(codec, w.wid, layer, proj, p.N, p.K)
+    x = activations(w.wid, layer, proj + 16 * M, M, p.K, w.outliers)
+    return x, codes, scale, mn
+
+
+def random_codec_problem(codec: str, seed: int, M: int, N: int, K: int, outliers: bool = False):
+    """Seeded codec inputs for an arbitrary (M, N, K), used by edge-shape tests."""
+    codes, scale, mn = codec_weights(codec, 1000 + seed, 0, 0, N, K)
+    x = activations(1000 + seed, 0, 0, M, K, outliers)
+    return x, codes, scale, mn
+
+
 def random_problem(seed: int, M: int, N: int, K: int, outliers: bool = False):
     """Seeded inputs for an arbitrary (M, N, K), used by edge-shape tests."""
     codes, scale, mn = weights(1000 + seed, 0, 0, N, K)
