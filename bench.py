@@ -52,8 +52,7 @@ def gemv_bytes(M, N, K):
 # and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
 # only while the kernel is unchanged since the counters were taken.
 TRAFFIC = {
-    # (16,753.25 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    "gemv_kernel<1, 1, 1>": 34_363_904,
+    # gemv_kernel<1, 1, 1>: not yet re-counted since its code last changed
     # (2,137,259.6 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
     "chain_kernel<1, 2, 4>": 4_383_792_435,
 }

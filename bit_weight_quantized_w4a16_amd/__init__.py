@@ -22,6 +22,10 @@ W4A16_ERR_ALIGN = 3
 W4A16_ERR_SIZE = 4
 W4A16_ERR_OVERLAP = 5
 W4A16_ERR_HIP = 6
+W4A16_ERR_FORMAT = 7
+
+# weight-code variants (enum w4a16_codec)
+CODEC_IDS = {"q4": 0, "q4_sym": 1, "q5": 2, "q8_sym": 3}
 
 # every symbol include/w4a16.h declares
 EXPORTS = (
@@ -38,6 +42,11 @@ EXPORTS = (
     "w4a16_gemv_chain_timed",
     "w4a16_gemv_chain",
     "w4a16_status_string",
+    "w4a16_codec_packed_bytes",
+    "w4a16_codec_pack",
+    "w4a16_codec_gemv",
+    "w4a16_codec_gemv_timed",
+    "w4a16_codec_launch_shape",
 )
 
 W4A16_CHAIN_WORKSPACE_BYTES = 69632
@@ -91,6 +100,16 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemv_chain_timed.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp, c_vp]
     L.w4a16_gemv_chain.restype = c_i32
     L.w4a16_gemv_chain.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp]
+    L.w4a16_codec_packed_bytes.restype = c_sz
+    L.w4a16_codec_packed_bytes.argtypes = [c_i32, c_i32, c_i32]
+    L.w4a16_codec_pack.restype = c_i32
+    L.w4a16_codec_pack.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_sz]
+    L.w4a16_codec_gemv.restype = c_i32
+    L.w4a16_codec_gemv.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp]
+    L.w4a16_codec_gemv_timed.restype = c_i32
+    L.w4a16_codec_gemv_timed.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+    L.w4a16_codec_launch_shape.restype = c_i32
+    L.w4a16_codec_launch_shape.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_status_string.argtypes = [c_i32]
     _lib = L
@@ -264,3 +283,103 @@ def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None) -> None:
                               workspace.numel() * workspace.element_size(), s)
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemv_chain")
+
+
+# ---------------------------------------------------------------------------
+# weight-code variants
+# ---------------------------------------------------------------------------
+
+
+def codec_id(codec) -> int:
+    """Codec name ("q4", "q4_sym", "q5", "q8_sym") or id -> the C enum value."""
+    if isinstance(codec, str):
+        if codec not in CODEC_IDS:
+            raise ValueError(f"unknown codec {codec!r}")
+        return CODEC_IDS[codec]
+    return int(codec)
+
+
+def w4a16_codec_packed_bytes(codec, N: int, K: int) -> int:
+    return int(lib().w4a16_codec_packed_bytes(codec_id(codec), int(N), int(K)))
+
+
+def w4a16_codec_pack(codec, codes: np.ndarray, scale: np.ndarray, mn: np.ndarray | None = None) -> np.ndarray:
+    """Host repack of one codec's canonical arrays into a uint8 blob.
+
+    codes: uint8[N, K/2] for the 4-bit codecs, uint8[N, K] (values < 32) for
+    "q5", int8[N, K] for "q8_sym"; scale (and min, affine codecs only)
+    float16[N, K/32].
+    """
+    cid = codec_id(codec)
+    codes = np.ascontiguousarray(codes)
+    if codes.dtype not in (np.uint8, np.int8):
+        raise TypeError("codes must be uint8 or int8")
+    N = codes.shape[0]
+    K = codes.shape[1] * (2 if cid in (0, 1) else 1)
+    scale = np.ascontiguousarray(scale, dtype=np.float16)
+    if scale.shape != (N, K // 32):
+        raise ValueError("scale must be [N, K/32]")
+    mp = None
+    if mn is not None:
+        mn = np.ascontiguousarray(mn, dtype=np.float16)
+        if mn.shape != (N, K // 32):
+            raise ValueError("min must be [N, K/32]")
+        mp = mn.ctypes.data
+    nbytes = w4a16_codec_packed_bytes(cid, N, K)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    st = lib().w4a16_codec_pack(cid, codes.ctypes.data, scale.ctypes.data, mp, N, K, out.ctypes.data, out.nbytes)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_codec_pack")
+    return out
+
+
+def w4a16_codec_launch_shape(codec, M: int, N: int, K: int) -> dict:
+    """(groups per lane, waves, passes over K) and the kernel name w4a16_codec_gemv would use."""
+    cid = codec_id(codec)
+    out = (ctypes.c_int32 * 3)()
+    st = lib().w4a16_codec_launch_shape(cid, M, N, K, out)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_codec_launch_shape")
+    mode = 2 if out[2] > 1 else 1 if out[1] > 1 else 0
+    name = (f"gemv_kernel<{M}, {out[0]}, {mode}>" if cid == 0 else f"codec_kernel<{cid}, {M}, {out[0]}, {mode}>")
+    return {"groups_per_lane": out[0], "waves": out[1], "k_passes": out[2], "kernel": name}
+
+
+def w4a16_codec_gemv_raw(codec, x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int,
+                         stream: int = 0) -> int:
+    """Direct C call with raw pointers; returns the status code."""
+    return int(lib().w4a16_codec_gemv(codec_id(codec), x_ptr, packed_ptr, y_ptr, M, N, K, stream))
+
+
+def w4a16_codec_gemv_timed_raw(codec, x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int,
+                               stream: int, start_event: int, stop_event: int) -> int:
+    """w4a16_codec_gemv_timed with raw pointers and hipEvent_t handles; returns the status code."""
+    return int(lib().w4a16_codec_gemv_timed(codec_id(codec), x_ptr, packed_ptr, y_ptr, M, N, K, stream,
+                                            start_event, stop_event))
+
+
+def w4a16_codec_gemv(codec, x, packed, y, stream=None) -> None:
+    """y[M, N] = x[M, K] @ w_hat.T for a blob from w4a16_codec_pack (device tensors)."""
+    if str(x.dtype) != "torch.float16" or str(y.dtype) != "torch.float32":
+        raise TypeError("x must be float16 and y float32")
+    if x.dim() != 2 or y.dim() != 2 or int(y.shape[0]) != int(x.shape[0]):
+        raise ValueError("x must be [M, K] and y [M, N]")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and y must be contiguous")
+    M, K, N = int(x.shape[0]), int(x.shape[1]), int(y.shape[1])
+    need = w4a16_codec_packed_bytes(codec, N, K)
+    if need == 0:
+        raise W4A16Error(W4A16_ERR_SHAPE, "w4a16_codec_gemv")
+    if packed.numel() * packed.element_size() < need:
+        raise ValueError(f"packed blob has {packed.numel() * packed.element_size()} bytes, needs {need}")
+    if stream is None:
+        import torch
+
+        s = torch.cuda.current_stream(x.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        s = stream.cuda_stream
+    else:
+        s = int(stream)
+    st = w4a16_codec_gemv_raw(codec, _ptr(x), _ptr(packed), _ptr(y), M, N, K, s)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_codec_gemv")

@@ -33,166 +33,24 @@
 #include "w4a16.h"
 #include "w4a16_device.h"
 #include "w4a16_host.h"
+#include "w4a16_skeleton.h"
 
 using namespace w4a16_dev;
 
 namespace {
 
-// Waves per workgroup an instantiation may use: its VGPR estimate (x slice,
-// tile loads in flight, accumulators) must fit the 512-entry register file
-// shared by the waves on one SIMD.
-__host__ __device__ constexpr int max_waves(int M, int GPL) {
-  return (16 * M * GPL + (double_buffered(M) ? 40 : 20) * GPL + 6 * M + 30) <= 128 ? 16 : 8;
-}
+using w4a16_host::LaunchShape;
+using w4a16_host::gpl_allowed;
+using w4a16_host::kGplOptions;
+using w4a16_host::kNumGpl;
 
-// Launch modes of one GEMV.
-//   kDirect: one wave covers all of K for its tile and stores the results;
-//   kBlock:  the waves of a workgroup split K; per-wave partials of a block
-//            of tiles are combined through LDS;
-//   kMulti:  K also takes several passes of the workgroup (x re-fetched per
-//            pass, partials carried in LDS).
-constexpr int kDirect = 0, kBlock = 1, kMulti = 2;
-
+// The 4-bit group-affine GEMV: the shared skeleton with the device header's
+// tile loads and dot products.
 template <int M, int GPL, int MODE>
-__global__ void __launch_bounds__(64 * max_waves(M, GPL))
+__global__ void __launch_bounds__(64 * max_waves_of<CodecQ4>(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
             float* __restrict__ y, int N, int G, int T, int nchunks, int tpb) {
-  const int lane = threadIdx.x & 63;
-  // wave-uniform values kept in scalar registers, so every load address is a
-  // scalar base plus the one per-lane offset `lane`
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
-  const int nblocks = (T + tpb - 1) / tpb;
-  if (int(blockIdx.x) >= nblocks) return;
-
-  auto bases = [&](int c, int (&g0)[GPL]) {
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) g0[j] = c * chunk_groups + (wave * GPL + j) * 64;
-  };
-
-  u32x4 xv[M][GPL][4];
-  float xs[M][GPL];
-  auto fetch_x = [&](int c) {
-    int g0[GPL];
-    bases(c, g0);
-    load_x<M, GPL>(x, G, g0, lane, xv, xs);
-  };
-
-  // per-wave partials of one block of tiles: [tile][row][m][wave]
-  __shared__ float part[MODE == kDirect ? 1 : kTilesPerBlock][kTileRows][M][MODE == kDirect ? 1 : kMaxWaves];
-
-  // combine the waves' partials of block b (all passes done) and store
-  auto reduce_block = [&](int b) {
-    __syncthreads();
-    const int ntiles = min(tpb, T - b * tpb);
-    for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
-      const int ti = i / (kTileRows * M);
-      const int r = (i / M) % kTileRows;
-      const int m = i % M;
-      const int n = (b * tpb + ti) * kTileRows + r;
-      if (n < N) {
-        float s = 0.f;
-        for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
-        y[size_t(m) * N + n] = s;
-      }
-    }
-    __syncthreads();
-  };
-
-  if constexpr (MODE == kMulti) {
-    // passes over K outermost within a block: x of pass c is fetched once at
-    // the top of the pass and stays in registers for the block's tiles
-    for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
-      const int ntiles = min(tpb, T - b * tpb);
-      for (int c = 0; c < nchunks; ++c) {
-        fetch_x(c);
-        int g0[GPL];
-        bases(c, g0);
-        for (int tb = 0; tb < ntiles; ++tb) {
-          TileLoads<GPL> la;
-          fetch_tile<GPL>(codes, sm, N, G, b * tpb + tb, g0, lane, la);
-          float acc[kTileRows][M];
-          compute_tile<M, GPL>(la, RegX<M, GPL>{xv, xs}, acc);
-          if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-              for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + acc[r][m];
-          }
-        }
-      }
-      reduce_block(b);
-    }
-    return;
-  } else {
-    // Items e = 0 .. n_items-1 of this workgroup: tile tb = e % tpb of its
-    // (e / tpb)-th block. The item count is known up front and the loop's
-    // only exit is its condition, so every fetch inside the loop is
-    // unconditional (a fetch that might not happen would make the compiler
-    // merge buffer contents with register moves that wait for the loads in
-    // flight); tiles past T (in the matrix's last block only) fetch a clamped
-    // tile and are skipped. A scheduling barrier after each fetch keeps the
-    // next tile's loads ahead of the current tile's compute.
-    const int my_blocks = (nblocks - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
-    const int n_items = my_blocks * tpb;
-    int g0[GPL];
-    bases(0, g0);
-    auto tile_of = [&](int e) { return (int(blockIdx.x) + (e / tpb) * int(gridDim.x)) * tpb + e % tpb; };
-    auto fetch = [&](int e, TileLoads<GPL>& L) {
-      const int t = tile_of(e);
-      fetch_tile<GPL>(codes, sm, N, G, t < T ? t : T - 1, g0, lane, L);
-    };
-    auto finish = [&](const TileLoads<GPL>& L, int e) {
-      const int t = tile_of(e);
-      if (t < T) {
-        float acc[kTileRows][M];
-        compute_tile<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
-        if constexpr (MODE == kDirect) {
-          store_tile<M>(acc, y, N, t, lane);
-        } else if (lane == 0) {
-          const int tb = e % tpb;
-#pragma unroll
-          for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) part[tb][r][m][wave] = acc[r][m];
-        }
-      }
-      if constexpr (MODE == kBlock) {
-        if (e % tpb == tpb - 1) reduce_block(int(blockIdx.x) + (e / tpb) * int(gridDim.x));
-      }
-    };
-
-    TileLoads<GPL> la, lb;
-    fetch(0, la);
-    fetch_x(0);  // after the first tile's loads, so both latencies overlap
-    int e = 0;
-    if constexpr (double_buffered(M)) {
-      while (e + 2 < n_items) {
-        fetch(e + 1, lb);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(la, e);
-        fetch(e + 2, la);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(lb, e + 1);
-        e += 2;
-      }
-      if (n_items - e == 2) {
-        fetch(e + 1, lb);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(la, e);
-        finish(lb, e + 1);
-      } else {
-        finish(la, e);
-      }
-    } else {
-      finish(la, 0);
-      for (e = 1; e < n_items; ++e) {
-        fetch(e, la);
-        finish(la, e);
-      }
-    }
-  }
+  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,12 +59,7 @@ gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const 
 
 typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, float*, int, int, int, int, int);
 
-constexpr int kGplOptions[] = {1, 2, 4};
-constexpr int kNumGpl = 3;
 constexpr int32_t kMaxK = 1 << 20;
-
-// the x slice of one lane stays within 32 VGPRs (one group per lane always allowed)
-constexpr bool gpl_allowed(int M, int gpl) { return 16 * M * gpl <= 32 || gpl == 1; }
 
 template <int M, int GPL, int MODE>
 constexpr kernel_fn instance() {
@@ -234,52 +87,9 @@ kernel_fn kernel_for(int M, int gi) {
   }
 }
 
-int mode_of(int waves, int nchunks) { return nchunks > 1 ? kMulti : waves > 1 ? kBlock : kDirect; }
-
 kernel_fn kernel_for_mode(int mode, int M, int gi) {
   return mode == kMulti ? kernel_for<kMulti>(M, gi) : mode == kBlock ? kernel_for<kBlock>(M, gi)
                                                                       : kernel_for<kDirect>(M, gi);
-}
-
-struct LaunchShape {
-  int gi;       // index into kGplOptions
-  int waves;    // waves per workgroup
-  int nchunks;  // passes over K
-};
-
-LaunchShape shape_for_gpl(int M, int G, int gi) {
-  const int gpl = kGplOptions[gi];
-  const int wmax = max_waves(M, gpl);
-  const int nchunks = (G + wmax * 64 * gpl - 1) / (wmax * 64 * gpl);
-  const int waves = (G + nchunks * 64 * gpl - 1) / (nchunks * 64 * gpl);
-  return LaunchShape{gi, waves, nchunks};
-}
-
-// Fewest passes over K; then avoid leaving more than a quarter of the lanes
-// idle; then, at M = 1, one group per lane (a tile's K split over more waves:
-// each wave loads less of x and more waves share the streaming; measured
-// faster on every decode-step shape); then the fewest waves per workgroup;
-// then the fewest idle lanes.
-LaunchShape choose_shape(int M, int G) {
-  LaunchShape best{-1, 0, 0};
-  long best_key[5] = {0, 0, 0, 0, 0};
-  for (int gi = kNumGpl - 1; gi >= 0; --gi) {
-    if (!gpl_allowed(M, kGplOptions[gi])) continue;
-    const LaunchShape s = shape_for_gpl(M, G, gi);
-    const long slots = long(s.nchunks) * s.waves * 64 * kGplOptions[gi];
-    const long idle = slots - G;
-    const long key[5] = {s.nchunks, 4 * idle > slots ? 1 : 0, M == 1 ? kGplOptions[gi] : 0, s.waves, idle};
-    bool better = best.gi < 0;
-    for (int i = 0; i < 5 && !better; ++i) {
-      if (key[i] < best_key[i]) better = true;
-      if (key[i] > best_key[i]) break;
-    }
-    if (better) {
-      best = s;
-      for (int i = 0; i < 5; ++i) best_key[i] = key[i];
-    }
-  }
-  return best;
 }
 
 // Resident workgroups per CU of one instantiation at one block size (cached;
@@ -308,7 +118,7 @@ extern "C" w4a16_status w4a16_launch_shape(int32_t M, int32_t N, int32_t K, int3
   if (M < 1 || M > kMaxM || N < 1 || K < kGroup || K % kGroup || K > w4a16_max_k(M) ||
       w4a16_packed_bytes(N, K) == 0)
     return W4A16_ERR_SHAPE;
-  const LaunchShape shape = choose_shape(M, K / kGroup);
+  const LaunchShape shape = w4a16_host::choose_shape<CodecQ4>(M, K / kGroup);
   if (shape.gi < 0) return W4A16_ERR_SHAPE;
   out[0] = kGplOptions[shape.gi];
   out[1] = shape.waves;
@@ -337,13 +147,13 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
     return W4A16_ERR_OVERLAP;
 
   const int G = K / kGroup;
-  LaunchShape shape = choose_shape(M, G);
+  LaunchShape shape = w4a16_host::choose_shape<CodecQ4>(M, G);
   if (const int g = tune("W4A16_TUNE_GPL")) {  // sweep builds only
     for (int gi = 0; gi < kNumGpl; ++gi)
-      if (kGplOptions[gi] == g && gpl_allowed(M, g)) shape = shape_for_gpl(M, G, gi);
+      if (kGplOptions[gi] == g && gpl_allowed(M, g)) shape = w4a16_host::shape_for_gpl<CodecQ4>(M, G, gi);
   }
   if (shape.gi < 0) return W4A16_ERR_SHAPE;
-  const int mode = mode_of(shape.waves, shape.nchunks);
+  const int mode = w4a16_host::mode_of(shape.waves, shape.nchunks);
   kernel_fn fn = kernel_for_mode(mode, M, shape.gi);
 
   int dev = 0;
@@ -353,16 +163,13 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   // all workgroups resident at once, each walking an equal share of the tiles
   int occ = occupancy(M, shape.gi, mode, shape.waves, fn);
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
-  const int max_grid = w4a16_host::cu_count(dev) * occ;
-  // tiles per block: a workgroup reads its x slices once per block, so wide
-  // workgroups (long K split over four or more waves, a large x) take enough
-  // tiles per block for about one workgroup per CU; narrower ones fill the
-  // resident slots first
-  int tpb = direct ? 1 : shape.waves >= 4 ? T / w4a16_host::cu_count(dev) : T / max_grid;
-  tpb = tpb < 1 ? 1 : tpb > kTilesPerBlock ? kTilesPerBlock : tpb;
-  if (const int v = tune("W4A16_TUNE_TPB")) tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
-  const int units = (T + tpb - 1) / tpb;
-  const int grid = units < max_grid ? units : max_grid;
+  int tpb = 0, grid = 0;
+  w4a16_host::grid_of(T, shape.waves, direct, w4a16_host::cu_count(dev), occ, tpb, grid);
+  if (const int v = tune("W4A16_TUNE_TPB")) {  // sweep builds only
+    tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
+    const int units = (T + tpb - 1) / tpb, max_grid = w4a16_host::cu_count(dev) * occ;
+    grid = units < max_grid ? units : max_grid;
+  }
 
   const size_t codes_region = (size_t(N) * size_t(K) / 2 + 255) / 256 * 256;
   const u32x4* xp = static_cast<const u32x4*>(x);

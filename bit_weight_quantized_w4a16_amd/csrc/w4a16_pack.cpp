@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "w4a16.h"
+#include "w4a16_codec_internal.h"
 
 namespace {
 
@@ -115,7 +116,148 @@ extern "C" w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, 
   return W4A16_OK;
 }
 
-extern "C" int32_t w4a16_abi_version(void) { return 1; }
+// ---------------------------------------------------------------------------
+// Weight-code variants (formats in include/w4a16.h)
+// ---------------------------------------------------------------------------
+
+namespace w4a16_codecs {
+
+bool regions(int codec, int32_t N, int32_t K, Regions& r) {
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return false;
+  if (N < 1 || K < kGroup || K % kGroup) return false;
+  const int64_t G = K / kGroup;
+  if (int64_t(N) * G > INT32_MAX) return false;
+  const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
+  const int64_t code_bytes = int64_t(N) * G * (codec == W4A16_CODEC_Q8_SYM ? 32 : 16);
+  const int64_t S = (code_bytes + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+  const int64_t side_entry = (codec == W4A16_CODEC_Q4_SYM || codec == W4A16_CODEC_Q8_SYM) ? 8 : 16;
+  r.codes = size_t(code_bytes);
+  r.aux = codec == W4A16_CODEC_Q5 ? size_t(S) : 0;
+  r.side = size_t(S + (codec == W4A16_CODEC_Q5 ? T * G * 16 : 0));
+  r.total = r.side + size_t(T * G * side_entry);
+  return true;
+}
+
+}  // namespace w4a16_codecs
+
+namespace {
+
+// Bit b = 4j + d of a row's fifth-bit word of a group holds k = 8d + 2(j mod 4) + j/4.
+constexpr int fifth_bit_k(int b) { return 8 * (b % 4) + 2 * ((b / 4) % 4) + (b / 4) / 4; }
+
+// The four binary16 numbers of rows 4t..4t+3 for group g (zero past N).
+void tile_halves(const uint16_t* v, int64_t N, int64_t G, int64_t t, int64_t g, uint16_t (&e)[4]) {
+  for (int64_t r = 0; r < kTileRows; ++r) {
+    const int64_t n = t * kTileRows + r;
+    e[r] = n < N ? v[n * G + g] : 0;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t w4a16_codec_packed_bytes(int32_t codec, int32_t N, int32_t K) {
+  w4a16_codecs::Regions r;
+  return w4a16_codecs::regions(codec, N, K, r) ? r.total : 0;
+}
+
+extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, const uint16_t* scale,
+                                         const uint16_t* min, int32_t N, int32_t K, void* out, size_t out_bytes) {
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return W4A16_ERR_FORMAT;
+  if (codec == W4A16_CODEC_Q4) return w4a16_pack(codes, scale, min, N, K, out, out_bytes);
+  const bool affine = codec == W4A16_CODEC_Q5;
+  if (!codes || !scale || (affine && !min) || !out) return W4A16_ERR_NULL;
+  w4a16_codecs::Regions reg;
+  if (!w4a16_codecs::regions(codec, N, K, reg)) return W4A16_ERR_SHAPE;
+  if (out_bytes < reg.total) return W4A16_ERR_SIZE;
+  const int64_t G = K / kGroup;
+  const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
+  if (codec == W4A16_CODEC_Q5) {  // every code must fit 5 bits; checked before anything is written
+    const int64_t total = int64_t(N) * K;
+    for (int64_t i = 0; i < total; ++i)
+      if (codes[i] > 31) return W4A16_ERR_FORMAT;
+  }
+  uint8_t* o = static_cast<uint8_t*>(out);
+  std::memset(o + reg.codes, 0, reg.total - reg.codes);  // padding and tiles past N
+
+  // code chunks
+  parallel_rows(N, K, [&](int64_t r0, int64_t r1) {
+    for (int64_t n = r0; n < r1; ++n) {
+      if (codec == W4A16_CODEC_Q4_SYM) {  // the 4-bit code's chunk layout
+        const uint8_t* src = codes + n * (K / 2);
+        uint8_t* dst = o + n * (K / 2);
+        for (int64_t b = 0; b < K / 2; b += 4) {
+          uint32_t v;
+          std::memcpy(&v, src + b, 4);
+          v = split_even_odd(v);
+          std::memcpy(dst + b, &v, 4);
+        }
+      } else if (codec == W4A16_CODEC_Q5) {  // low nibbles in the 4-bit layout
+        const uint8_t* src = codes + n * int64_t(K);
+        uint8_t* dst = o + n * (K / 2);
+        for (int64_t k = 0; k < K; k += 8) {
+          uint32_t v = 0;
+          for (int i = 0; i < 4; ++i)
+            v |= uint32_t((src[k + 2 * i] & 0xF) | ((src[k + 2 * i + 1] & 0xF) << 4)) << (8 * i);
+          v = split_even_odd(v);
+          std::memcpy(dst + k / 2, &v, 4);
+        }
+      } else {  // 8-bit: offset-binary bytes, low halves then high halves of every group
+        const uint8_t* src = codes + n * int64_t(K);
+        uint8_t* row = o + n * G * 32;
+        static constexpr int kSlotOf[4] = {0, 2, 1, 3};  // byte slot of i = 0..3 in a word
+        for (int64_t g = 0; g < G; ++g)
+          for (int h = 0; h < 2; ++h) {
+            uint8_t* dst = row + (h * G + g) * 16;
+            for (int e = 0; e < 4; ++e)
+              for (int i = 0; i < 4; ++i)
+                dst[4 * e + kSlotOf[i]] = uint8_t(src[32 * g + 16 * h + 4 * e + i] ^ 0x80u);
+          }
+      }
+    }
+  });
+
+  // fifth-bit tiles (5-bit code)
+  if (codec == W4A16_CODEC_Q5) {
+    uint8_t* hb = o + reg.aux;
+    parallel_rows(T, G * 128, [&](int64_t t0, int64_t t1) {
+      for (int64_t t = t0; t < t1; ++t)
+        for (int64_t g = 0; g < G; ++g) {
+          uint32_t e[4] = {0, 0, 0, 0};
+          for (int64_t r = 0; r < kTileRows; ++r) {
+            const int64_t n = t * kTileRows + r;
+            if (n >= N) continue;
+            const uint8_t* q = codes + n * int64_t(K) + 32 * g;
+            for (int b = 0; b < 32; ++b) e[r] |= uint32_t((q[fifth_bit_k(b)] >> 4) & 1u) << b;
+          }
+          std::memcpy(hb + (t * G + g) * 16, e, 16);
+        }
+    });
+  }
+
+  // scale (and min) tiles
+  uint8_t* side = o + reg.side;
+  parallel_rows(T, G * 16, [&](int64_t t0, int64_t t1) {
+    for (int64_t t = t0; t < t1; ++t)
+      for (int64_t g = 0; g < G; ++g) {
+        uint16_t s4[4], m4[4] = {0, 0, 0, 0};
+        tile_halves(scale, N, G, t, g, s4);
+        if (affine) {
+          tile_halves(min, N, G, t, g, m4);
+          uint16_t e[8];
+          for (int r = 0; r < 4; ++r) {
+            e[2 * r] = s4[r];
+            e[2 * r + 1] = m4[r];
+          }
+          std::memcpy(side + (t * G + g) * 16, e, 16);
+        } else {
+          std::memcpy(side + (t * G + g) * 8, s4, 8);
+        }
+      }
+  });
+  return W4A16_OK;
+}
+
+extern "C" int32_t w4a16_abi_version(void) { return 2; }
 
 extern "C" const char* w4a16_status_string(int32_t status) {
   switch (status) {
@@ -126,6 +268,7 @@ extern "C" const char* w4a16_status_string(int32_t status) {
     case W4A16_ERR_SIZE: return "output buffer smaller than required";
     case W4A16_ERR_OVERLAP: return "y overlaps x or the packed weights";
     case W4A16_ERR_HIP: return "the HIP runtime reported an error";
+    case W4A16_ERR_FORMAT: return "unknown codec, or a code outside its codec's range";
     default: return "unknown status";
   }
 }

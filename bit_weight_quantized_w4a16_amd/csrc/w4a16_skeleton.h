@@ -1,0 +1,560 @@
+// The single-GEMV kernel skeleton, shared by every weight code, and the
+// host-side choice of its launch shape. Internal header of libw4a16.
+//
+// The skeleton streams 4-row tiles of a weight matrix: a lane owns GPL groups
+// of 32 k along K and keeps that slice of every activation row in registers,
+// the W waves of a workgroup cover W*64*GPL groups per pass over K, each
+// tile's loads are issued before the previous tile is computed, lane partials
+// are summed across the wave without LDS and across waves through LDS in a
+// fixed order. What differs between weight codes is only how one tile is
+// loaded and how its codes become dot products; a codec policy supplies
+// those two steps:
+//
+//   template <int GPL> struct Loads;   // one lane's loads of one tile
+//   template <int GPL> static void fetch(const WeightPtrs&, int N, int G, int t,
+//                                        const int (&g0)[GPL], int lane, Loads<GPL>&);
+//   template <int M, int GPL, class XA> static void compute(const Loads<GPL>&, const XA&,
+//                                                           float (&acc)[kTileRows][M]);
+//   static constexpr int kTileVgprs;    // VGPRs of one group slot's loads
+//
+// compute() returns wave-wide sums (every lane holds them).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "w4a16_device.h"
+
+namespace w4a16_dev {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Launch modes of one GEMV.
+//   kDirect: one wave covers all of K for its tile and stores the results;
+//   kBlock:  the waves of a workgroup split K; per-wave partials of a block
+//            of tiles are combined through LDS;
+//   kMulti:  K also takes several passes of the workgroup (x re-fetched per
+//            pass, partials carried in LDS).
+constexpr int kDirect = 0, kBlock = 1, kMulti = 2;
+
+// Regions of one packed blob, in the units the loads use.
+struct WeightPtrs {
+  const u32x4* codes;  // code chunks
+  const u32x4* aux;    // extra per-tile entries (the 5-bit code's fifth-bit plane), else null
+  const void* side;    // per-tile scale (and min) entries
+};
+
+// Lane-clamped group slot: the lane reads group g0 + base + gl. A lane past G
+// reads group G-1 instead (its activations are zero, so it adds exactly 0), a
+// slot entirely past G is pulled back to G-1. Every load stays unconditional.
+struct Slot {
+  int base, gl;
+};
+__device__ __forceinline__ Slot slot_of(int G, int g0, int lane) {
+  const int last = G - 1 - g0;  // wave-uniform; < 0 when the whole slot is past G
+  return Slot{last < 0 ? G - 1 - g0 : 0, lane < last ? lane : (last > 0 ? last : 0)};
+}
+__device__ __forceinline__ int clamp_row(int t, int r, int N) {
+  return t * kTileRows + r < N ? t * kTileRows + r : N - 1;
+}
+
+// binary16 number h of a 4-row entry of 8 bytes (row r in bytes 2r..2r+1)
+__device__ __forceinline__ float half_of(const u32x2& v, int r) {
+  const uint32_t w = r < 2 ? v.x : v.y;
+  const uint16_t b = uint16_t((r & 1) ? (w >> 16) : (w & 0xFFFFu));
+  return float(__builtin_bit_cast(_Float16, b));
+}
+
+// ---------------------------------------------------------------------------
+// Codec policies
+// ---------------------------------------------------------------------------
+
+// 4-bit group-affine code (w_hat = s*q + m): the tile loads and dot products
+// of the device header, unchanged.
+struct CodecQ4 {
+  static constexpr int kTileVgprs = 20;
+  template <int GPL>
+  using Loads = TileLoads<GPL>;
+  template <int GPL>
+  __device__ __forceinline__ static void fetch(const WeightPtrs& w, int N, int G, int t, const int (&g0)[GPL],
+                                               int lane, Loads<GPL>& L) {
+    fetch_tile<GPL>(w.codes, static_cast<const u32x4*>(w.side), N, G, t, g0, lane, L);
+  }
+  template <int M, int GPL, class XA>
+  __device__ __forceinline__ static void compute(const Loads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
+    compute_tile<M, GPL>(L, xa, acc);
+  }
+};
+
+// The four nibble pairs of one 32-bit code word against one 16-byte chunk of
+// x (as in compute_tile): lo gathers q * 2^-24 terms, hi gathers q * 2^-20.
+// `five` adds a fifth code bit below each nibble's plane (0 for 4-bit codes):
+// bits 4/20 of fa and 8/24 of fa for the first two pairs, of fb for the last
+// two, already shifted into place by the caller.
+template <int M, bool FIVE>
+__device__ __forceinline__ void nibble_dots(uint32_t w, uint32_t fa, uint32_t fb, const u32x4 (&xq)[M],
+                                            float (&lo)[M], float (&hi)[M]) {
+  const uint32_t w8 = w >> 8;
+  uint32_t pa = w & 0x000F000Fu, pb = w & 0x00F000F0u, pc = w8 & 0x000F000Fu, pd = w8 & 0x00F000F0u;
+  if constexpr (FIVE) {
+    pa |= fa & 0x00100010u;
+    pb |= fa & 0x01000100u;
+    pc |= fb & 0x00100010u;
+    pd |= fb & 0x01000100u;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    lo[m] = dot2(pa, elem(xq[m], 0), lo[m]);
+    hi[m] = dot2(pb, elem(xq[m], 1), hi[m]);
+    lo[m] = dot2(pc, elem(xq[m], 2), lo[m]);
+    hi[m] = dot2(pd, elem(xq[m], 3), hi[m]);
+  }
+}
+
+// Symmetric 4-bit code (w_hat = s*(q - 8)): the 4-bit code chunks, and one
+// 8-byte entry of four binary16 scales per (tile, group).
+struct CodecQ4Sym {
+  static constexpr int kTileVgprs = 18;
+  template <int GPL>
+  struct Loads {
+    u32x2 sc[GPL];
+    u32x4 code[kTileRows][GPL];
+  };
+  template <int GPL>
+  __device__ __forceinline__ static void fetch(const WeightPtrs& w, int N, int G, int t, const int (&g0)[GPL],
+                                               int lane, Loads<GPL>& L) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const Slot s = slot_of(G, g0[j], lane);
+      const u32x2* sp = static_cast<const u32x2*>(w.side) + (size_t(t) * G + g0[j] + s.base);
+      L.sc[j] = __builtin_nontemporal_load(sp + s.gl);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+        L.code[r][j] = __builtin_nontemporal_load(w.codes + (size_t(clamp_row(t, r, N)) * G + g0[j] + s.base) + s.gl);
+    }
+  }
+  template <int M, int GPL, class XA>
+  __device__ __forceinline__ static void compute(const Loads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float lo[kTileRows][M], hi[kTileRows][M];
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u32x4 xq[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) nibble_dots<M, false>(elem(L.code[r][j], d), 0u, 0u, xq, lo[r], hi[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const float s = half_of(L.sc[j], r);
+        const float sc = s * 0x1p20f;
+        const float mn = -8.f * s;  // exact
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  }
+};
+
+// 5-bit group-affine code (w_hat = s*q + m, q = nibble + 16 * fifth bit): the
+// low nibbles in 4-bit code chunks, one 16-byte entry of four 32-bit
+// fifth-bit words per (tile, group), and the 4-bit code's scale/min entries.
+// Bit 4j + d of a row's fifth-bit word belongs to k = 8d + 2(j mod 4) + j/4
+// of the group, so for chunk word d the word shifted left by 4 - d has the
+// bits of its first two nibble pairs at 4/20 and 8/24, and shifted right by
+// 4 + d those of the last two.
+struct CodecQ5 {
+  static constexpr int kTileVgprs = 24;
+  template <int GPL>
+  struct Loads {
+    u32x4 sm[GPL];
+    u32x4 hb[GPL];
+    u32x4 code[kTileRows][GPL];
+  };
+  template <int GPL>
+  __device__ __forceinline__ static void fetch(const WeightPtrs& w, int N, int G, int t, const int (&g0)[GPL],
+                                               int lane, Loads<GPL>& L) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const Slot s = slot_of(G, g0[j], lane);
+      const size_t e = size_t(t) * G + g0[j] + s.base;
+      L.sm[j] = __builtin_nontemporal_load(static_cast<const u32x4*>(w.side) + e + s.gl);
+      L.hb[j] = __builtin_nontemporal_load(w.aux + e + s.gl);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+        L.code[r][j] = __builtin_nontemporal_load(w.codes + (size_t(clamp_row(t, r, N)) * G + g0[j] + s.base) + s.gl);
+    }
+  }
+  template <int M, int GPL, class XA>
+  __device__ __forceinline__ static void compute(const Loads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float lo[kTileRows][M], hi[kTileRows][M];
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u32x4 xq[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) {
+          const uint32_t h = elem(L.hb[j], r);
+          nibble_dots<M, true>(elem(L.code[r][j], d), h << (4 - d), h >> (4 + d), xq, lo[r], hi[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const f16x2 hm = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
+        const float sc = float(hm[0]) * 0x1p20f;
+        const float mn = float(hm[1]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  }
+};
+
+// Symmetric 8-bit code (w_hat = s*q, q signed): offset-binary bytes u = q + 128,
+// each row's group halves in two runs of 16-byte chunks (all low halves, then
+// all high halves, so each load instruction reads 1 KiB contiguously), and
+// the symmetric 4-bit code's 8-byte scale entries. In a code word the bytes
+// hold k = 4e + (0, 2, 1, 3): AND 0x00FF00FF gives the pair (k, k+1) as
+// binary16 subnormals u * 2^-24, the word shifted right by 8 the pair
+// (k+2, k+3). The offset is removed with the group's activation sum:
+// s * sum u*x - 128 s * sum x.
+struct CodecQ8Sym {
+  static constexpr int kTileVgprs = 34;
+  template <int GPL>
+  struct Loads {
+    u32x2 sc[GPL];
+    u32x4 code[kTileRows][GPL][2];
+  };
+  template <int GPL>
+  __device__ __forceinline__ static void fetch(const WeightPtrs& w, int N, int G, int t, const int (&g0)[GPL],
+                                               int lane, Loads<GPL>& L) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      const Slot s = slot_of(G, g0[j], lane);
+      const u32x2* sp = static_cast<const u32x2*>(w.side) + (size_t(t) * G + g0[j] + s.base);
+      L.sc[j] = __builtin_nontemporal_load(sp + s.gl);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const u32x4* row = w.codes + size_t(clamp_row(t, r, N)) * (2 * size_t(G)) + g0[j] + s.base;
+        L.code[r][j][0] = __builtin_nontemporal_load(row + s.gl);
+        L.code[r][j][1] = __builtin_nontemporal_load(row + G + s.gl);
+      }
+    }
+  }
+  template <int M, int GPL, class XA>
+  __device__ __forceinline__ static void compute(const Loads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) {
+      float lo[kTileRows][M], hi[kTileRows][M];
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {  // x chunk d: k = 8d .. 8d+7 = half d/2, code words 2(d%2), 2(d%2)+1
+        u32x4 xq[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t w = elem(L.code[r][j][d / 2], 2 * (d % 2) + i);
+            const uint32_t p0 = w & 0x00FF00FFu, p1 = (w >> 8) & 0x00FF00FFu;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              lo[r][m] = dot2(p0, elem(xq[m], 2 * i), lo[r][m]);
+              hi[r][m] = dot2(p1, elem(xq[m], 2 * i + 1), hi[r][m]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const float s = half_of(L.sc[j], r);
+        const float sc = s * 0x1p24f;
+        const float mn = -128.f * s;  // exact
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          acc[r][m] = __builtin_fmaf(sc, lo[r][m] + hi[r][m], acc[r][m]);
+          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  }
+};
+
+// Waves per workgroup an instantiation may use: its VGPR estimate (x slice,
+// tile loads in flight, accumulators) must fit the 512-entry register file
+// shared by the waves on one SIMD.
+template <class C>
+__host__ __device__ constexpr int max_waves_of(int M, int GPL) {
+  return (16 * M * GPL + (double_buffered(M) ? 2 : 1) * C::kTileVgprs * GPL + 6 * M + 30) <= 128 ? 16 : 8;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel body
+// ---------------------------------------------------------------------------
+
+template <class C, int M, int GPL, int MODE>
+__device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const WeightPtrs& wp, float* __restrict__ y,
+                                          int N, int G, int T, int nchunks, int tpb) {
+  const int lane = threadIdx.x & 63;
+  // wave-uniform values kept in scalar registers, so every load address is a
+  // scalar base plus the one per-lane offset `lane`
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
+  const int nblocks = (T + tpb - 1) / tpb;
+  if (int(blockIdx.x) >= nblocks) return;
+
+  auto bases = [&](int c, int (&g0)[GPL]) {
+#pragma unroll
+    for (int j = 0; j < GPL; ++j) g0[j] = c * chunk_groups + (wave * GPL + j) * 64;
+  };
+
+  u32x4 xv[M][GPL][4];
+  float xs[M][GPL];
+  auto fetch_x = [&](int c) {
+    int g0[GPL];
+    bases(c, g0);
+    load_x<M, GPL>(x, G, g0, lane, xv, xs);
+  };
+
+  // per-wave partials of one block of tiles: [tile][row][m][wave]
+  __shared__ float part[MODE == kDirect ? 1 : kTilesPerBlock][kTileRows][M][MODE == kDirect ? 1 : kMaxWaves];
+
+  // combine the waves' partials of block b (all passes done) and store
+  auto reduce_block = [&](int b) {
+    __syncthreads();
+    const int ntiles = min(tpb, T - b * tpb);
+    for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
+      const int ti = i / (kTileRows * M);
+      const int r = (i / M) % kTileRows;
+      const int m = i % M;
+      const int n = (b * tpb + ti) * kTileRows + r;
+      if (n < N) {
+        float s = 0.f;
+        for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
+        y[size_t(m) * N + n] = s;
+      }
+    }
+    __syncthreads();
+  };
+
+  using Loads = typename C::template Loads<GPL>;
+
+  if constexpr (MODE == kMulti) {
+    // passes over K outermost within a block: x of pass c is fetched once at
+    // the top of the pass and stays in registers for the block's tiles
+    for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
+      const int ntiles = min(tpb, T - b * tpb);
+      for (int c = 0; c < nchunks; ++c) {
+        fetch_x(c);
+        int g0[GPL];
+        bases(c, g0);
+        for (int tb = 0; tb < ntiles; ++tb) {
+          Loads la;
+          C::template fetch<GPL>(wp, N, G, b * tpb + tb, g0, lane, la);
+          float acc[kTileRows][M];
+          C::template compute<M, GPL>(la, RegX<M, GPL>{xv, xs}, acc);
+          if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+              for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + acc[r][m];
+          }
+        }
+      }
+      reduce_block(b);
+    }
+    return;
+  } else {
+    // Items e = 0 .. n_items-1 of this workgroup: tile tb = e % tpb of its
+    // (e / tpb)-th block. The item count is known up front and the loop's
+    // only exit is its condition, so every fetch inside the loop is
+    // unconditional (a fetch that might not happen would make the compiler
+    // merge buffer contents with register moves that wait for the loads in
+    // flight); tiles past T (in the matrix's last block only) fetch a clamped
+    // tile and are skipped. A scheduling barrier after each fetch keeps the
+    // next tile's loads ahead of the current tile's compute.
+    const int my_blocks = (nblocks - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+    const int n_items = my_blocks * tpb;
+    int g0[GPL];
+    bases(0, g0);
+    auto tile_of = [&](int e) { return (int(blockIdx.x) + (e / tpb) * int(gridDim.x)) * tpb + e % tpb; };
+    auto fetch = [&](int e, Loads& L) {
+      const int t = tile_of(e);
+      C::template fetch<GPL>(wp, N, G, t < T ? t : T - 1, g0, lane, L);
+    };
+    auto finish = [&](const Loads& L, int e) {
+      const int t = tile_of(e);
+      if (t < T) {
+        float acc[kTileRows][M];
+        C::template compute<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
+        if constexpr (MODE == kDirect) {
+          store_tile<M>(acc, y, N, t, lane);
+        } else if (lane == 0) {
+          const int tb = e % tpb;
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) part[tb][r][m][wave] = acc[r][m];
+        }
+      }
+      if constexpr (MODE == kBlock) {
+        if (e % tpb == tpb - 1) reduce_block(int(blockIdx.x) + (e / tpb) * int(gridDim.x));
+      }
+    };
+
+    Loads la, lb;
+    fetch(0, la);
+    fetch_x(0);  // after the first tile's loads, so both latencies overlap
+    int e = 0;
+    if constexpr (double_buffered(M)) {
+      while (e + 2 < n_items) {
+        fetch(e + 1, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(la, e);
+        fetch(e + 2, la);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(lb, e + 1);
+        e += 2;
+      }
+      if (n_items - e == 2) {
+        fetch(e + 1, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(la, e);
+        finish(lb, e + 1);
+      } else {
+        finish(la, e);
+      }
+    } else {
+      finish(la, 0);
+      for (e = 1; e < n_items; ++e) {
+        fetch(e, la);
+        finish(la, e);
+      }
+    }
+  }
+}
+
+}  // namespace w4a16_dev
+
+// ---------------------------------------------------------------------------
+// Host side: launch-shape choice
+// ---------------------------------------------------------------------------
+
+namespace w4a16_host {
+
+constexpr int kGplOptions[] = {1, 2, 4};
+constexpr int kNumGpl = 3;
+
+// the x slice of one lane stays within 32 VGPRs (one group per lane always allowed)
+constexpr bool gpl_allowed(int M, int gpl) { return 16 * M * gpl <= 32 || gpl == 1; }
+
+inline int mode_of(int waves, int nchunks) {
+  return nchunks > 1 ? w4a16_dev::kMulti : waves > 1 ? w4a16_dev::kBlock : w4a16_dev::kDirect;
+}
+
+struct LaunchShape {
+  int gi;       // index into kGplOptions
+  int waves;    // waves per workgroup
+  int nchunks;  // passes over K
+};
+
+template <class C>
+LaunchShape shape_for_gpl(int M, int G, int gi) {
+  const int gpl = kGplOptions[gi];
+  const int wmax = w4a16_dev::max_waves_of<C>(M, gpl);
+  const int nchunks = (G + wmax * 64 * gpl - 1) / (wmax * 64 * gpl);
+  const int waves = (G + nchunks * 64 * gpl - 1) / (nchunks * 64 * gpl);
+  return LaunchShape{gi, waves, nchunks};
+}
+
+// Fewest passes over K; then avoid leaving more than a quarter of the lanes
+// idle; then, at M = 1, one group per lane (a tile's K split over more waves:
+// each wave loads less of x and more waves share the streaming; measured
+// faster on every decode-step shape); then the fewest waves per workgroup;
+// then the fewest idle lanes.
+template <class C>
+LaunchShape choose_shape(int M, int G) {
+  LaunchShape best{-1, 0, 0};
+  long best_key[5] = {0, 0, 0, 0, 0};
+  for (int gi = kNumGpl - 1; gi >= 0; --gi) {
+    if (!gpl_allowed(M, kGplOptions[gi])) continue;
+    const LaunchShape s = shape_for_gpl<C>(M, G, gi);
+    const long slots = long(s.nchunks) * s.waves * 64 * kGplOptions[gi];
+    const long idle = slots - G;
+    const long key[5] = {s.nchunks, 4 * idle > slots ? 1 : 0, M == 1 ? kGplOptions[gi] : 0, s.waves, idle};
+    bool better = best.gi < 0;
+    for (int i = 0; i < 5 && !better; ++i) {
+      if (key[i] < best_key[i]) better = true;
+      if (key[i] > best_key[i]) break;
+    }
+    if (better) {
+      best = s;
+      for (int i = 0; i < 5; ++i) best_key[i] = key[i];
+    }
+  }
+  return best;
+}
+
+// Tiles per block and grid of a launch: every workgroup resident at once,
+// each walking an equal share of the tiles. A workgroup reads its x slices
+// once per block, so wide workgroups (long K split over four or more waves, a
+// large x) take enough tiles per block for about one workgroup per CU;
+// narrower ones fill the resident slots first.
+inline void grid_of(int T, int waves, bool direct, int cus, int occ, int& tpb, int& grid) {
+  const int max_grid = cus * occ;
+  tpb = direct ? 1 : waves >= 4 ? T / cus : T / max_grid;
+  tpb = tpb < 1 ? 1 : tpb > w4a16_dev::kTilesPerBlock ? w4a16_dev::kTilesPerBlock : tpb;
+  const int units = (T + tpb - 1) / tpb;
+  grid = units < max_grid ? units : max_grid;
+}
+
+}  // namespace w4a16_host

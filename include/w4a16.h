@@ -61,7 +61,8 @@ typedef enum w4a16_status {
   W4A16_ERR_ALIGN = 3,    /* a pointer breaks its alignment rule */
   W4A16_ERR_SIZE = 4,     /* an output buffer is smaller than required */
   W4A16_ERR_OVERLAP = 5,  /* y overlaps x or the packed weights */
-  W4A16_ERR_HIP = 6       /* the HIP runtime reported an error */
+  W4A16_ERR_HIP = 6,      /* the HIP runtime reported an error */
+  W4A16_ERR_FORMAT = 7    /* unknown codec, or a code outside its codec's range */
 } w4a16_status;
 
 /* Version of this ABI and of the packed layout; bumped on any change. */
@@ -238,6 +239,98 @@ w4a16_status w4a16_gemv_chain_timed(const void* plan, int32_t count, int32_t M, 
  * Errors: NULL out -> W4A16_ERR_NULL; M outside 1..8 -> W4A16_ERR_SHAPE.
  */
 w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]);
+
+/*
+ * Weight-code variants: the same decode GEMV over other group codes.
+ *
+ * The Magnitude page (section 4.2, model conversion) compares the quantisation
+ * types it measured: a symmetric 4-bit type (smallest, least accurate), the
+ * 4-bit K-quant (the group-affine code above) and a 5-bit K-quant (more
+ * accurate, about a quarter larger). The core-modules page puts edge weights
+ * at INT8 or INT4 (section 5.1) and lists 4-bit and 8-bit weight
+ * quantisation among the runtimes (section 5.2). No page defines these
+ * formats; every codec below keeps groups of 32 consecutive k of one row
+ * with binary16 parameters and no super-blocks. s and m are binary16
+ * [N][K/32] arrays as in "Weight format"; G, T and S are as in "Packed
+ * layout", S being the code region's size rounded up to 256 bytes.
+ *
+ * W4A16_CODEC_Q4 (0): the group-affine 4-bit code of w4a16_pack / w4a16_gemv.
+ *
+ * W4A16_CODEC_Q4_SYM (1): w_hat = s * (q - 8), q unsigned 4-bit.
+ *   codes uint8 [N][K/2] as in "Weight format"; no min.
+ *   packed: [0, N*K/2) the 4-bit code chunks of "Packed layout";
+ *           [S, S + T*G*8) scale tiles: [T][G] entries of 8 bytes, row r of
+ *           entry (t, g) in bytes 2r..2r+1 (rows at or beyond N are zero).
+ *
+ * W4A16_CODEC_Q5 (2): w_hat = s * q + m, q unsigned 5-bit (0..31).
+ *   codes uint8 [N][K], one code per byte (a code above 31 is refused).
+ *   packed: [0, N*K/2) the codes' low 4 bits as 4-bit code chunks;
+ *           [S, S + T*G*16) fifth-bit tiles: [T][G] entries of 16 bytes, row
+ *           r of entry (t, g) in the little-endian 32-bit word at bytes
+ *           4r..4r+3, whose bit 4j + d (j = 0..7, d = 0..3) is bit 4 of the
+ *           code of k = 32g + 8d + 2(j mod 4) + j/4;
+ *           [S + T*G*16, S + 2*T*G*16) scale/min tiles as in "Packed layout".
+ *
+ * W4A16_CODEC_Q8_SYM (3): w_hat = s * q, q signed 8-bit (two's complement).
+ *   codes int8 [N][K] (passed as their bytes); no min.
+ *   packed: [0, N*K) codes: row n occupies K bytes, first the G 16-byte low
+ *           halves of its groups (k = 32g .. 32g+15), then the G high halves
+ *           (k = 32g+16 .. 32g+31); each byte is q + 128, and the
+ *           little-endian 32-bit word e of a half holds k = 4e + i of that
+ *           half with i = 0, 2, 1, 3 in bytes 0, 1, 2, 3;
+ *           [S, S + T*G*8) scale tiles as for W4A16_CODEC_Q4_SYM.
+ */
+typedef enum w4a16_codec {
+  W4A16_CODEC_Q4 = 0,
+  W4A16_CODEC_Q4_SYM = 1,
+  W4A16_CODEC_Q5 = 2,
+  W4A16_CODEC_Q8_SYM = 3
+} w4a16_codec;
+
+/* Bytes of the packed blob of a codec (0 for an unknown codec or a bad N/K). */
+size_t w4a16_codec_packed_bytes(int32_t codec, int32_t N, int32_t K);
+
+/*
+ * w4a16_codec_pack - host repacker of a codec (init time; touches no GPU).
+ *   codes  host array in the codec's canonical layout (see above), read only
+ *   scale  host binary16 bits [N][K/32], read only
+ *   min    host binary16 bits [N][K/32] for the affine codecs (0 and 2);
+ *          ignored, and may be NULL, for the symmetric ones
+ *   out    host buffer of at least w4a16_codec_packed_bytes(codec, N, K)
+ *          bytes, owned by the caller, written completely
+ * Errors: unknown codec or a 5-bit code above 31 -> W4A16_ERR_FORMAT (nothing
+ * written); NULL -> W4A16_ERR_NULL; bad N/K -> W4A16_ERR_SHAPE; out_bytes too
+ * small -> W4A16_ERR_SIZE. Codec 0 is exactly w4a16_pack.
+ */
+w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, const uint16_t* scale, const uint16_t* min,
+                              int32_t N, int32_t K, void* out, size_t out_bytes);
+
+/*
+ * w4a16_codec_gemv - y[M][N] = x[M][K] * w_hat^T for a blob written by
+ * w4a16_codec_pack with the same codec, N and K. Arguments, ownership,
+ * alignment (packed 256-byte aligned), overwrite semantics, determinism and
+ * errors are those of w4a16_gemv, plus: unknown codec -> W4A16_ERR_FORMAT.
+ * Codec 0 is exactly w4a16_gemv.
+ */
+w4a16_status w4a16_codec_gemv(int32_t codec, const void* x, const void* packed, float* y, int32_t M, int32_t N,
+                              int32_t K, void* stream);
+
+/* w4a16_codec_gemv with the kernel's own start and end recorded into two
+ * caller-owned HIP events, as w4a16_gemv_timed. Either event NULL ->
+ * W4A16_ERR_NULL. */
+w4a16_status w4a16_codec_gemv_timed(int32_t codec, const void* x, const void* packed, float* y, int32_t M,
+                                    int32_t N, int32_t K, void* stream, void* start_event, void* stop_event);
+
+/*
+ * w4a16_codec_launch_shape - host only: out[0] = groups of 32 k per lane,
+ * out[1] = waves per workgroup, out[2] = passes over K of the kernel
+ * w4a16_codec_gemv launches; for codecs 1..3 profilers name it
+ * codec_kernel<codec, M, out[0], mode> with mode 0 (one wave per tile),
+ * 1 (waves split K) or 2 (several passes over K). Codec 0: as
+ * w4a16_launch_shape. Errors: NULL -> W4A16_ERR_NULL; unknown codec ->
+ * W4A16_ERR_FORMAT; shape out of range -> W4A16_ERR_SHAPE.
+ */
+w4a16_status w4a16_codec_launch_shape(int32_t codec, int32_t M, int32_t N, int32_t K, int32_t out[3]);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* w4a16_status_string(int32_t status);
