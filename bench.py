@@ -21,7 +21,9 @@ oracle timed on this host's cores as a reported CPU baseline.
 
 --only chain|separate times one form (for counter runs); --copy-calibration
 runs only a plain device copy of 1 GiB three times (the FETCH_SIZE /
-WRITE_SIZE scale of a kernel of known traffic).
+WRITE_SIZE scale of a kernel of known traffic). --codec q4_sym|q5|q8_sym runs
+the same step with one of the weight-code variants (separate launches only:
+the chain streams the 4-bit code) and reports it the same way.
 """
 from __future__ import annotations
 
@@ -44,17 +46,33 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD = "llama8b_step"
 
 
-def gemv_bytes(M, N, K):
-    return N * K // 2 + 4 * N * (K // 32) + 2 * M * K + 4 * M * N
+# code bits per weight and parameter bytes per group of 32 weights, per codec
+CODEC_BITS = {"q4": (4, 4), "q4_sym": (4, 2), "q5": (5, 4), "q8_sym": (8, 2)}
+CODEC_DTYPE = {"q4": "u4xf16->f32", "q4_sym": "u4xf16->f32", "q5": "u5xf16->f32", "q8_sym": "i8xf16->f32"}
+CODEC_TEXT = {"q4": "4-bit codes, group 32, fp16 scale+min",
+              "q4_sym": "symmetric 4-bit codes (s*(q-8)), group 32, fp16 scale",
+              "q5": "5-bit codes, group 32, fp16 scale+min",
+              "q8_sym": "symmetric 8-bit codes (s*q, int8), group 32, fp16 scale"}
+
+
+def gemv_bytes(M, N, K, codec="q4"):
+    """Algorithmic bytes of one GEMV: codes, per-group parameters, x and y."""
+    bits, par = CODEC_BITS[codec]
+    return N * K * bits // 8 + par * N * (K // 32) + 2 * M * K + 4 * M * N
 
 
 # HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
 # only while the kernel is unchanged since the counters were taken.
 TRAFFIC = {
-    # gemv_kernel<1, 1, 1>: not yet re-counted since its code last changed
-    # (2,137,259.6 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
-    "chain_kernel<1, 2, 4>": 4_383_792_435,
+    # (16,745.89 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    "gemv_kernel<1, 1, 1>": 34_348_829,
+    # (2,137,261.1 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
+    "chain_kernel<1, 2, 4>": 4_383_795_507,
+    # weight-code variants: (15,090.96 / 20,099.55 / 28,412.93 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
+    "codec_kernel<1, 1, 1, 1>": 30_959_537,
+    "codec_kernel<2, 1, 1, 1>": 41_217_127,
+    "codec_kernel<3, 1, 1, 1>": 58_252_492,
 }
 
 
@@ -73,14 +91,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_inputs(torch, w4, M, dev, threads):
+def build_inputs(torch, w4, M, dev, threads, codec="q4"):
     """Generate, pack and upload every GEMV of the step; returns a list of dicts."""
     items = list(workload.workload_gemvs(WORKLOAD, M))
 
     def make(item):
         layer, pi, p, m = item
-        x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, layer, pi, m)
-        blob = w4.w4a16_pack(codes, scale, mn)
+        x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, layer, pi, m)
+        blob = w4.w4a16_codec_pack(codec, codes, scale, mn)
         return item, x, blob
 
     out = []
@@ -90,33 +108,34 @@ def build_inputs(torch, w4, M, dev, threads):
             xd = torch.from_numpy(x).to(dev)
             y = torch.zeros((m, p.N), dtype=torch.float32, device=dev)
             out.append(dict(layer=layer, proj=pi, name=p.name, M=m, N=p.N, K=p.K, x=xd, packed=packed, y=y,
-                            bytes=gemv_bytes(m, p.N, p.K),
-                            kernel=w4.w4a16_launch_shape(m, p.N, p.K)["kernel"]))
+                            bytes=gemv_bytes(m, p.N, p.K, codec),
+                            kernel=w4.w4a16_codec_launch_shape(codec, m, p.N, p.K)["kernel"]))
             del blob
     return out
 
 
-def launch_step(w4, gemvs, stream_handle):
+def launch_step(w4, gemvs, stream_handle, codec="q4"):
+    cid = w4.codec_id(codec)
     for g in gemvs:
-        st = w4.w4a16_gemv_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], stream_handle)
+        st = w4.w4a16_codec_gemv_raw(cid, g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], stream_handle)
         if st != 0:
-            raise w4.W4A16Error(st, "w4a16_gemv")
+            raise w4.W4A16Error(st, "w4a16_codec_gemv")
 
 
-def spot_check(w4, gemvs, torch):
+def spot_check(w4, gemvs, torch, codec="q4"):
     """Sampled rows of two GEMVs of the step against the oracle (sanity only)."""
     import oracle
 
     for g in (gemvs[2], gemvs[3]):
-        x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, g["layer"], g["proj"], g["M"])
+        x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, g["layer"], g["proj"], g["M"])
         rows = np.arange(0, g["N"], max(1, g["N"] // 64))
-        y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
+        y_ref, B = oracle.codecs_ref.gemv_rows(codec, x, codes, scale, mn, rows)
         y = g["y"].cpu().numpy()[:, rows].astype(np.float64)
         if not oracle.within_tolerance(y, y_ref, B).all():
             raise AssertionError(f"bench spot check failed on {g['name']} layer {g['layer']}")
 
 
-def cpu_baseline(budget_s=12.0):
+def cpu_baseline(budget_s=12.0, codec="q4"):
     """The fp64 oracle on whole GEMVs of the same step until ~budget_s of work."""
     import threadpoolctl
 
@@ -128,11 +147,14 @@ def cpu_baseline(budget_s=12.0):
     t_total = 0.0
     with threadpoolctl.threadpool_limits(1):
         for layer, pi, p, m in workload.workload_gemvs(WORKLOAD, 1):
-            x, codes, scale, mn = workload.gemv_inputs(WORKLOAD, layer, pi, m)
+            x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, layer, pi, m)
             t0 = time.perf_counter()
-            oracle.gemv(x, codes, scale, mn, threads=threads)
+            if codec == "q4":
+                oracle.gemv(x, codes, scale, mn, threads=threads)
+            else:
+                oracle.codecs_ref.gemv(codec, x, codes, scale, mn, threads=threads)
             t_total += time.perf_counter() - t0
-            done_bytes += gemv_bytes(m, p.N, p.K)
+            done_bytes += gemv_bytes(m, p.N, p.K, codec)
             done.append(f"L{layer}.{p.name}")
             if t_total >= budget_s:
                 break
@@ -146,7 +168,7 @@ def cpu_baseline(budget_s=12.0):
                   f"{done_bytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, "
                   f"{threads} worker threads, BLAS threads limited to 1",
         "us_per_step_extrapolated": round(t_total / done_bytes * sum(
-            gemv_bytes(m, p.N, p.K) for _, _, p, m in workload.workload_gemvs(WORKLOAD, 1)) * 1e6, 1),
+            gemv_bytes(m, p.N, p.K, codec) for _, _, p, m in workload.workload_gemvs(WORKLOAD, 1)) * 1e6, 1),
     }
 
 
@@ -174,7 +196,14 @@ def main():
     ap.add_argument("--only", choices=["chain", "separate"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time separate launches eagerly (counter runs)")
+    ap.add_argument("--codec", choices=list(CODEC_BITS), default="q4",
+                    help="weight code of the step (the chain runs the 4-bit code only)")
     args = ap.parse_args()
+    codec = args.codec
+    if codec != "q4":
+        if args.only == "chain":
+            ap.error("the chain streams the 4-bit code only")
+        args.only = "separate"
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the W4A16 GEMV path has no multi-GPU code "
@@ -197,7 +226,7 @@ def main():
     M = 1
 
     t0 = time.time()
-    gemvs = build_inputs(torch, w4, M, dev, threads=min(16, len(os.sched_getaffinity(0))))
+    gemvs = build_inputs(torch, w4, M, dev, threads=min(16, len(os.sched_getaffinity(0))), codec=codec)
     torch.cuda.synchronize()
     for g in gemvs:
         g["xp"], g["pp"], g["yp"] = g["x"].data_ptr(), g["packed"].data_ptr(), g["y"].data_ptr()
@@ -207,45 +236,48 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
 
-    # the decode step as one chained launch: plan and workspace made once
-    plan = torch.from_numpy(w4.w4a16_chain_plan(
-        [(g["x"], g["packed"], g["y"], g["N"], g["K"]) for g in gemvs], M)).to(dev)
-    workspace = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev)
-    plan_p, ws_p, count = plan.data_ptr(), workspace.data_ptr(), len(gemvs)
-
-    ws_bytes = workspace.numel() * workspace.element_size()
-
-    def chain_step():
-        st = w4.w4a16_gemv_chain_raw(plan_p, count, M, ws_p, ws_bytes, sh)
-        if st != 0:
-            raise w4.W4A16Error(st, "w4a16_gemv_chain")
-
-    # separate launches first (their outputs are the chain's reference), then the chain
+    # separate launches first (their outputs are the chain's reference)
     with torch.cuda.stream(stream):
-        launch_step(w4, gemvs, sh)
+        launch_step(w4, gemvs, sh, codec)
     stream.synchronize()
-    spot_check(w4, gemvs, torch)
-    separate = [g["y"].clone() for g in gemvs]
-    for g in gemvs:
-        g["y"].fill_(float("nan"))
-    with torch.cuda.stream(stream):
-        chain_step()
-    stream.synchronize()
-    spot_check(w4, gemvs, torch)
-    worst = max(float(((g["y"] - r).abs() / (r.abs() + 1e-3)).max()) for g, r in zip(gemvs, separate))
-    if workspace.cpu().numpy().any():
-        raise AssertionError("chain workspace not clean after a call (counters, flags or error word)")
-    log(f"[bench] spot checks ok; chain vs separate launches: max rel diff {worst:.2e}")
+    spot_check(w4, gemvs, torch, codec)
+
+    if codec == "q4":
+        # the decode step as one chained launch: plan and workspace made once
+        plan = torch.from_numpy(w4.w4a16_chain_plan(
+            [(g["x"], g["packed"], g["y"], g["N"], g["K"]) for g in gemvs], M)).to(dev)
+        workspace = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev)
+        plan_p, ws_p, count = plan.data_ptr(), workspace.data_ptr(), len(gemvs)
+        ws_bytes = workspace.numel() * workspace.element_size()
+
+        def chain_step():
+            st = w4.w4a16_gemv_chain_raw(plan_p, count, M, ws_p, ws_bytes, sh)
+            if st != 0:
+                raise w4.W4A16Error(st, "w4a16_gemv_chain")
+
+        separate = [g["y"].clone() for g in gemvs]
+        for g in gemvs:
+            g["y"].fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            chain_step()
+        stream.synchronize()
+        spot_check(w4, gemvs, torch)
+        worst = max(float(((g["y"] - r).abs() / (r.abs() + 1e-3)).max()) for g, r in zip(gemvs, separate))
+        if workspace.cpu().numpy().any():
+            raise AssertionError("chain workspace not clean after a call (counters, flags or error word)")
+        log(f"[bench] spot checks ok; chain vs separate launches: max rel diff {worst:.2e}")
+    else:
+        log(f"[bench] spot checks ok ({codec})")
 
     forms = {}
     if args.only in (None, "separate"):
         # separate launches, replayed from a HIP graph
         if args.no_graph:
-            replay = lambda: launch_step(w4, gemvs, sh)  # noqa: E731
+            replay = lambda: launch_step(w4, gemvs, sh, codec)  # noqa: E731
         else:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
-                launch_step(w4, gemvs, stream.cuda_stream)
+                launch_step(w4, gemvs, stream.cuda_stream, codec)
             torch.cuda.synchronize()
             replay = graph.replay
         forms["separate"] = time_loop(torch, stream, replay, args.warmup, args.steps)
@@ -291,13 +323,13 @@ def main():
                 for g in gemvs:
                     if g["kernel"] == kernel:
                         a, b = timed_events()
-                        st = w4.w4a16_gemv_timed_raw(g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"], sh,
-                                                     a.cuda_event, b.cuda_event)
+                        st = w4.w4a16_codec_gemv_timed_raw(codec, g["xp"], g["pp"], g["yp"], g["M"], g["N"], g["K"],
+                                                           sh, a.cuda_event, b.cuda_event)
                         if st != 0:
-                            raise w4.W4A16Error(st, "w4a16_gemv_timed")
+                            raise w4.W4A16Error(st, "w4a16_codec_gemv_timed")
                         marks.append((a, b))
                     else:
-                        launch_step(w4, [g], sh)
+                        launch_step(w4, [g], sh, codec)
     torch.cuda.synchronize()
     avg_us = sum(a.elapsed_time(b) for a, b in marks) / len(marks) * 1e3
     per_launch = sum(launch_bytes) / len(launch_bytes)
@@ -319,15 +351,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4xf16->f32",
+        "dtype": CODEC_DTYPE[codec],
         "data": "synthetic",
         "config": {
             "workload": "llama8b_step: 32 Llama-3-8B-shaped layers x (qkv 4096->6144, o 4096->4096, "
-                        "gate_up 4096->28672, down 14336->4096), M=1, 4-bit codes, group 32, fp16 scale+min",
+                        "gate_up 4096->28672, down 14336->4096), M=1, " + CODEC_TEXT[codec],
             "gemvs_per_step": len(gemvs),
             "bytes_per_step": step_bytes,
             "launch": {"chain": "one w4a16_gemv_chain launch per step, products ordered on the device",
-                       "separate": "128 w4a16_gemv launches per step, replayed from a HIP graph"}[form],
+                       "separate": "128 %s launches per step, replayed from a HIP graph"
+                                   % ("w4a16_gemv" if codec == "q4" else "w4a16_codec_gemv")}[form],
             "us_per_step_by_launch_form": {k: round(v * 1e6, 2) for k, v in forms.items()},
         },
         "roofline": {
@@ -344,7 +377,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on host cores ...")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget, codec)
     print(json.dumps(line), flush=True)
 
 
