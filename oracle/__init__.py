@@ -18,3 +18,4 @@ from .w4a16_ref import (  # noqa: F401
     within_tolerance,
 )
 from . import codecs_ref  # noqa: F401,E402  (weight-code variants)
+from . import kv_attention_ref  # noqa: F401,E402  (decode attention over a quantised KV cache)

@@ -172,6 +172,46 @@ def random_codec_problem(codec: str, seed: int, M: int, N: int, K: int, outliers
     return x, codes, scale, mn
 
 
+# Decode attention over a quantised KV cache (one layer per call): the
+# Llama-3-8B attention shape (32 query heads, 8 KV heads, head size 128,
+# 32 layers). The context lengths are the core-modules page's maximum contexts
+# for a 2.37 GiB KV budget (section 5.4): 38,863 tokens with INT8 values and
+# 77,726 with INT4. Recipe per layer (own seed keys):
+#   INT8: codes uniform -128..127, scale U[0.004, 0.012] -> binary16;
+#   INT4: codes uniform bytes (two uniform nibbles), scale U[0.08, 0.16] and
+#         min U[-1.2, -0.6] -> binary16;
+#   q:    N(0, 1) -> binary16, [Hq, 128].
+KV_HQ, KV_HKV, KV_D, KV_LAYERS = 32, 8, 128, 32
+KV_CONTEXT = {8: 38863, 4: 77726}
+_T_KV = 40  # first tensor id of the KV draws
+
+
+def kv_cache(bits: int, wid: int, layer: int, T: int, Hkv: int = KV_HKV):
+    """Seeded (k_codes, k_scale, k_min, v_codes, v_scale, v_min) of one layer's
+    cache; the mins are None for INT8."""
+    if bits not in (8, 4) or T < 1 or Hkv < 1:
+        raise ValueError("bits must be 8 or 4, T and Hkv positive")
+    out = []
+    for which in range(2):  # keys, then values
+        base = _T_KV + 4 * which
+        r = _rng(wid, layer, 0, base)
+        if bits == 8:
+            codes = r.integers(-128, 128, size=(T, Hkv, KV_D), dtype=np.int8)
+            scale = _rng(wid, layer, 0, base + 1).uniform(0.004, 0.012, size=(T, Hkv, KV_D // GROUP))
+            out += [codes, scale.astype(np.float16), None]
+        else:
+            codes = r.integers(0, 256, size=(T, Hkv, KV_D // 2), dtype=np.uint8)
+            scale = _rng(wid, layer, 0, base + 1).uniform(0.08, 0.16, size=(T, Hkv, KV_D // GROUP))
+            mn = _rng(wid, layer, 0, base + 2).uniform(-1.2, -0.6, size=(T, Hkv, KV_D // GROUP))
+            out += [codes, scale.astype(np.float16), mn.astype(np.float16)]
+    return tuple(out)
+
+
+def kv_query(wid: int, layer: int, Hq: int = KV_HQ) -> np.ndarray:
+    """Seeded query q binary16 [Hq, 128]."""
+    return _rng(wid, layer, 0, _T_KV + 9).standard_normal(size=(Hq, KV_D)).astype(np.float16)
+
+
 def random_problem(seed: int, M: int, N: int, K: int, outliers: bool = False):
     """Seeded inputs for an arbitrary (M, N, K), used by edge-shape tests."""
     codes, scale, mn = weights(1000 + seed, 0, 0, N, K)
