@@ -47,6 +47,12 @@ EXPORTS = (
     "w4a16_codec_gemv",
     "w4a16_codec_gemv_timed",
     "w4a16_codec_launch_shape",
+    "w4a16_kv_packed_bytes",
+    "w4a16_kv_pack",
+    "w4a16_kv_workspace_bytes",
+    "w4a16_kv_attention",
+    "w4a16_kv_attention_timed",
+    "w4a16_kv_launch_shape",
 )
 
 W4A16_CHAIN_WORKSPACE_BYTES = 69632
@@ -110,6 +116,18 @@ def lib() -> ctypes.CDLL:
     L.w4a16_codec_gemv_timed.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
     L.w4a16_codec_launch_shape.restype = c_i32
     L.w4a16_codec_launch_shape.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
+    L.w4a16_kv_packed_bytes.restype = c_sz
+    L.w4a16_kv_packed_bytes.argtypes = [c_i32, c_i32, c_i32]
+    L.w4a16_kv_pack.restype = c_i32
+    L.w4a16_kv_pack.argtypes = [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_sz]
+    L.w4a16_kv_workspace_bytes.restype = c_sz
+    L.w4a16_kv_workspace_bytes.argtypes = [c_i32, c_i32]
+    L.w4a16_kv_attention.restype = c_i32
+    L.w4a16_kv_attention.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
+    L.w4a16_kv_attention_timed.restype = c_i32
+    L.w4a16_kv_attention_timed.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp, c_vp]
+    L.w4a16_kv_launch_shape.restype = c_i32
+    L.w4a16_kv_launch_shape.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_status_string.argtypes = [c_i32]
     _lib = L
@@ -383,3 +401,93 @@ def w4a16_codec_gemv(codec, x, packed, y, stream=None) -> None:
     st = w4a16_codec_gemv_raw(codec, _ptr(x), _ptr(packed), _ptr(y), M, N, K, s)
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_codec_gemv")
+
+
+# ---------------------------------------------------------------------------
+# decode attention over a quantised KV cache
+# ---------------------------------------------------------------------------
+
+
+def w4a16_kv_packed_bytes(bits: int, T: int, Hkv: int) -> int:
+    return int(lib().w4a16_kv_packed_bytes(int(bits), int(T), int(Hkv)))
+
+
+def w4a16_kv_workspace_bytes(T: int, Hq: int) -> int:
+    return int(lib().w4a16_kv_workspace_bytes(int(T), int(Hq)))
+
+
+def w4a16_kv_pack(bits: int, k_codes, k_scale, k_min, v_codes, v_scale, v_min) -> np.ndarray:
+    """Host repack of one layer's canonical cache (see include/w4a16.h) into a uint8 blob."""
+    k_codes = np.ascontiguousarray(k_codes)
+    v_codes = np.ascontiguousarray(v_codes)
+    T, Hkv = int(k_codes.shape[0]), int(k_codes.shape[1])
+    want = (T, Hkv, 128 if bits == 8 else 64)
+    if k_codes.shape != want or v_codes.shape != want:
+        raise ValueError(f"codes must be {want}")
+    arrs = []
+    for a in (k_scale, k_min, v_scale, v_min):
+        if a is None:
+            arrs.append(None)
+            continue
+        a = np.ascontiguousarray(a, dtype=np.float16)
+        if a.shape != (T, Hkv, 4):
+            raise ValueError("scales and mins must be [T, Hkv, 4]")
+        arrs.append(a)
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    nbytes = w4a16_kv_packed_bytes(bits, T, Hkv)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    st = lib().w4a16_kv_pack(int(bits), k_codes.ctypes.data, ptr(arrs[0]), ptr(arrs[1]), v_codes.ctypes.data,
+                             ptr(arrs[2]), ptr(arrs[3]), T, Hkv, out.ctypes.data, out.nbytes)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_kv_pack")
+    return out
+
+
+def w4a16_kv_launch_shape(bits: int, T: int, Hq: int, Hkv: int) -> dict:
+    out = (ctypes.c_int32 * 3)()
+    st = lib().w4a16_kv_launch_shape(int(bits), int(T), int(Hq), int(Hkv), out)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_kv_launch_shape")
+    return {"heads_per_kv_head": out[0], "blocks_per_workgroup": out[1], "workgroups_per_kv_head": out[2],
+            "kernel": f"kv_attn_kernel<{int(bits)}, {out[0]}>", "merge_kernel": f"kv_combine_kernel<{out[0]}>"}
+
+
+def w4a16_kv_attention_raw(bits: int, q_ptr: int, kv_ptr: int, o_ptr: int, T: int, Hq: int, Hkv: int,
+                           ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
+    """Direct C call with raw pointers; returns the status code."""
+    return int(lib().w4a16_kv_attention(int(bits), q_ptr, kv_ptr, o_ptr, int(T), int(Hq), int(Hkv), ws_ptr,
+                                        int(ws_bytes), stream))
+
+
+def w4a16_kv_attention_timed_raw(bits: int, q_ptr: int, kv_ptr: int, o_ptr: int, T: int, Hq: int, Hkv: int,
+                                 ws_ptr: int, ws_bytes: int, stream: int, start_event: int, stop_event: int) -> int:
+    return int(lib().w4a16_kv_attention_timed(int(bits), q_ptr, kv_ptr, o_ptr, int(T), int(Hq), int(Hkv), ws_ptr,
+                                              int(ws_bytes), stream, start_event, stop_event))
+
+
+def w4a16_kv_attention(bits: int, q, kv, o, T: int, Hkv: int, workspace, stream=None) -> None:
+    """o[Hq, 128] for one layer (device tensors: q float16 [Hq, 128], kv the
+    uploaded packed cache, o float32 [Hq, 128], workspace any device buffer of
+    w4a16_kv_workspace_bytes(T, Hq) bytes)."""
+    if str(q.dtype) != "torch.float16" or str(o.dtype) != "torch.float32":
+        raise TypeError("q must be float16 and o float32")
+    if q.dim() != 2 or tuple(o.shape) != tuple(q.shape) or int(q.shape[1]) != 128:
+        raise ValueError("q and o must be [Hq, 128]")
+    if not (q.is_contiguous() and o.is_contiguous()):
+        raise ValueError("q and o must be contiguous")
+    Hq = int(q.shape[0])
+    need = w4a16_kv_packed_bytes(bits, T, Hkv)
+    if need == 0 or kv.numel() * kv.element_size() < need:
+        raise ValueError(f"packed cache too small or bad shape (needs {need} bytes)")
+    if stream is None:
+        import torch
+
+        s = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        s = stream.cuda_stream
+    else:
+        s = int(stream)
+    st = w4a16_kv_attention_raw(bits, _ptr(q), _ptr(kv), _ptr(o), T, Hq, Hkv, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), s)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_kv_attention")

@@ -60,6 +60,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, unsigned(q[0])) + __builtin_bit_cast(float, unsigned(q[1]));
 }
 
+// Maximum over the 64 lanes of a wave, by the same exchanges as wave_sum;
+// every lane ends with the same value.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  const unsigned b = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = fmaxf(__builtin_bit_cast(float, unsigned(p[0])), __builtin_bit_cast(float, unsigned(p[1])));
+  const unsigned c = __builtin_bit_cast(unsigned, v);
+  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(q[0])), __builtin_bit_cast(float, unsigned(q[1])));
+}
+
 // Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
 template <int GPL>
 struct TileLoads {

@@ -257,7 +257,76 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
   return W4A16_OK;
 }
 
-extern "C" int32_t w4a16_abi_version(void) { return 2; }
+// ---------------------------------------------------------------------------
+// Quantised KV cache (format in include/w4a16.h)
+// ---------------------------------------------------------------------------
+
+extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, const uint16_t* k_scale,
+                                      const uint16_t* k_min, const uint8_t* v_codes, const uint16_t* v_scale,
+                                      const uint16_t* v_min, int32_t T, int32_t Hkv, void* out, size_t out_bytes) {
+  if (bits != 8 && bits != 4) return W4A16_ERR_FORMAT;
+  if (!k_codes || !k_scale || !v_codes || !v_scale || !out || (bits == 4 && (!k_min || !v_min)))
+    return W4A16_ERR_NULL;
+  const size_t need = w4a16_kv_packed_bytes(bits, T, Hkv);
+  if (need == 0) return W4A16_ERR_SHAPE;
+  if (out_bytes < need) return W4A16_ERR_SIZE;
+  constexpr int64_t kD = 128, kTok = 64;
+  const int64_t nb = (int64_t(T) + kTok - 1) / kTok;
+  const int64_t R = bits == 8 ? 17408 : 10240;
+  const int64_t cb = bits == 8 ? kD : kD / 2;  // canonical code bytes per (token, head)
+  uint8_t* o = static_cast<uint8_t*>(out);
+  parallel_rows(int64_t(Hkv) * nb, R, [&](int64_t r0, int64_t r1) {
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t g = r / nb, b = r % nb;
+      uint8_t* rec = o + r * R;
+      std::memset(rec, 0, size_t(R));
+      for (int64_t tt = 0; tt < kTok; ++tt) {
+        const int64_t t = b * kTok + tt;
+        if (t >= T) break;
+        const uint8_t* kc = k_codes + (t * Hkv + g) * cb;
+        const uint8_t* vc = v_codes + (t * Hkv + g) * cb;
+        const int64_t pi = (t * Hkv + g) * 4;  // parameters of (t, g)
+        if (bits == 8) {
+          static constexpr int kDimOf[4] = {0, 2, 1, 3};  // dim offset held by byte slot j of a word
+          for (int c = 0; c < 8; ++c)
+            for (int e = 0; e < 4; ++e)
+              for (int j = 0; j < 4; ++j)
+                rec[c * 1024 + tt * 16 + 4 * e + j] = uint8_t(kc[16 * c + 4 * e + kDimOf[j]] ^ 0x80u);
+          std::memcpy(rec + 8192 + tt * 8, k_scale + pi, 8);
+          std::memcpy(rec + 8704 + tt * 8, v_scale + pi, 8);
+          // values: load c = tokens 8c..8c+7, lane l = dims 2l, 2l+1, byte 2*(token % 8) + e
+          const int64_t c = tt / 8, ti = tt % 8;
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 2; ++e)
+              rec[9216 + c * 1024 + l * 16 + 2 * ti + e] = uint8_t(vc[2 * l + e] ^ 0x80u);
+        } else {
+          for (int c = 0; c < 4; ++c)
+            for (int wd = 0; wd < 4; ++wd) {
+              uint32_t v;
+              std::memcpy(&v, kc + 16 * c + 4 * wd, 4);
+              v = split_even_odd(v);
+              std::memcpy(rec + c * 1024 + tt * 16 + 4 * wd, &v, 4);
+            }
+          uint16_t kp[8], vp[8];
+          for (int grp = 0; grp < 4; ++grp) {
+            kp[2 * grp] = k_scale[pi + grp];
+            kp[2 * grp + 1] = k_min[pi + grp];
+            vp[2 * grp] = v_scale[pi + grp];
+            vp[2 * grp + 1] = v_min[pi + grp];
+          }
+          std::memcpy(rec + 4096 + tt * 16, kp, 16);
+          std::memcpy(rec + 5120 + tt * 16, vp, 16);
+          // values: load c = tokens 16c..16c+15, lane l = canonical byte l (dims 2l, 2l+1), byte token % 16
+          const int64_t c = tt / 16, ti = tt % 16;
+          for (int l = 0; l < 64; ++l) rec[6144 + c * 1024 + l * 16 + ti] = vc[l];
+        }
+      }
+    }
+  });
+  return W4A16_OK;
+}
+
+extern "C" int32_t w4a16_abi_version(void) { return 3; }
 
 extern "C" const char* w4a16_status_string(int32_t status) {
   switch (status) {

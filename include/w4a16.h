@@ -332,6 +332,106 @@ w4a16_status w4a16_codec_gemv_timed(int32_t codec, const void* x, const void* pa
  */
 w4a16_status w4a16_codec_launch_shape(int32_t codec, int32_t M, int32_t N, int32_t K, int32_t out[3]);
 
+/*
+ * Decode attention over a quantised KV cache.
+ *
+ * The core-modules page (section 5.4, memory manager: KV budget) sizes the KV
+ * cache of an 8B grouped-query model (32 layers, 8 KV heads, head size 128)
+ * at 131,072 bytes per token in fp16, halved with INT8 and quartered with
+ * INT4 values: at every decode step the whole cache is read once per layer,
+ * the other bandwidth-bound operation of the step. The page defines no
+ * format; the one here quantises per (token, KV head, group of 32 consecutive
+ * dims) with binary16 parameters, like the weights:
+ *   INT8 (bits = 8): v = s * q, q signed 8-bit;
+ *   INT4 (bits = 4): v = s * q + m, q unsigned 4-bit.
+ * One call computes one layer for one new token: for each query head h (KV
+ * head g = h / (Hq / Hkv)),
+ *   o[h][d] = sum_t softmax_t(q[h] . k_hat[t][g] / sqrt(128)) * v_hat[t][g][d].
+ * The head size is 128; Hq / Hkv must be 1, 2, 4 or 8.
+ *
+ * Canonical cache arrays (host, per layer, tokens t < T):
+ *   INT8: codes int8 [T][Hkv][128] (as bytes), scale binary16 [T][Hkv][4];
+ *   INT4: codes uint8 [T][Hkv][64] (low nibble = even dim), scale and min
+ *         binary16 [T][Hkv][4].
+ * Packed cache (what w4a16_kv_pack writes): nb = ceil(T / 64) blocks of 64
+ * tokens per KV head; records of R bytes ordered [g][block], R = 17,408
+ * (INT8) or 10,240 (INT4). Inside the record of block b, slot i is token
+ * 64b + i; slots at or beyond T are zero.
+ *   INT8: [0, 8192) key codes: chunk c = dims 16c..16c+15 at 1024c, slot i's
+ *         16 bytes at 1024c + 16i, little-endian word e holding dims
+ *         16c + 4e + (0, 2, 1, 3) in bytes 0..3, each q + 128;
+ *         [8192, 8704) key scales, 8 bytes per slot (groups 0..3);
+ *         [8704, 9216) value scales, the same way;
+ *         [9216, 17408) value codes: load c = slots 8c..8c+7 at 9216 + 1024c,
+ *         lane l's 16 bytes at + 16l holding dims 2l, 2l+1 of those slots,
+ *         byte 2j + e = dim 2l + e of slot 8c + j, each q + 128.
+ *   INT4: [0, 4096) key codes: chunk c = group c (dims 32c..32c+31), slot i's
+ *         16 bytes at 1024c + 16i in the 4-bit weight chunk layout of
+ *         "Packed layout" (dims in the place of k);
+ *         [4096, 5120) key (scale, min) pairs, 16 bytes per slot;
+ *         [5120, 6144) value (scale, min) pairs, the same way;
+ *         [6144, 10240) value codes: load c = slots 16c..16c+15 at
+ *         6144 + 1024c, lane l's 16 bytes at + 16l, byte j = the canonical
+ *         byte l (dims 2l, 2l+1) of slot 16c + j.
+ */
+
+/* Bytes of one layer's packed cache (0 if bits is not 8 or 4, T < 1,
+ * T > 2^24, or Hkv outside 1..4096). */
+size_t w4a16_kv_packed_bytes(int32_t bits, int32_t T, int32_t Hkv);
+
+/*
+ * w4a16_kv_pack - host repacker of one layer's cache (touches no GPU).
+ *   k_codes, v_codes  canonical codes (see above), read only
+ *   k_scale, v_scale  binary16 bits [T][Hkv][4], read only
+ *   k_min, v_min      binary16 bits [T][Hkv][4] for INT4; ignored (may be
+ *                     NULL) for INT8
+ *   out               host buffer of at least w4a16_kv_packed_bytes bytes,
+ *                     owned by the caller, written completely
+ * Errors: bits not 8 or 4 -> W4A16_ERR_FORMAT; NULL -> W4A16_ERR_NULL; bad
+ * T/Hkv -> W4A16_ERR_SHAPE; out_bytes too small -> W4A16_ERR_SIZE.
+ */
+w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_min,
+                           const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_min, int32_t T,
+                           int32_t Hkv, void* out, size_t out_bytes);
+
+/* Bytes of the device workspace w4a16_kv_attention needs for (T, Hq) (an
+ * upper bound that holds on every device; 0 for a bad T or Hq). */
+size_t w4a16_kv_workspace_bytes(int32_t T, int32_t Hq);
+
+/*
+ * w4a16_kv_attention - o[Hq][128] for one layer and one new token.
+ *   q          device binary16 [Hq][128], 16-byte aligned (read only)
+ *   kv         device copy of a w4a16_kv_pack blob for (bits, T, Hkv),
+ *              256-byte aligned (read only)
+ *   o          device fp32 [Hq][128], 16-byte aligned, overwritten
+ *   workspace  device buffer of workspace_bytes >= w4a16_kv_workspace_bytes,
+ *              16-byte aligned, owned by the caller; no initial contents
+ *              needed; calls that share it must not run concurrently
+ *   stream     hipStream_t to enqueue on
+ * Two kernels are enqueued (the split attention pass and the merge of its
+ * partials); the call never allocates or synchronises, and results are
+ * bitwise repeatable. Errors (host side, before anything is enqueued): NULL
+ * -> W4A16_ERR_NULL; bits, T or heads out of range -> W4A16_ERR_SHAPE;
+ * misaligned pointer -> W4A16_ERR_ALIGN; workspace too small ->
+ * W4A16_ERR_SIZE; o or the workspace intersecting an input or each other ->
+ * W4A16_ERR_OVERLAP; launch rejected -> W4A16_ERR_HIP.
+ */
+w4a16_status w4a16_kv_attention(int32_t bits, const void* q, const void* kv, float* o, int32_t T, int32_t Hq,
+                                int32_t Hkv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* w4a16_kv_attention with the start and end of its split attention kernel
+ * (the dominant one; the merge kernel follows it) recorded into two
+ * caller-owned HIP events. Either event NULL -> W4A16_ERR_NULL. */
+w4a16_status w4a16_kv_attention_timed(int32_t bits, const void* q, const void* kv, float* o, int32_t T, int32_t Hq,
+                                      int32_t Hkv, void* workspace, size_t workspace_bytes, void* stream,
+                                      void* start_event, void* stop_event);
+
+/* Host only: out[0] = query heads per KV head (the kernel's template argument,
+ * kv_attn_kernel<bits, out[0]>), out[1] = blocks per workgroup, out[2] =
+ * workgroups per KV head on the current device. NULL -> W4A16_ERR_NULL; bad
+ * shape -> W4A16_ERR_SHAPE. */
+w4a16_status w4a16_kv_launch_shape(int32_t bits, int32_t T, int32_t Hq, int32_t Hkv, int32_t out[3]);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* w4a16_status_string(int32_t status);
 

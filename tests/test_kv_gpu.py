@@ -1,0 +1,118 @@
+"""GPU parity of decode attention over an INT8/INT4 KV cache, through the C ABI,
+against the fp64 oracle: |o - o_ref| <= 1e-3 * sum_t p_t |v_hat_t| + 1e-5 per
+element. Ragged token counts (partial last block, fewer blocks than waves),
+every query-heads-per-KV-head ratio, the full 8B contexts of the page's KV
+budget, a sharply peaked softmax, repeatability and workspace reuse.
+"""
+import numpy as np
+import pytest
+
+import bit_weight_quantized_w4a16_amd as w4
+import oracle
+import workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+A = oracle.kv_attention_ref
+
+
+def run_kv(bits, q, cache, ws=None):
+    T, Hkv = cache[0].shape[0], cache[0].shape[1]
+    kv = w4.upload_packed(w4.w4a16_kv_pack(bits, *cache), DEV)
+    qd = torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
+    o = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    if ws is None:
+        ws = torch.empty(w4.w4a16_kv_workspace_bytes(T, q.shape[0]) // 4, dtype=torch.float32, device=DEV)
+    w4.w4a16_kv_attention(bits, qd, kv, o, T, Hkv, ws)
+    torch.cuda.synchronize()
+    return o.cpu().numpy().astype(np.float64)
+
+
+def check(o, o_ref, B, label):
+    ok = A.within_tolerance(o, o_ref, B)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        detail = [(tuple(i), o[tuple(i)], o_ref[tuple(i)], A.tolerance(B)[tuple(i)]) for i in bad]
+        pytest.fail(f"{label}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. {detail}")
+
+
+SMALL = [
+    (8, 1, 4, 1), (8, 63, 8, 2), (8, 64, 32, 8), (8, 65, 32, 8), (8, 1000, 32, 8), (8, 5000, 16, 16),
+    (8, 777, 16, 8), (8, 3001, 64, 8), (4, 1, 1, 1), (4, 127, 16, 2), (4, 4097, 32, 8), (4, 3000, 64, 8),
+    (4, 999, 8, 8), (4, 2222, 32, 16),
+]
+
+
+@pytest.mark.parametrize("bits,T,Hq,Hkv", SMALL)
+def test_kv_small_shapes(w4a16_lib, bits, T, Hq, Hkv):
+    print(f"[kv shape] bits={bits} T={T} Hq={Hq} Hkv={Hkv}", flush=True)
+    cache = workload.kv_cache(bits, 700 + T, 0, T, Hkv)
+    q = workload.kv_query(700 + T, 0, Hq)
+    o = run_kv(bits, q, cache)
+    o_ref, B = A.attention(bits, q, *cache)
+    check(o, o_ref, B, f"bits={bits} T={T} Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_full_context_8b(w4a16_lib, bits):
+    T = workload.KV_CONTEXT[bits]
+    print(f"[kv full] bits={bits} T={T}", flush=True)
+    cache = workload.kv_cache(bits, 2, 0, T)
+    q = workload.kv_query(2, 0)
+    o = run_kv(bits, q, cache)
+    o_ref, B = A.attention(bits, q, *cache)
+    check(o, o_ref, B, f"bits={bits} T={T}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_peaked_softmax(w4a16_lib, bits):
+    """A large query scale makes a handful of tokens carry the weight: the
+    running maximum changes across blocks and workgroups."""
+    T = 3000
+    cache = workload.kv_cache(bits, 31, 0, T, 8)
+    q = (workload.kv_query(31, 0).astype(np.float32) * 12).astype(np.float16)
+    o = run_kv(bits, q, cache)
+    o_ref, B = A.attention(bits, q, *cache)
+    check(o, o_ref, B, f"peaked bits={bits}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_bitwise_repeatable_and_workspace_reuse(w4a16_lib, bits):
+    Hq = 32
+    ws = torch.empty(w4.w4a16_kv_workspace_bytes(4000, Hq) // 4, dtype=torch.float32, device=DEV)
+    c1 = workload.kv_cache(bits, 41, 0, 4000, 8)
+    q1 = workload.kv_query(41, 0)
+    a = run_kv(bits, q1, c1, ws)
+    c2 = workload.kv_cache(bits, 42, 0, 150, 8)
+    q2 = workload.kv_query(42, 0)
+    b = run_kv(bits, q2, c2, ws)        # a smaller call on the same workspace
+    again = run_kv(bits, q1, c1, ws)
+    np.testing.assert_array_equal(a, again)
+    o_ref, B = A.attention(bits, q2, *c2)
+    check(b, o_ref, B, "second call on a reused workspace")
+
+
+def test_kv_timed_matches_untimed(w4a16_lib):
+    bits, T, Hq, Hkv = 8, 2000, 32, 8
+    cache = workload.kv_cache(bits, 51, 0, T, Hkv)
+    q = workload.kv_query(51, 0)
+    kv = w4.upload_packed(w4.w4a16_kv_pack(bits, *cache), DEV)
+    qd = torch.from_numpy(q).to(DEV)
+    ws = torch.empty(w4.w4a16_kv_workspace_bytes(T, Hq) // 4, dtype=torch.float32, device=DEV)
+    o0 = torch.empty((Hq, 128), dtype=torch.float32, device=DEV)
+    o1 = torch.full((Hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream(device=DEV)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        a.record(s)
+        b.record(s)
+        w4.w4a16_kv_attention(bits, qd, kv, o0, T, Hkv, ws, s)
+        st = w4.w4a16_kv_attention_timed_raw(bits, qd.data_ptr(), kv.data_ptr(), o1.data_ptr(), T, Hq, Hkv,
+                                             ws.data_ptr(), ws.numel() * 4, s.cuda_stream, a.cuda_event,
+                                             b.cuda_event)
+    assert st == w4.W4A16_OK
+    s.synchronize()
+    assert torch.equal(o0, o1)
+    assert 0.0 < a.elapsed_time(b) < 100.0
