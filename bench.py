@@ -23,7 +23,12 @@ oracle timed on this host's cores as a reported CPU baseline.
 runs only a plain device copy of 1 GiB three times (the FETCH_SIZE /
 WRITE_SIZE scale of a kernel of known traffic). --codec q4_sym|q5|q8_sym runs
 the same step with one of the weight-code variants (separate launches only:
-the chain streams the 4-bit code) and reports it the same way.
+the chain streams the 4-bit code) and reports it the same way. --kv 8|4 runs
+the other bandwidth-bound operation of the decode step instead: attention of
+one new token over the INT8 / INT4 KV cache of all 32 layers of the 8B shape
+(32 query heads, 8 KV heads, head size 128) at the context the core-modules
+page's KV budget allows (38,863 / 77,726 tokens), one w4a16_kv_attention call
+per layer replayed from a HIP graph.
 """
 from __future__ import annotations
 
@@ -73,7 +78,20 @@ TRAFFIC = {
     "codec_kernel<1, 1, 1, 1>": 30_959_537,
     "codec_kernel<2, 1, 1, 1>": 41_217_127,
     "codec_kernel<3, 1, 1, 1>": 58_252_492,
+    # KV-cache attention, split pass: (41,499.65 / 48,768.74 KiB x 2.000 + 1,235.0 / 1,657.5 KiB x 1.000)
+    "kv_attn_kernel<8, 4>": 86_255_921,
+    "kv_attn_kernel<4, 4>": 101_575_670,
 }
+
+
+KV_METRIC = "KV-cache decode attention µs/step and effective HBM GB/s (% of peak), 8B shapes"
+
+
+def kv_layer_bytes(bits, T, Hq, Hkv):
+    """Algorithmic bytes of one layer's attention: the codes and group
+    parameters of T tokens (keys and values), q and o."""
+    per_value = {8: 1 + 2 / 32, 4: 0.5 + 4 / 32}[bits]
+    return int(round(T * Hkv * 128 * 2 * per_value)) + Hq * 128 * 2 + Hq * 128 * 4
 
 
 def copy_calibration(torch, dev):
@@ -186,6 +204,143 @@ def time_loop(torch, stream, fn, warmup, steps):
     return (time.perf_counter() - t0) / steps
 
 
+def kv_cpu_baseline(bits, T, budget_s):
+    """The fp64 attention oracle on whole layers of the same step until ~budget_s."""
+    import threadpoolctl
+
+    import oracle
+
+    done, t_total, nbytes = 0, 0.0, 0
+    Hq, Hkv = workload.KV_HQ, workload.KV_HKV
+    while t_total < budget_s and done < workload.KV_LAYERS:
+        cache = workload.kv_cache(bits, 3, done, T, Hkv)
+        q = workload.kv_query(3, done, Hq)
+        t0 = time.perf_counter()
+        with threadpoolctl.threadpool_limits(1):
+            oracle.kv_attention_ref.attention(bits, q, *cache)
+        t_total += time.perf_counter() - t0
+        nbytes += kv_layer_bytes(bits, T, Hq, Hkv)
+        done += 1
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 attention oracle (numpy) on the first {done} of the step's {workload.KV_LAYERS} layers "
+                  f"(T = {T}), {nbytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, one thread",
+    }
+
+
+def main_kv(args, torch, w4, dev):
+    bits = args.kv
+    T = workload.KV_CONTEXT[bits]
+    Hq, Hkv, L = workload.KV_HQ, workload.KV_HKV, workload.KV_LAYERS
+    t0 = time.time()
+    layers = []
+    for layer in range(L):
+        cache = workload.kv_cache(bits, 3, layer, T, Hkv)
+        q = workload.kv_query(3, layer, Hq)
+        kv = w4.upload_packed(w4.w4a16_kv_pack(bits, *cache), dev)
+        qd = torch.from_numpy(q).to(dev)
+        o = torch.zeros((Hq, 128), dtype=torch.float32, device=dev)
+        layers.append(dict(kv=kv, q=qd, o=o))
+        del cache
+    ws = torch.empty(w4.w4a16_kv_workspace_bytes(T, Hq) // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    layer_bytes = kv_layer_bytes(bits, T, Hq, Hkv)
+    step_bytes = L * layer_bytes
+    log(f"[bench] KV attention: {L} layers, INT{bits}, T={T}, {step_bytes / 1e9:.3f} GB/step, "
+        f"inputs ready in {time.time() - t0:.1f} s")
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    ptrs = [(g["q"].data_ptr(), g["kv"].data_ptr(), g["o"].data_ptr()) for g in layers]
+    wsp, wsb = ws.data_ptr(), ws.numel() * 4
+
+    def step(handle=sh):
+        for qp, kp, op in ptrs:
+            st = w4.w4a16_kv_attention_raw(bits, qp, kp, op, T, Hq, Hkv, wsp, wsb, handle)
+            if st != 0:
+                raise w4.W4A16Error(st, "w4a16_kv_attention")
+
+    with torch.cuda.stream(stream):
+        step()
+    stream.synchronize()
+    import oracle
+
+    for layer in (0, L - 1):  # sanity: sampled heads against the oracle
+        cache = workload.kv_cache(bits, 3, layer, T, Hkv)
+        heads = [0, 13, Hq - 1]
+        o_ref, B = oracle.kv_attention_ref.attention(bits, workload.kv_query(3, layer, Hq), *cache, heads=heads)
+        if not oracle.kv_attention_ref.within_tolerance(layers[layer]["o"].cpu().numpy()[heads], o_ref, B).all():
+            raise AssertionError(f"bench spot check failed on layer {layer}")
+    log("[bench] spot checks ok")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    sec = time_loop(torch, stream, graph.replay, args.warmup, args.steps)
+    log(f"[bench] KV attention step: {sec * 1e6:.1f} us")
+    marks = []
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.steps // 4)):
+            for qp, kp, op in ptrs:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                b.record(stream)
+                st = w4.w4a16_kv_attention_timed_raw(bits, qp, kp, op, T, Hq, Hkv, wsp, wsb, sh, a.cuda_event,
+                                                     b.cuda_event)
+                if st != 0:
+                    raise w4.W4A16Error(st, "w4a16_kv_attention_timed")
+                marks.append((a, b))
+    torch.cuda.synchronize()
+    avg_us = sum(a.elapsed_time(b) for a, b in marks) / len(marks) * 1e3
+    shape = w4.w4a16_kv_launch_shape(bits, T, Hq, Hkv)
+    kernel = shape["kernel"]
+    achieved = layer_bytes / (avg_us * 1e-6) / 1e9
+    log(f"[bench] {kernel}: avg {avg_us:.2f} us per launch, {layer_bytes / 1e6:.2f} MB, {achieved:.1f} GB/s")
+    value = step_bytes / sec / 1e9
+    line = {
+        "metric": KV_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "us_per_step": round(sec * 1e6, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"i{bits}xf16->f32" if bits == 8 else "u4xf16->f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"llama8b_kv_int{bits}: one new token's attention over 32 layers x (32 query heads, "
+                        f"8 KV heads, head size 128), INT{bits} KV cache of {T} tokens, group-32 fp16 parameters",
+            "layers": L,
+            "tokens": T,
+            "bytes_per_step": step_bytes,
+            "launch": f"{L} w4a16_kv_attention calls per step ({kernel} + {shape['merge_kernel']}), "
+                      f"replayed from a HIP graph",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": TRAFFIC.get(kernel),
+            "avg_launch_us": round(avg_us, 3),
+            "bytes_per_launch": layer_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on host cores ...")
+        line["cpu_baseline"] = kv_cpu_baseline(bits, T, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +353,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time separate launches eagerly (counter runs)")
     ap.add_argument("--codec", choices=list(CODEC_BITS), default="q4",
                     help="weight code of the step (the chain runs the 4-bit code only)")
+    ap.add_argument("--kv", type=int, choices=[8, 4], default=None,
+                    help="bench decode attention over an INT8 / INT4 KV cache instead of the GEMVs")
     args = ap.parse_args()
     codec = args.codec
     if codec != "q4":
@@ -222,6 +379,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(torch, dev)
+        return
+    if args.kv is not None:
+        main_kv(args, torch, w4, dev)
         return
     M = 1
 

@@ -319,23 +319,62 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
   }
 }
 
-// One workgroup per query head h, one thread per dim: merge the S partials of
-// h's KV head in order and normalise.
+// One workgroup of 512 threads per query head h: merge the S partials of h's
+// KV head. The maximum is a reduction over all threads; the weighted sums are
+// split into 4 fixed slices of the partials (slice k takes s = k, k+4, ...),
+// each thread summing one dim of one slice with its loads issued 8 at a
+// time, and the slices are added in order 0..3: a fixed summation order.
+constexpr int kMergeThreads = 512, kMergeSlices = kMergeThreads / kD, kMergeUnroll = 8;
+static_assert(kMergeSlices == 4, "the final sum below adds four slices");
+
 template <int GQ>
-__global__ void __launch_bounds__(kD) kv_combine_kernel(const float* __restrict__ part, float* __restrict__ o, int S) {
-  const int h = blockIdx.x, d = threadIdx.x;
+__global__ void __launch_bounds__(kMergeThreads) kv_combine_kernel(const float* __restrict__ part, float* __restrict__ o,
+                                                                  int S) {
+  const int h = blockIdx.x;
   const int g = h / GQ, j = h % GQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = tid % kD, k = tid / kD;
   const float* p = part + (size_t(g * S) * GQ + j) * kPartFloats;
   const size_t stride = size_t(GQ) * kPartFloats;
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float accs[kMergeSlices][kD];
+  __shared__ float lss[kMergeSlices];
+
   float mx = -__builtin_inff();
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p[s * stride + kD]);
+  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, p[s * stride + kD]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
+
   float a = 0.f, ls = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float f = __builtin_amdgcn_exp2f(p[s * stride + kD] - mx);
-    a = __builtin_fmaf(f, p[s * stride + d], a);
-    ls = __builtin_fmaf(f, p[s * stride + kD + 1], ls);
+  for (int s0 = k; s0 < S; s0 += kMergeSlices * kMergeUnroll) {
+    float mv[kMergeUnroll], av[kMergeUnroll], lv[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {  // clamped, unconditional loads
+      const int s = s0 + kMergeSlices * u;
+      const size_t c = size_t(s < S ? s : 0) * stride;  // partial 0 always exists (S >= 1)
+      mv[u] = p[c + kD];
+      av[u] = p[c + d];
+      lv[u] = p[c + kD + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float f = s0 + kMergeSlices * u < S ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
+      a = __builtin_fmaf(f, av[u], a);
+      ls = __builtin_fmaf(f, lv[u], ls);
+    }
   }
-  o[size_t(h) * kD + d] = a / ls;
+  accs[k][d] = a;
+  if (d == 0) lss[k] = ls;
+  __syncthreads();
+  if (k == 0) {
+    const float num = (accs[0][d] + accs[1][d]) + (accs[2][d] + accs[3][d]);
+    const float den = (lss[0] + lss[1]) + (lss[2] + lss[3]);
+    o[size_t(h) * kD + d] = num / den;
+  }
 }
 
 typedef void (*attn_fn)(const uint32_t*, const uint8_t*, float*, int, int, int, float);
@@ -428,7 +467,7 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
     return W4A16_ERR_HIP;
   const float* cp = pp;
   void* a2[] = {&cp, &o, &s_arg};
-  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fc), dim3(Hq), dim3(kD), a2, 0, st, nullptr, nullptr, 0) !=
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fc), dim3(Hq), dim3(kMergeThreads), a2, 0, st, nullptr, nullptr, 0) !=
       hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
