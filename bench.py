@@ -78,9 +78,9 @@ TRAFFIC = {
     "codec_kernel<1, 1, 1, 1>": 30_959_537,
     "codec_kernel<2, 1, 1, 1>": 41_217_127,
     "codec_kernel<3, 1, 1, 1>": 58_252_492,
-    # KV-cache attention, split pass: (41,499.65 / 48,768.74 KiB x 2.000 + 1,235.0 / 1,657.5 KiB x 1.000)
-    "kv_attn_kernel<8, 4>": 86_255_921,
-    "kv_attn_kernel<4, 4>": 101_575_670,
+    # KV-cache attention, split pass: (41,497.15 / 48,749.27 KiB x 2.000 + 1,235.0 / 1,657.5 KiB x 1.000)
+    "kv_attn_kernel<8, 4>": 86_250_813,
+    "kv_attn_kernel<4, 4>": 101_535_791,
 }
 
 

@@ -148,8 +148,8 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
   const int b0 = split * bpw;
   const int b1 = min(b0 + bpw, nb);
 
-  __shared__ __attribute__((aligned(16))) float wbuf[kWaves][GQ][4][kBlockTokens];  // p * s_v per (head, group, token)
-  __shared__ __attribute__((aligned(16))) float zbuf[BITS == 4 ? kWaves : 1][GQ][4][kBlockTokens];  // p * m_v (INT4)
+  // binary16 token weights p * s_v * 2^E per (wave, head, value group, slot)
+  __shared__ __attribute__((aligned(16))) _Float16 wh[kWaves][GQ][4][kBlockTokens];
   __shared__ float comb[kWaves][GQ][kPartFloats];
 
   // per-group sums of each query head (the offset / min terms of the score)
@@ -166,15 +166,25 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     }
   }
 
-  float m[GQ], l[GQ], acc[GQ][2], zs[GQ];
+  // Running state per query head j: the maximum m (uniform, exp2 domain) and,
+  // in real units, l (the weight sum of this lane's tokens), acc (the weighted
+  // values of this lane's two dims) and off[grp] (the offset / min term of
+  // this lane's tokens for value group grp).
+  float m[GQ], l[GQ], acc[GQ][2], off[GQ][4];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     m[j] = -__builtin_inff();
     l[j] = 0.f;
     acc[j][0] = acc[j][1] = 0.f;
-    zs[j] = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) off[j][grp] = 0.f;
   }
   const int vgrp = lane >> 4;  // group of this lane's two dims in phase 2
+  // slot of this lane's token in a row of binary16 weights: INT8 keeps token
+  // order (dword k = tokens 2k, 2k+1, the pair a value word forms); INT4
+  // stores each 4-token group as (t0, t2, t1, t3), the pairs its value bytes
+  // form under the nibble masks
+  const int wpos = BITS == 8 ? lane : (lane & ~3) | ((lane & 1) << 1) | ((lane >> 1) & 1);
 
   for (int b = b0 + wave; b < b1; b += kWaves) {
     const uint8_t* rec = kv + (size_t(g) * nb + b) * R::kBytes;
@@ -196,6 +206,22 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
       vp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVPar) + lane);
     }
     static_assert(kKPar * kBlockTokens == 512 || kKPar * kBlockTokens == 1024, "parameter layout");
+    float vs[4], vm[4];  // this lane's token's value scales (and mins)
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      if constexpr (BITS == 8) {
+        vs[grp] = (grp & 1) ? half_hi(elem(vp, grp >> 1)) : half_lo(elem(vp, grp >> 1));
+        vm[grp] = 0.f;
+      } else {
+        vs[grp] = half_lo(elem(vp, grp));
+        vm[grp] = half_hi(elem(vp, grp));
+      }
+    }
+    // block scale 2^E: every |p * s_v| * 2^E stays below 2^14, so the binary16
+    // weights are normal numbers down to 2^-28 of the block's largest scale
+    float smax = fmaxf(fmaxf(fabsf(vs[0]), fabsf(vs[1])), fmaxf(fabsf(vs[2]), fabsf(vs[3])));
+    smax = wave_max(smax);
+    const int E = 14 - (smax > 0.f ? __builtin_amdgcn_frexp_expf(smax) : 0);
 
     // phase 1: one lane per token
     const bool valid = b * kBlockTokens + lane < T;
@@ -210,86 +236,91 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
       l[j] = __builtin_fmaf(l[j], corr, p);
       acc[j][0] *= corr;
       acc[j][1] *= corr;
-      zs[j] *= corr;
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
+        // the token's weight p * s_v, rounded to binary16 at scale 2^E; the
+        // offset / min term is formed from the same rounded weight, so the
+        // rounding only perturbs each token's weight by 2^-11 relative
+        const float ps = p * vs[grp];
+        const _Float16 h = _Float16(__builtin_ldexpf(ps, E));
+        const float wr = __builtin_ldexpf(float(h), -E);
         if constexpr (BITS == 8) {
-          const uint32_t w = elem(vp, grp >> 1);
-          wbuf[wave][j][grp][lane] = p * ((grp & 1) ? half_hi(w) : half_lo(w));
+          off[j][grp] = __builtin_fmaf(off[j][grp], corr, -128.f * wr);
         } else {
-          const uint32_t w = elem(vp, grp);
-          wbuf[wave][j][grp][lane] = p * half_lo(w);
-          zbuf[wave][j][grp][lane] = p * half_hi(w);
+          const float fix = vs[grp] != 0.f ? (wr - ps) * (vm[grp] * __builtin_amdgcn_rcpf(vs[grp])) : 0.f;
+          off[j][grp] = __builtin_fmaf(off[j][grp], corr, __builtin_fmaf(p, vm[grp], fix));
         }
+        wh[wave][j][grp][wpos] = h;
       }
     }
     wave_lds_sync();  // phase 2 reads the weights other lanes wrote
 
-    // phase 2: one lane per two dims (2*lane, 2*lane + 1)
+    // phase 2: one lane per two dims (2*lane, 2*lane + 1); the value codes are
+    // binary16 subnormal pairs over two tokens, dotted with the weight pairs
     if constexpr (BITS == 8) {
+      float blk[GQ][2];
 #pragma unroll
-      for (int c = 0; c < R::kVLoads; ++c) {  // tokens 8c .. 8c+7
-        float x[8][2];
+      for (int j = 0; j < GQ; ++j) blk[j][0] = blk[j][1] = 0.f;
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t w = elem(vc[c], wd);  // tokens 2wd, 2wd+1: bytes (t0 d0, t0 d1, t1 d0, t1 d1)
-          x[2 * wd][0] = byte_f(w, 0) - 128.f;
-          x[2 * wd][1] = byte_f(w, 1) - 128.f;
-          x[2 * wd + 1][0] = byte_f(w, 2) - 128.f;
-          x[2 * wd + 1][1] = byte_f(w, 3) - 128.f;
-        }
+      for (int c = 0; c < R::kVLoads; ++c) {  // tokens 8c .. 8c+7; word wd = tokens 8c+2wd, +1
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
-          const float4 wa = *reinterpret_cast<const float4*>(&wbuf[wave][j][vgrp][8 * c]);
-          const float4 wb = *reinterpret_cast<const float4*>(&wbuf[wave][j][vgrp][8 * c + 4]);
-          const float wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+          const u32x4 wp = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][8 * c]);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            acc[j][0] = __builtin_fmaf(wt[t], x[t][0], acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wt[t], x[t][1], acc[j][1]);
+          for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t w = elem(vc[c], wd);  // bytes (t0 d0, t0 d1, t1 d0, t1 d1), each q + 128
+            blk[j][0] = dot2(w & 0x00FF00FFu, elem(wp, wd), blk[j][0]);
+            blk[j][1] = dot2((w >> 8) & 0x00FF00FFu, elem(wp, wd), blk[j][1]);
           }
         }
       }
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) {  // codes were q + 128 times 2^-24, weights times 2^E
+        acc[j][0] = __builtin_fmaf(blk[j][0], __builtin_ldexpf(1.f, 24 - E), acc[j][0]);
+        acc[j][1] = __builtin_fmaf(blk[j][1], __builtin_ldexpf(1.f, 24 - E), acc[j][1]);
+      }
     } else {
+      float lo[GQ], hi[GQ];
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) lo[j] = hi[j] = 0.f;
 #pragma unroll
       for (int c = 0; c < R::kVLoads; ++c) {  // tokens 16c .. 16c+15
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {      // tokens 16c + 4wd + i, byte i: (low nibble d0, high nibble d1)
-          const uint32_t w = elem(vc[c], wd);
-          const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-          float x0[4], x1[4];
+        for (int j = 0; j < GQ; ++j) {
+          const u32x4 wa = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][16 * c]);
+          const u32x4 wb = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][16 * c + 8]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x0[i] = byte_f(lo, i);
-            x1[i] = byte_f(hi, i);
-          }
-#pragma unroll
-          for (int j = 0; j < GQ; ++j) {
-            const int t0 = 16 * c + 4 * wd;
-            const float4 wt = *reinterpret_cast<const float4*>(&wbuf[wave][j][vgrp][t0]);
-            const float4 zt = *reinterpret_cast<const float4*>(&zbuf[wave][j][vgrp][t0]);
-            acc[j][0] = __builtin_fmaf(wt.x, x0[0], acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wt.x, x1[0], acc[j][1]);
-            acc[j][0] = __builtin_fmaf(wt.y, x0[1], acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wt.y, x1[1], acc[j][1]);
-            acc[j][0] = __builtin_fmaf(wt.z, x0[2], acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wt.z, x1[2], acc[j][1]);
-            acc[j][0] = __builtin_fmaf(wt.w, x0[3], acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wt.w, x1[3], acc[j][1]);
-            zs[j] += (zt.x + zt.y) + (zt.z + zt.w);
+          for (int wd = 0; wd < 4; ++wd) {  // tokens 16c + 4wd + i in byte i: (low nibble d0, high nibble d1)
+            const uint32_t w = elem(vc[c], wd), w8 = w >> 8;
+            const uint32_t p02 = wd < 2 ? elem(wa, 2 * wd) : elem(wb, 2 * wd - 4);      // weights (t0, t2)
+            const uint32_t p13 = wd < 2 ? elem(wa, 2 * wd + 1) : elem(wb, 2 * wd - 3);  // weights (t1, t3)
+            lo[j] = dot2(w & 0x000F000Fu, p02, lo[j]);
+            hi[j] = dot2(w & 0x00F000F0u, p02, hi[j]);
+            lo[j] = dot2(w8 & 0x000F000Fu, p13, lo[j]);
+            hi[j] = dot2(w8 & 0x00F000F0u, p13, hi[j]);
           }
         }
+      }
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) {  // dim d0 in units of 2^-24, d1 of 2^-20, weights times 2^E
+        acc[j][0] = __builtin_fmaf(lo[j], __builtin_ldexpf(1.f, 24 - E), acc[j][0]);
+        acc[j][1] = __builtin_fmaf(hi[j], __builtin_ldexpf(1.f, 20 - E), acc[j][1]);
       }
     }
     wave_lds_sync();  // the next block's phase 1 overwrites the weights just read
   }
 
-  // this wave's partial: maximum (uniform), weight sum, weighted values
+  // this wave's partial: maximum (uniform), weight sum, weighted values; the
+  // offset / min terms of the value groups are summed over the wave's tokens
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     const float lsum = wave_sum(l[j]);
-    comb[wave][j][2 * lane] = acc[j][0] + zs[j];
-    comb[wave][j][2 * lane + 1] = acc[j][1] + zs[j];
+    float o4[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) o4[grp] = wave_sum(off[j][grp]);
+    const float oq = vgrp == 0 ? o4[0] : vgrp == 1 ? o4[1] : vgrp == 2 ? o4[2] : o4[3];
+    comb[wave][j][2 * lane] = acc[j][0] + oq;
+    comb[wave][j][2 * lane + 1] = acc[j][1] + oq;
     if (lane == 0) {
       comb[wave][j][kD] = m[j];
       comb[wave][j][kD + 1] = lsum;
