@@ -24,8 +24,16 @@ consecutive k of one row with binary16 parameters, as for the 4-bit code:
              into 5 bits is the library's business).
 * ``q8_sym`` ``w_hat = s * q``,       q signed 8-bit (-128..127, two's
              complement), codes ``int8[N, K]`` (passed as their bytes).
+* ``pal4``   ``w_hat = lut[n, q]``,   q unsigned 4-bit, same code bytes as
+             ``q4``; a 16-entry binary16 palette per output row (Core ML's
+             palettisation, named in the core-modules page's runtime table,
+             section 5.2, read at per-channel granularity: one lookup table
+             per row, since a table per group of 32 weights would cost more
+             bytes than the weights it encodes).
 
-s and m are binary16 ``[N, K/32]``; the symmetric codecs have no m.
+s and m are binary16 ``[N, K/32]``; the symmetric codecs have no m. For
+``pal4`` the ``scale`` argument carries the palettes, binary16 ``[N, 16]``,
+and there is no m.
 
 What is computed: y[m, n] = sum_k w_hat[n, k] * x[m, k] and the tolerance scale
 B[m, n] = sum_k |w_hat[n, k] * x[m, k]|, in fp64, with the same pass rule
@@ -37,7 +45,8 @@ Parity status: the pages print no worked values for any codec. The pins are
 exact rational brute force, hand-derived golden fixtures under tests/golden/,
 closed forms, and special cases that reduce to the pinned 4-bit group-affine
 oracle (q4_sym is q4 with m = -8 s; q5 with codes below 16 is q4; q8_sym with
-codes 0..15 is q4 with m = 0).
+codes 0..15 is q4 with m = 0; pal4 with an affine palette s*c + m is q4 with
+that scale and min).
 """
 from __future__ import annotations
 
@@ -46,10 +55,11 @@ import concurrent.futures as _cf
 import numpy as np
 
 GROUP = 32
-CODECS = ("q4", "q4_sym", "q5", "q8_sym")
-SYMMETRIC = {"q4": False, "q4_sym": True, "q5": False, "q8_sym": True}
+CODECS = ("q4", "q4_sym", "q5", "q8_sym", "pal4")
+SYMMETRIC = {"q4": False, "q4_sym": True, "q5": False, "q8_sym": True, "pal4": True}  # True: no min array
 # code bytes per weight in the canonical (unpacked) layout
-_CODE_BYTES_PER_K = {"q4": 0.5, "q4_sym": 0.5, "q5": 1.0, "q8_sym": 1.0}
+_CODE_BYTES_PER_K = {"q4": 0.5, "q4_sym": 0.5, "q5": 1.0, "q8_sym": 1.0, "pal4": 0.5}
+PALETTE = 16
 
 
 def code_shape(codec: str, N: int, K: int):
@@ -64,7 +74,7 @@ def _check(codec, codes, scale, mn):
         raise ValueError(f"unknown codec {codec!r}")
     codes = np.asarray(codes)
     N = codes.shape[0]
-    if codec in ("q4", "q4_sym"):
+    if codec in ("q4", "q4_sym", "pal4"):
         if codes.dtype != np.uint8:
             raise TypeError("4-bit codes must be uint8 [N, K/2]")
         K = 2 * codes.shape[1]
@@ -80,6 +90,10 @@ def _check(codec, codes, scale, mn):
         K = codes.shape[1]
     if K % GROUP or K <= 0:
         raise ValueError("K must be a positive multiple of 32")
+    if codec == "pal4":
+        if np.asarray(scale).shape != (N, PALETTE):
+            raise ValueError("the palettes must be [N, 16]")
+        return N, K
     if np.asarray(scale).shape != (N, K // GROUP):
         raise ValueError("scale must be [N, K/32]")
     if not SYMMETRIC[codec] and (mn is None or np.asarray(mn).shape != (N, K // GROUP)):
@@ -90,7 +104,7 @@ def _check(codec, codes, scale, mn):
 def unpack(codec: str, codes) -> np.ndarray:
     """Canonical codes -> int64 [N, K] code values q (before the affine map)."""
     codes = np.asarray(codes)
-    if codec in ("q4", "q4_sym"):
+    if codec in ("q4", "q4_sym", "pal4"):
         q = np.empty((codes.shape[0], 2 * codes.shape[1]), dtype=np.int64)
         q[:, 0::2] = codes & 0x0F
         q[:, 1::2] = codes >> 4
@@ -105,6 +119,10 @@ def unpack(codec: str, codes) -> np.ndarray:
 def dequantise(codec: str, codes, scale, mn=None) -> np.ndarray:
     """w_hat in fp64 (exact) for one of CODECS."""
     _check(codec, codes, scale, mn)
+    if codec == "pal4":  # w_hat[n, k] = lut[n, q[n, k]]
+        q = unpack(codec, codes)
+        lut = np.asarray(scale).astype(np.float64)
+        return np.take_along_axis(lut, q, axis=1)
     q = unpack(codec, codes).astype(np.float64)
     s = np.repeat(np.asarray(scale).astype(np.float64), GROUP, axis=1)
     if codec == "q4_sym":

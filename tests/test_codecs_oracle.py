@@ -34,7 +34,7 @@ def _golden():
         return json.load(f)
 
 
-@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym"])
+@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym", "pal4"])
 def test_golden_tiny_examples(codec):
     fx = _golden()
     case = fx["cases"][codec]
@@ -51,9 +51,9 @@ def test_golden_tiny_examples(codec):
 
 def _code_value(codec, codes, n, k):
     """The code of weight (n, k), decoded from the raw bytes with integer arithmetic."""
-    if codec == "q4_sym":
+    if codec in ("q4_sym", "pal4"):
         hi, lo = divmod(int(codes[n, k // 2]), 16)
-        return (hi if k % 2 else lo) - 8
+        return (hi if k % 2 else lo) - (8 if codec == "q4_sym" else 0)
     if codec == "q5":
         return int(codes[n, k])
     b = int(np.asarray(codes[n, k]).view(np.uint8))
@@ -67,7 +67,10 @@ def _exact(codec, x, codes, scale, mn):
     B = [[Fraction(0)] * N for _ in range(M)]
     for n in range(N):
         for k in range(K):
-            w = Fraction(float(scale[n, k // 32])) * _code_value(codec, codes, n, k)
+            if codec == "pal4":  # palette entry of the code
+                w = Fraction(float(scale[n, _code_value(codec, codes, n, k)]))
+            else:
+                w = Fraction(float(scale[n, k // 32])) * _code_value(codec, codes, n, k)
             if mn is not None:
                 w += Fraction(float(mn[n, k // 32]))
             for m in range(M):
@@ -77,7 +80,7 @@ def _exact(codec, x, codes, scale, mn):
     return y, B
 
 
-@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym"])
+@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym", "pal4"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (8, 5, 96)])
 def test_exact_rational_bruteforce(codec, M, N, K):
     x, codes, scale, mn = workload.random_codec_problem(codec, 7, M, N, K)
@@ -129,6 +132,23 @@ def test_q8_sym_small_codes_is_q4_with_zero_min(M, N, K):
     np.testing.assert_array_equal(B, B4)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 7, 64), (3, 33, 512)])
+def test_pal4_affine_palette_is_q4(M, N, K):
+    """A palette lut[n][c] = s_n * c + m_n (exact in binary16) is the 4-bit
+    group-affine code with that scale and min in every group of row n."""
+    x, codes, _, _ = workload.random_codec_problem("pal4", 12, M, N, K)
+    rng = np.random.default_rng(3)
+    s = rng.integers(1, 8, size=N).astype(np.float64) / 64.0     # a few mantissa bits: s*c + m exact
+    m = -rng.integers(0, 32, size=N).astype(np.float64) / 16.0
+    lut = (s[:, None] * np.arange(16)[None, :] + m[:, None]).astype(np.float16)
+    assert np.array_equal(lut.astype(np.float64), s[:, None] * np.arange(16)[None, :] + m[:, None])
+    G = K // 32
+    y, B = C.gemv("pal4", x, codes, lut)
+    y4, B4 = oracle.gemv(x, codes, np.repeat(s[:, None], G, 1).astype(np.float16), np.repeat(m[:, None], G, 1).astype(np.float16))
+    np.testing.assert_array_equal(y, y4)
+    np.testing.assert_array_equal(B, B4)
+
+
 def _group_sums(x):
     M, K = x.shape
     return x.astype(np.float64).reshape(M, K // 32, 32).sum(axis=2)
@@ -174,7 +194,7 @@ def test_q5_fifth_bit_split():
     assert (h <= 1).all() and h.any()
 
 
-@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym"])
+@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym", "pal4"])
 def test_one_hot_x_selects_single_weight(codec):
     N, K = 6, 96
     _, codes, scale, mn = workload.random_codec_problem(codec, 9, 1, N, K)
@@ -183,7 +203,10 @@ def test_one_hot_x_selects_single_weight(codec):
         x[0, k] = 1.0
         y, B = C.gemv(codec, x, codes, scale, mn)
         for n in range(N):
-            w = float(scale[n, k // 32]) * _code_value(codec, codes, n, k)
+            if codec == "pal4":
+                w = float(scale[n, _code_value(codec, codes, n, k)])
+            else:
+                w = float(scale[n, k // 32]) * _code_value(codec, codes, n, k)
             if mn is not None:
                 w += float(mn[n, k // 32])
             assert y[0, n] == w and B[0, n] == abs(w)
@@ -200,13 +223,15 @@ def test_rejects_bad_inputs():
         C.gemv("q8_sym", x, np.zeros((2, 64), np.uint8), s)
     with pytest.raises(ValueError):
         C.gemv("q5", x, np.zeros((2, 64), np.uint8), s, None)
+    with pytest.raises(ValueError):   # a palette must have 16 entries per row
+        C.gemv("pal4", x, np.zeros((2, 32), np.uint8), s)
 
 
 def test_codec_workload_recipe():
     for codec in workload.CODECS:
         codes, scale, mn = workload.codec_weights(codec, 2, 0, 0, 8, 64)
         assert codes.shape == C.code_shape(codec, 8, 64)
-        assert scale.shape == (8, 2) and scale.dtype == np.float16
+        assert scale.shape == ((8, 16) if codec == "pal4" else (8, 2)) and scale.dtype == np.float16
         assert (mn is None) == C.SYMMETRIC[codec]
     q4 = workload.codec_weights("q4", 2, 0, 0, 8, 64)
     base = workload.weights(2, 0, 0, 8, 64)

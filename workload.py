@@ -134,10 +134,13 @@ def gemv_inputs(name: str, layer: int, proj: int, M: int):
 # canonical code array per codec is
 #   "q4", "q4_sym": uniform random bytes uint8[N, K/2] (two uniform 4-bit codes);
 #   "q5":           uniform integers 0..31, uint8[N, K] (one code per byte);
-#   "q8_sym":       uniform integers -128..127, int8[N, K].
+#   "q8_sym":       uniform integers -128..127, int8[N, K];
+#   "pal4":         uniform random bytes uint8[N, K/2], and per row a palette
+#                   of 16 values U[-0.08, 0.07] sorted, -> binary16 [N, 16]
+#                   (passed in the place of the scales).
 # Scale and min are the same draws as for the 4-bit code; the symmetric codecs
 # take no min (None). Codes of the variants use their own seed keys.
-CODECS = ("q4", "q4_sym", "q5", "q8_sym")
+CODECS = ("q4", "q4_sym", "q5", "q8_sym", "pal4")
 
 
 def codec_weights(codec: str, wid: int, layer: int, proj: int, N: int, K: int):
@@ -151,8 +154,11 @@ def codec_weights(codec: str, wid: int, layer: int, proj: int, N: int, K: int):
         codes = r.integers(0, 32, size=(N, K), dtype=np.uint8)
     elif codec == "q8_sym":
         codes = r.integers(-128, 128, size=(N, K), dtype=np.int8)
-    elif codec == "q4_sym":
+    elif codec in ("q4_sym", "pal4"):
         codes = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    if codec == "pal4":
+        lut = np.sort(_rng(wid, layer, proj, _T_SCALE + 8 * ci).uniform(-0.08, 0.07, size=(N, 16)), axis=1)
+        return codes, lut.astype(np.float16), None
     return codes, scale, (None if codec in ("q4_sym", "q8_sym") else mn)
 
 
