@@ -52,18 +52,21 @@ WORKLOAD = "llama8b_step"
 
 
 # code bits per weight and parameter bytes per group of 32 weights, per codec
-CODEC_BITS = {"q4": (4, 4), "q4_sym": (4, 2), "q5": (5, 4), "q8_sym": (8, 2)}
-CODEC_DTYPE = {"q4": "u4xf16->f32", "q4_sym": "u4xf16->f32", "q5": "u5xf16->f32", "q8_sym": "i8xf16->f32"}
+CODEC_BITS = {"q4": (4, 4), "q4_sym": (4, 2), "q5": (5, 4), "q8_sym": (8, 2), "pal4": (4, 0)}
+CODEC_DTYPE = {"q4": "u4xf16->f32", "q4_sym": "u4xf16->f32", "q5": "u5xf16->f32", "q8_sym": "i8xf16->f32",
+               "pal4": "u4xf16->f32"}
 CODEC_TEXT = {"q4": "4-bit codes, group 32, fp16 scale+min",
               "q4_sym": "symmetric 4-bit codes (s*(q-8)), group 32, fp16 scale",
               "q5": "5-bit codes, group 32, fp16 scale+min",
-              "q8_sym": "symmetric 8-bit codes (s*q, int8), group 32, fp16 scale"}
+              "q8_sym": "symmetric 8-bit codes (s*q, int8), group 32, fp16 scale",
+              "pal4": "palettised 4-bit codes (a 16-entry fp16 palette per row)"}
 
 
 def gemv_bytes(M, N, K, codec="q4"):
     """Algorithmic bytes of one GEMV: codes, per-group parameters, x and y."""
     bits, par = CODEC_BITS[codec]
-    return N * K * bits // 8 + par * N * (K // 32) + 2 * M * K + 4 * M * N
+    palettes = 32 * N if codec == "pal4" else 0  # 16 binary16 entries per row
+    return N * K * bits // 8 + par * N * (K // 32) + palettes + 2 * M * K + 4 * M * N
 
 
 # HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
@@ -78,6 +81,8 @@ TRAFFIC = {
     "codec_kernel<1, 1, 1, 1>": 30_959_537,
     "codec_kernel<2, 1, 1, 1>": 41_217_127,
     "codec_kernel<3, 1, 1, 1>": 58_252_492,
+    # palettised codes: (13,826.38 KiB x 2.000 + 61.34 KiB x 1.000)
+    "codec_kernel<4, 1, 1, 1>": 28_379_234,
     # KV-cache attention, split pass: (41,497.15 / 48,749.27 KiB x 2.000 + 1,235.0 / 1,657.5 KiB x 1.000)
     "kv_attn_kernel<8, 4>": 86_250_813,
     "kv_attn_kernel<4, 4>": 101_535_791,

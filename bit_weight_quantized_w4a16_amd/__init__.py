@@ -25,7 +25,7 @@ W4A16_ERR_HIP = 6
 W4A16_ERR_FORMAT = 7
 
 # weight-code variants (enum w4a16_codec)
-CODEC_IDS = {"q4": 0, "q4_sym": 1, "q5": 2, "q8_sym": 3}
+CODEC_IDS = {"q4": 0, "q4_sym": 1, "q5": 2, "q8_sym": 3, "pal4": 4}
 
 # every symbol include/w4a16.h declares
 EXPORTS = (
@@ -326,17 +326,17 @@ def w4a16_codec_pack(codec, codes: np.ndarray, scale: np.ndarray, mn: np.ndarray
 
     codes: uint8[N, K/2] for the 4-bit codecs, uint8[N, K] (values < 32) for
     "q5", int8[N, K] for "q8_sym"; scale (and min, affine codecs only)
-    float16[N, K/32].
+    float16[N, K/32]; for "pal4" scale carries the palettes, float16[N, 16].
     """
     cid = codec_id(codec)
     codes = np.ascontiguousarray(codes)
     if codes.dtype not in (np.uint8, np.int8):
         raise TypeError("codes must be uint8 or int8")
     N = codes.shape[0]
-    K = codes.shape[1] * (2 if cid in (0, 1) else 1)
+    K = codes.shape[1] * (2 if cid in (0, 1, 4) else 1)
     scale = np.ascontiguousarray(scale, dtype=np.float16)
-    if scale.shape != (N, K // 32):
-        raise ValueError("scale must be [N, K/32]")
+    if scale.shape != ((N, 16) if cid == 4 else (N, K // 32)):
+        raise ValueError("scale must be [N, K/32] ([N, 16] palettes for pal4)")
     mp = None
     if mn is not None:
         mn = np.ascontiguousarray(mn, dtype=np.float16)

@@ -19,6 +19,7 @@ UNITS = [
     ("csrc/w4a16_codec_kernels.hip", ["-DW4A16_CODEC_ID=1"]),
     ("csrc/w4a16_codec_kernels.hip", ["-DW4A16_CODEC_ID=2"]),
     ("csrc/w4a16_codec_kernels.hip", ["-DW4A16_CODEC_ID=3"]),
+    ("csrc/w4a16_codec_kernels.hip", ["-DW4A16_CODEC_ID=4"]),
     ("csrc/w4a16_codec.cpp", []),
     ("csrc/w4a16_kv.hip", []),
     ("csrc/w4a16_pack.cpp", []),

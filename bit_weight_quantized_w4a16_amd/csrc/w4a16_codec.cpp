@@ -15,7 +15,7 @@ constexpr int kMaxM = 8;
 
 w4a16_status codec_enqueue(int32_t codec, const void* x, const void* packed, float* y, int32_t M, int32_t N,
                            int32_t K, void* stream, hipEvent_t start, hipEvent_t stop) {
-  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return W4A16_ERR_FORMAT;
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_PAL4) return W4A16_ERR_FORMAT;
   if (codec == W4A16_CODEC_Q4) {
     if (start || stop) return w4a16_gemv_timed(x, packed, y, M, N, K, stream, start, stop);
     return w4a16_gemv(x, packed, y, M, N, K, stream);
@@ -35,7 +35,8 @@ w4a16_status codec_enqueue(int32_t codec, const void* x, const void* packed, flo
   switch (codec) {
     case W4A16_CODEC_Q4_SYM: return w4a16_codecs::enqueue_q4_sym(l, reg);
     case W4A16_CODEC_Q5: return w4a16_codecs::enqueue_q5(l, reg);
-    default: return w4a16_codecs::enqueue_q8_sym(l, reg);
+    case W4A16_CODEC_Q8_SYM: return w4a16_codecs::enqueue_q8_sym(l, reg);
+    default: return w4a16_codecs::enqueue_pal4(l, reg);
   }
 }
 
@@ -56,13 +57,14 @@ extern "C" w4a16_status w4a16_codec_gemv_timed(int32_t codec, const void* x, con
 
 extern "C" w4a16_status w4a16_codec_launch_shape(int32_t codec, int32_t M, int32_t N, int32_t K, int32_t out[3]) {
   if (!out) return W4A16_ERR_NULL;
-  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return W4A16_ERR_FORMAT;
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_PAL4) return W4A16_ERR_FORMAT;
   if (codec == W4A16_CODEC_Q4) return w4a16_launch_shape(M, N, K, out);
   w4a16_codecs::Regions reg;
   if (M < 1 || M > kMaxM || K > w4a16_max_k(M) || !w4a16_codecs::regions(codec, N, K, reg)) return W4A16_ERR_SHAPE;
   switch (codec) {
     case W4A16_CODEC_Q4_SYM: return w4a16_codecs::shape_q4_sym(M, K, out);
     case W4A16_CODEC_Q5: return w4a16_codecs::shape_q5(M, K, out);
-    default: return w4a16_codecs::shape_q8_sym(M, K, out);
+    case W4A16_CODEC_Q8_SYM: return w4a16_codecs::shape_q8_sym(M, K, out);
+    default: return w4a16_codecs::shape_pal4(M, K, out);
   }
 }

@@ -32,13 +32,15 @@ struct Launch {
   hipEvent_t start, stop;
 };
 
-// Enqueue one GEMV of codec 1, 2 or 3, or report its launch shape
+// Enqueue one GEMV of codec 1, 2, 3 or 4, or report its launch shape
 // (groups per lane, waves, passes) through `shape`.
 w4a16_status enqueue_q4_sym(const Launch& l, const Regions& r);
 w4a16_status enqueue_q5(const Launch& l, const Regions& r);
 w4a16_status enqueue_q8_sym(const Launch& l, const Regions& r);
+w4a16_status enqueue_pal4(const Launch& l, const Regions& r);
 w4a16_status shape_q4_sym(int M, int K, int32_t shape[3]);
 w4a16_status shape_q5(int M, int K, int32_t shape[3]);
 w4a16_status shape_q8_sym(int M, int K, int32_t shape[3]);
+w4a16_status shape_pal4(int M, int K, int32_t shape[3]);
 
 }  // namespace w4a16_codecs

@@ -1,7 +1,7 @@
 // gfx950 kernels of the weight-code variants: the single-GEMV skeleton with
 // one codec policy. This file is compiled once per codec, with
-// W4A16_CODEC_ID = 1 (symmetric 4-bit), 2 (5-bit affine) or 3 (symmetric
-// 8-bit); the codec formats are defined in include/w4a16.h.
+// W4A16_CODEC_ID = 1 (symmetric 4-bit), 2 (5-bit affine), 3 (symmetric 8-bit)
+// or 4 (palettised 4-bit); the codec formats are defined in include/w4a16.h.
 //
 // The variants are the quantisation types the Magnitude page compares when
 // converting a model (section 4.2: a symmetric 4-bit type, the 4-bit and
@@ -23,7 +23,7 @@
 #include "w4a16_skeleton.h"
 
 #ifndef W4A16_CODEC_ID
-#error "compile with -DW4A16_CODEC_ID=1, 2 or 3"
+#error "compile with -DW4A16_CODEC_ID=1, 2, 3 or 4"
 #endif
 
 using namespace w4a16_dev;
@@ -36,6 +36,8 @@ using Codec = CodecQ4Sym;
 using Codec = CodecQ5;
 #elif W4A16_CODEC_ID == 3
 using Codec = CodecQ8Sym;
+#elif W4A16_CODEC_ID == 4
+using Codec = CodecPal4;
 #else
 #error "unknown W4A16_CODEC_ID"
 #endif
@@ -140,8 +142,11 @@ w4a16_status shape_q4_sym(int M, int K, int32_t out[3]) { return shape(M, K, out
 #elif W4A16_CODEC_ID == 2
 w4a16_status enqueue_q5(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_q5(int M, int K, int32_t out[3]) { return shape(M, K, out); }
-#else
+#elif W4A16_CODEC_ID == 3
 w4a16_status enqueue_q8_sym(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_q8_sym(int M, int K, int32_t out[3]) { return shape(M, K, out); }
+#else
+w4a16_status enqueue_pal4(const Launch& l, const Regions& r) { return enqueue(l, r); }
+w4a16_status shape_pal4(int M, int K, int32_t out[3]) { return shape(M, K, out); }
 #endif
 }  // namespace w4a16_codecs

@@ -123,17 +123,21 @@ extern "C" w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, 
 namespace w4a16_codecs {
 
 bool regions(int codec, int32_t N, int32_t K, Regions& r) {
-  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return false;
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_PAL4) return false;
   if (N < 1 || K < kGroup || K % kGroup) return false;
   const int64_t G = K / kGroup;
   if (int64_t(N) * G > INT32_MAX) return false;
   const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
   const int64_t code_bytes = int64_t(N) * G * (codec == W4A16_CODEC_Q8_SYM ? 32 : 16);
   const int64_t S = (code_bytes + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
-  const int64_t side_entry = (codec == W4A16_CODEC_Q4_SYM || codec == W4A16_CODEC_Q8_SYM) ? 8 : 16;
   r.codes = size_t(code_bytes);
   r.aux = codec == W4A16_CODEC_Q5 ? size_t(S) : 0;
   r.side = size_t(S + (codec == W4A16_CODEC_Q5 ? T * G * 16 : 0));
+  if (codec == W4A16_CODEC_PAL4) {  // one 128-byte palette entry per tile
+    r.total = r.side + size_t(T * 128);
+    return true;
+  }
+  const int64_t side_entry = (codec == W4A16_CODEC_Q4_SYM || codec == W4A16_CODEC_Q8_SYM) ? 8 : 16;
   r.total = r.side + size_t(T * G * side_entry);
   return true;
 }
@@ -162,7 +166,7 @@ extern "C" size_t w4a16_codec_packed_bytes(int32_t codec, int32_t N, int32_t K) 
 
 extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, const uint16_t* scale,
                                          const uint16_t* min, int32_t N, int32_t K, void* out, size_t out_bytes) {
-  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_Q8_SYM) return W4A16_ERR_FORMAT;
+  if (codec < W4A16_CODEC_Q4 || codec > W4A16_CODEC_PAL4) return W4A16_ERR_FORMAT;
   if (codec == W4A16_CODEC_Q4) return w4a16_pack(codes, scale, min, N, K, out, out_bytes);
   const bool affine = codec == W4A16_CODEC_Q5;
   if (!codes || !scale || (affine && !min) || !out) return W4A16_ERR_NULL;
@@ -178,6 +182,19 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
   }
   uint8_t* o = static_cast<uint8_t*>(out);
   std::memset(o + reg.codes, 0, reg.total - reg.codes);  // padding and tiles past N
+  if (codec == W4A16_CODEC_PAL4) {
+    // codes: the canonical bytes, row after row; palettes: per tile and row,
+    // the 16 entries' low bytes, then their high bytes
+    std::memcpy(o, codes, size_t(N) * size_t(K / 2));
+    uint8_t* lt = o + reg.side;
+    for (int64_t n = 0; n < N; ++n)
+      for (int c = 0; c < 16; ++c) {
+        const uint16_t e = scale[n * 16 + c];
+        lt[n * 32 + c] = uint8_t(e & 0xFFu);
+        lt[n * 32 + 16 + c] = uint8_t(e >> 8);
+      }
+    return W4A16_OK;
+  }
 
   // code chunks
   parallel_rows(N, K, [&](int64_t r0, int64_t r1) {

@@ -279,12 +279,25 @@ w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]);
  *           little-endian 32-bit word e of a half holds k = 4e + i of that
  *           half with i = 0, 2, 1, 3 in bytes 0, 1, 2, 3;
  *           [S, S + T*G*8) scale tiles as for W4A16_CODEC_Q4_SYM.
+ *
+ * W4A16_CODEC_PAL4 (4): w_hat[n][k] = lut[n][q], q unsigned 4-bit: a palette
+ *   of 16 binary16 values per output row (Core ML's palettisation, named in
+ *   the core-modules page's runtime table, section 5.2, at per-row
+ *   granularity: a table per group of 32 weights would outweigh them).
+ *   codes uint8 [N][K/2] as in "Weight format"; the palettes binary16
+ *   [N][16] are passed as `scale`; no min.
+ *   packed: [0, N*K/2) codes: the canonical bytes, row after row (chunk
+ *           (n, g) = the 16 bytes of group g, unchanged);
+ *           [S, S + T*128) palette tiles: 128 bytes per tile t, row r at
+ *           32r: the 16 entries' low bytes, then their 16 high bytes (rows
+ *           at or beyond N are zero).
  */
 typedef enum w4a16_codec {
   W4A16_CODEC_Q4 = 0,
   W4A16_CODEC_Q4_SYM = 1,
   W4A16_CODEC_Q5 = 2,
-  W4A16_CODEC_Q8_SYM = 3
+  W4A16_CODEC_Q8_SYM = 3,
+  W4A16_CODEC_PAL4 = 4
 } w4a16_codec;
 
 /* Bytes of the packed blob of a codec (0 for an unknown codec or a bad N/K). */
@@ -293,7 +306,8 @@ size_t w4a16_codec_packed_bytes(int32_t codec, int32_t N, int32_t K);
 /*
  * w4a16_codec_pack - host repacker of a codec (init time; touches no GPU).
  *   codes  host array in the codec's canonical layout (see above), read only
- *   scale  host binary16 bits [N][K/32], read only
+ *   scale  host binary16 bits [N][K/32], read only ([N][16] palettes for
+ *          W4A16_CODEC_PAL4)
  *   min    host binary16 bits [N][K/32] for the affine codecs (0 and 2);
  *          ignored, and may be NULL, for the symmetric ones
  *   out    host buffer of at least w4a16_codec_packed_bytes(codec, N, K)

@@ -17,7 +17,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-CODECS = ["q4_sym", "q5", "q8_sym"]
+CODECS = ["q4_sym", "q5", "q8_sym", "pal4"]
 C = oracle.codecs_ref
 
 
@@ -101,6 +101,25 @@ def test_q4_sym_kernel_equals_q4_kernel_with_min_minus_eight_scales(w4a16_lib):
     ys = run_codec("q4_sym", x, codes, scale, None)
     ya = run_codec("q4", x, codes, scale, mn)
     np.testing.assert_array_equal(ys, ya)
+
+
+def test_pal4_kernel_with_an_affine_palette_matches_the_q4_kernel(w4a16_lib):
+    """An affine palette lut[n][c] = s_n * c + m_n: the palette kernel and the
+    4-bit group-affine kernel compute the same product (within tolerance; the
+    two sum in different orders)."""
+    M, N, K = 2, 300, 4096
+    x, codes, _, _ = workload.random_codec_problem("pal4", 13, M, N, K)
+    rng = np.random.default_rng(5)
+    s = rng.integers(1, 8, size=N).astype(np.float64) / 512.0
+    m = -rng.integers(0, 32, size=N).astype(np.float64) / 256.0
+    lut = (s[:, None] * np.arange(16)[None, :] + m[:, None]).astype(np.float16)
+    G = K // 32
+    yp = run_codec("pal4", x, codes, lut, None)
+    ya = run_codec("q4", x, codes, np.repeat(s[:, None], G, 1).astype(np.float16),
+                   np.repeat(m[:, None], G, 1).astype(np.float16))
+    y_ref, B = C.gemv("pal4", x, codes, lut)
+    check(yp, y_ref, B, "pal4 affine palette")
+    check(ya, y_ref, B, "q4 with the palette's scale and min")
 
 
 def test_codec_q4_is_w4a16_gemv(w4a16_lib):

@@ -41,6 +41,14 @@ def decode_blob(codec, blob, N, K):
     S = _round_up(code_bytes, 256)
     pads = [blob[code_bytes:S]]
     mn = None
+    if codec == "pal4":  # canonical bytes, then per tile and row: 16 low bytes, 16 high bytes of the palette
+        codes = blob[:code_bytes].reshape(N, K // 2).copy()
+        T = (N + 3) // 4
+        lt = blob[S: S + T * 128].reshape(T * 4, 2, 16).astype(np.uint16)
+        assert blob.size == S + T * 128
+        lut = (lt[:, 0, :] | (lt[:, 1, :] << 8)).astype(np.uint16)
+        pads.append(lut[N:])
+        return codes, lut[:N].view(np.float16), None, pads
     if codec in ("q4_sym", "q5"):
         words = blob[:code_bytes].view("<u4").reshape(N, G, 4).astype(np.int64)
         q = _nibble_codes(words, N, G)
@@ -78,7 +86,7 @@ def decode_blob(codec, blob, N, K):
 SHAPES = [(1, 32), (3, 64), (4, 96), (5, 128), (17, 2080), (9, 4096), (7, 14336)]
 
 
-@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym"])
+@pytest.mark.parametrize("codec", ["q4_sym", "q5", "q8_sym", "pal4"])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_codec_pack_roundtrip_bit_exact(w4a16_lib, codec, N, K):
     codes, scale, mn = workload.codec_weights(codec, 77, N, K % 7, N, K)
@@ -125,7 +133,7 @@ def test_codec_pack_errors(w4a16_lib):
     out = np.zeros(4096, np.uint8)
     q5 = np.zeros((2, 64), np.uint8)
     # unknown codec, code above 31 (nothing written)
-    assert L.w4a16_codec_pack(4, q5.ctypes.data, one.ctypes.data, one.ctypes.data, 2, 64, out.ctypes.data,
+    assert L.w4a16_codec_pack(5, q5.ctypes.data, one.ctypes.data, one.ctypes.data, 2, 64, out.ctypes.data,
                               out.nbytes) == w4.W4A16_ERR_FORMAT
     bad = q5.copy()
     bad[1, 63] = 32
@@ -143,10 +151,11 @@ def test_codec_pack_errors(w4a16_lib):
     need = w4.w4a16_codec_packed_bytes("q8_sym", 2, 64)
     assert L.w4a16_codec_pack(3, q5.ctypes.data, one.ctypes.data, None, 2, 64, out.ctypes.data,
                               need - 1) == w4.W4A16_ERR_SIZE
-    assert w4.w4a16_codec_packed_bytes(9, 4, 64) == 0 and w4.w4a16_codec_packed_bytes("q5", 4, 48) == 0
+    assert w4.w4a16_codec_packed_bytes(9, 4, 64) == 0 and w4.w4a16_codec_packed_bytes(5, 4, 64) == 0 and w4.w4a16_codec_packed_bytes("q5", 4, 48) == 0
 
 
-@pytest.mark.parametrize("codec,expect", [("q4_sym", 18 / 32), ("q5", 24 / 32), ("q8_sym", 34 / 32)])
+@pytest.mark.parametrize("codec,expect", [("q4_sym", 18 / 32), ("q5", 24 / 32), ("q8_sym", 34 / 32),
+                                          ("pal4", 16 / 32 + 32 / 4096)])
 def test_codec_bytes_per_weight(w4a16_lib, codec, expect):
     N, K = 4096, 4096
     assert w4.w4a16_codec_packed_bytes(codec, N, K) == N * K * expect
@@ -156,6 +165,7 @@ def test_codec_gemv_rejects_before_any_hip_call(w4a16_lib):
     L = w4.lib()
     x, p, y = 0x10000, 0x20000, 0x40000
     assert L.w4a16_codec_gemv(5, x, p, y, 1, 8, 64, None) == w4.W4A16_ERR_FORMAT
+    assert L.w4a16_codec_gemv(-1, x, p, y, 1, 8, 64, None) == w4.W4A16_ERR_FORMAT
     assert L.w4a16_codec_gemv(2, None, p, y, 1, 8, 64, None) == w4.W4A16_ERR_NULL
     assert L.w4a16_codec_gemv(2, x, p, y, 9, 8, 64, None) == w4.W4A16_ERR_SHAPE
     assert L.w4a16_codec_gemv(3, x, p, y, 1, 8, 48, None) == w4.W4A16_ERR_SHAPE
@@ -166,7 +176,7 @@ def test_codec_gemv_rejects_before_any_hip_call(w4a16_lib):
 
 
 def test_codec_launch_shapes(w4a16_lib):
-    for codec, cid in (("q4_sym", 1), ("q5", 2), ("q8_sym", 3)):
+    for codec, cid in (("q4_sym", 1), ("q5", 2), ("q8_sym", 3), ("pal4", 4)):
         s = w4.w4a16_codec_launch_shape(codec, 1, 4096, 4096)
         assert s["kernel"] == f"codec_kernel<{cid}, 1, 1, 1>" and s["waves"] == 2
         s = w4.w4a16_codec_launch_shape(codec, 1, 4096, 14336)
