@@ -83,9 +83,9 @@ TRAFFIC = {
     "codec_kernel<3, 1, 1, 1>": 58_252_492,
     # palettised codes: (13,826.38 KiB x 2.000 + 61.34 KiB x 1.000)
     "codec_kernel<4, 1, 1, 1>": 28_379_234,
-    # KV-cache attention, split pass: (41,497.15 / 48,749.27 KiB x 2.000 + 1,235.0 / 1,657.5 KiB x 1.000)
-    "kv_attn_kernel<8, 4>": 86_250_813,
-    "kv_attn_kernel<4, 4>": 101_535_791,
+    # KV-cache attention, split pass: (41,499.66 / 48,759.26 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
+    "kv_attn_kernel<8, 4>": 86_255_945,
+    "kv_attn_kernel<4, 4>": 101_123_595,
 }
 
 

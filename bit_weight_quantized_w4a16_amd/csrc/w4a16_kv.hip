@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "w4a16.h"
@@ -80,6 +81,11 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
   asm volatile("" ::: "memory");
+}
+
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
 __device__ __forceinline__ float half_lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFFu))); }
@@ -162,7 +168,7 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s = dot2(qh[16 * grp + i], kOnes, s);
-      qsum[j][grp] = s;
+      qsum[j][grp] = uniform(s);
     }
   }
 
@@ -193,9 +199,6 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
 #pragma unroll
     for (int c = 0; c < R::kKChunks; ++c)
       kc[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kKCodes + c * 1024) + lane);
-#pragma unroll
-    for (int c = 0; c < R::kVLoads; ++c)
-      vc[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVCodes + c * 1024) + lane);
     if constexpr (BITS == 8) {
       const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rec + R::kKPar) + lane);
       const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rec + R::kVPar) + lane);
@@ -220,8 +223,8 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     // block scale 2^E: every |p * s_v| * 2^E stays below 2^14, so the binary16
     // weights are normal numbers down to 2^-28 of the block's largest scale
     float smax = fmaxf(fmaxf(fabsf(vs[0]), fabsf(vs[1])), fmaxf(fabsf(vs[2]), fabsf(vs[3])));
-    smax = wave_max(smax);
-    const int E = 14 - (smax > 0.f ? __builtin_amdgcn_frexp_expf(smax) : 0);
+    smax = uniform(wave_max(smax));
+    const int E = __builtin_amdgcn_readfirstlane(14 - (smax > 0.f ? __builtin_amdgcn_frexp_expf(smax) : 0));
 
     // phase 1: one lane per token
     const bool valid = b * kBlockTokens + lane < T;
@@ -229,7 +232,7 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     for (int j = 0; j < GQ; ++j) {
       const float sc = valid ? key_score<BITS>(kc, kp, q + (g * GQ + j) * (kD / 2), qsum[j]) * scale_log2
                              : -__builtin_inff();
-      const float m_new = fmaxf(m[j], wave_max(sc));  // finite: every block has a valid token
+      const float m_new = uniform(fmaxf(m[j], wave_max(sc)));  // finite: every block has a valid token
       const float corr = __builtin_amdgcn_exp2f(m[j] - m_new);
       const float p = __builtin_amdgcn_exp2f(sc - m_new);
       m[j] = m_new;
@@ -253,6 +256,11 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
         wh[wave][j][grp][wpos] = h;
       }
     }
+    // the value codes are loaded only now: their registers are live in
+    // phase 2 only, which keeps the kernel at more waves per SIMD
+#pragma unroll
+    for (int c = 0; c < R::kVLoads; ++c)
+      vc[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVCodes + c * 1024) + lane);
     wave_lds_sync();  // phase 2 reads the weights other lanes wrote
 
     // phase 2: one lane per two dims (2*lane, 2*lane + 1); the value codes are
@@ -443,11 +451,27 @@ bool shape_ok(int32_t bits, int32_t T, int32_t Hq, int32_t Hkv) {
   return int64_t(Hq) <= 4096;
 }
 
-// Blocks per workgroup: about 16 waves of work per CU, four blocks or more per
-// workgroup (one per wave), a multiple of four.
-int blocks_per_wg(int nb, int Hkv, int cus) {
-  const int64_t target_waves = int64_t(cus) * 16;
-  int64_t bw = (int64_t(nb) * Hkv + target_waves - 1) / target_waves;
+// Waves of the attention kernel that fit on the device at once (cached per
+// instantiation; without a device, the gfx950 figure for 4 query heads per
+// KV head: three workgroups per CU).
+int resident_waves(int bits, int gq, int cus, bool have_device) {
+  static std::atomic<int> cache[2][4];
+  const int bi = bits == 8 ? 0 : 1, gi = gq == 1 ? 0 : gq == 2 ? 1 : gq == 4 ? 2 : 3;
+  int occ = cache[bi][gi].load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    if (!have_device) return cus * 3 * kWaves;
+    const attn_fn fa = bits == 8 ? attn_for<8>(gq) : attn_for<4>(gq);
+    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fa), 64 * kWaves);
+    cache[bi][gi].store(occ, std::memory_order_relaxed);
+  }
+  return cus * occ * kWaves;
+}
+
+// Blocks per workgroup: as few as keep every workgroup resident in one round
+// (each wave then walks its blocks with no wave waiting for a free slot),
+// four blocks or more per workgroup (one per wave), a multiple of four.
+int blocks_per_wg(int nb, int Hkv, int resident) {
+  int64_t bw = (int64_t(nb) * Hkv + resident - 1) / resident;
   if (bw < 1) bw = 1;
   return int(4 * bw);
 }
@@ -479,7 +503,7 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int gq = Hq / Hkv;
-  const int bpw = blocks_per_wg(nb, Hkv, w4a16_host::cu_count(dev));
+  const int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, gq, w4a16_host::cu_count(dev), true));
   const int S = (nb + bpw - 1) / bpw;
   const attn_fn fa = bits == 8 ? attn_for<8>(gq) : attn_for<4>(gq);
   const comb_fn fc = comb_for(gq);
@@ -534,10 +558,11 @@ extern "C" w4a16_status w4a16_kv_attention_timed(int32_t bits, const void* q, co
 extern "C" w4a16_status w4a16_kv_launch_shape(int32_t bits, int32_t T, int32_t Hq, int32_t Hkv, int32_t out[3]) {
   if (!out) return W4A16_ERR_NULL;
   if (!shape_ok(bits, T, Hq, Hkv)) return W4A16_ERR_SHAPE;
-  int dev = 0;
-  const int cus = hipGetDevice(&dev) == hipSuccess ? w4a16_host::cu_count(dev) : 256;
+  int dev = 0, ndev = 0;
+  const bool have_device = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 && hipGetDevice(&dev) == hipSuccess;
+  const int cus = have_device ? w4a16_host::cu_count(dev) : 256;
   const int nb = (T + kBlockTokens - 1) / kBlockTokens;
-  const int bpw = blocks_per_wg(nb, Hkv, cus);
+  const int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, Hq / Hkv, cus, have_device));
   out[0] = Hq / Hkv;
   out[1] = bpw;
   out[2] = (nb + bpw - 1) / bpw;
