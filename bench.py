@@ -81,8 +81,8 @@ TRAFFIC = {
     "codec_kernel<1, 1, 1, 1>": 30_959_537,
     "codec_kernel<2, 1, 1, 1>": 41_217_127,
     "codec_kernel<3, 1, 1, 1>": 58_252_492,
-    # palettised codes: (13,826.38 KiB x 2.000 + 61.34 KiB x 1.000)
-    "codec_kernel<4, 1, 1, 1>": 28_379_234,
+    # palettised codes: (13,617.75 KiB x 2.000 + 52.0 KiB x 1.000)
+    "codec_kernel<4, 1, 1, 1>": 27_942_398,
     # KV-cache attention, split pass: (41,499.66 / 48,759.26 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
     "kv_attn_kernel<8, 4>": 86_255_945,
     "kv_attn_kernel<4, 4>": 101_123_595,

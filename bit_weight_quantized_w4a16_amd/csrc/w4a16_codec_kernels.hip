@@ -85,6 +85,18 @@ kernel_fn kernel_for_mode(int mode, int M, int gi) {
                                                                       : kernel_for<kDirect>(M, gi);
 }
 
+// LDS a codec asks for per wave beyond the skeleton's own (the palette
+// tables of the palettised code), given at launch as dynamic LDS
+template <class C, class = void>
+struct lds_per_wave {
+  static constexpr int value = 0;
+};
+template <class C>
+struct lds_per_wave<C, decltype(void(C::kLdsBytesPerWave))> {
+  static constexpr int value = C::kLdsBytesPerWave;
+};
+constexpr size_t dynamic_lds(int waves) { return size_t(lds_per_wave<Codec>::value) * waves; }
+
 // resident workgroups per CU, cached per instantiation and block size
 std::atomic<int> g_occupancy[kMaxM + 1][w4a16_host::kNumGpl][3][kMaxWaves + 1];
 
@@ -92,7 +104,7 @@ int occupancy(int M, int gi, int mode, int waves, kernel_fn fn) {
   std::atomic<int>& slot = g_occupancy[M][gi][mode][waves];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  v = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * waves);
+  v = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * waves, dynamic_lds(waves));
   slot.store(v, std::memory_order_relaxed);
   return v;
 }
@@ -127,8 +139,8 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
   float* y = l.y;
   int n_arg = l.N, g_arg = G, t_arg = T, c_arg = s.nchunks, b_arg = tpb;
   void* args[] = {&xp, &cp, &ap, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg};
-  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * s.waves), args, 0, l.stream,
-                         l.start, l.stop, 0) != hipSuccess)
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * s.waves), args,
+                         dynamic_lds(s.waves), l.stream, l.start, l.stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
 }

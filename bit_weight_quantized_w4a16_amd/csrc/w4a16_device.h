@@ -60,6 +60,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, unsigned(q[0])) + __builtin_bit_cast(float, unsigned(q[1]));
 }
 
+// A wave reads LDS words that other lanes of the same wave wrote: its LDS
+// operations complete in order once lgkmcnt drains, and the empty asm keeps
+// the compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  asm volatile("" ::: "memory");
+}
+
 // Maximum over the 64 lanes of a wave, by the same exchanges as wave_sum;
 // every lane ends with the same value.
 __device__ __forceinline__ float wave_max(float v) {

@@ -21,10 +21,12 @@ inline int cu_count(int dev) {
   return c;
 }
 
-// Resident workgroups per CU of a kernel at a block size (never below 1).
-inline int occupancy_of(const void* fn, int block_threads) {
+// Resident workgroups per CU of a kernel at a block size and dynamic LDS
+// size (never below 1).
+inline int occupancy_of(const void* fn, int block_threads, size_t dynamic_lds = 0) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block_threads, 0) != hipSuccess || nb <= 0) nb = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block_threads, dynamic_lds) != hipSuccess || nb <= 0)
+    nb = 1;
   return nb;
 }
 

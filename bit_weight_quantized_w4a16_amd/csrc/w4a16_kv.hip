@@ -75,14 +75,6 @@ struct Rec<4> {
 typedef const __attribute__((address_space(4))) uint32_t* QPtr;  // read through scalar loads
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// A wave reads LDS words that other lanes of the same wave wrote: its LDS
-// operations complete in order once lgkmcnt drains, and the empty asm keeps
-// the compiler from moving LDS accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
-  asm volatile("" ::: "memory");
-}
-
 // A value every lane of the wave holds, moved to a scalar register.
 __device__ __forceinline__ float uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));

@@ -183,15 +183,16 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
   uint8_t* o = static_cast<uint8_t*>(out);
   std::memset(o + reg.codes, 0, reg.total - reg.codes);  // padding and tiles past N
   if (codec == W4A16_CODEC_PAL4) {
-    // codes: the canonical bytes, row after row; palettes: per tile and row,
-    // the 16 entries' low bytes, then their high bytes
+    // codes: the canonical bytes, row after row; palettes: per tile, entry c
+    // of row r at byte 8c + 2r (binary16, little-endian)
     std::memcpy(o, codes, size_t(N) * size_t(K / 2));
     uint8_t* lt = o + reg.side;
     for (int64_t n = 0; n < N; ++n)
       for (int c = 0; c < 16; ++c) {
         const uint16_t e = scale[n * 16 + c];
-        lt[n * 32 + c] = uint8_t(e & 0xFFu);
-        lt[n * 32 + 16 + c] = uint8_t(e >> 8);
+        uint8_t* dst = lt + (n / kTileRows) * 128 + 8 * c + 2 * (n % kTileRows);
+        dst[0] = uint8_t(e & 0xFFu);
+        dst[1] = uint8_t(e >> 8);
       }
     return W4A16_OK;
   }
@@ -343,7 +344,7 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
   return W4A16_OK;
 }
 
-extern "C" int32_t w4a16_abi_version(void) { return 3; }
+extern "C" int32_t w4a16_abi_version(void) { return 4; }
 
 extern "C" const char* w4a16_status_string(int32_t status) {
   switch (status) {

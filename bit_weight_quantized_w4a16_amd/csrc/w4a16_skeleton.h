@@ -331,30 +331,32 @@ struct CodecQ8Sym {
 // Palettised 4-bit code (w_hat = lut[n][q], a 16-entry binary16 palette per
 // row): code chunks holding the group's canonical bytes (byte i of word d =
 // k = 8d + 2i in the low nibble, k + 1 in the high nibble), and per tile a
-// 128-byte entry with each row's palette as two 16-byte tables, the entries'
-// low bytes and their high bytes. A palette lookup is a byte permute: for the
-// four even codes of a word, v_perm_b32 with selectors (q & 7) picks their low
-// bytes from entries 0..7 and 8..15, a byte-wise bit-field insert keeps the
-// right half by bit 3 of each code, the same for the high bytes, and two more
-// permutes interleave them into binary16 pairs (w_k, w_k+2); the odd codes
-// give (w_k+1, w_k+3). The activation pairs are permuted to match once per
-// chunk and row of x, shared by the tile's four rows.
+// 128-byte entry with the palettes entry by entry (entry c of row r at byte
+// 8c + 2r). A code byte b indexes a pair of weights, so each wave expands the
+// tile's four palettes into a table of 256 binary16 pairs per row,
+// (lut[r][b & 15], lut[r][b >> 4]), in its own 4 KiB of LDS: lane l builds
+// the four consecutive entries 4l .. 4l + 3 of every row (low nibbles
+// 4(l & 3) .. +3, high nibble l >> 2) from 40 bytes of the palette tile. Each
+// code byte then costs one address operation and one LDS read, and the pair
+// it returns lines up with the activation pair (x_k, x_k+1) of the same word,
+// so it goes straight into v_dot2.
 struct CodecPal4 {
-  static constexpr int kTileVgprs = 48;
+  static constexpr int kTileVgprs = 26;
+  static constexpr int kLdsBytesPerWave = kTileRows * 256 * 4;
   template <int GPL>
   struct Loads {
-    u32x4 lut[kTileRows][2];  // per row: low-byte table, high-byte table
+    u32x4 lo[2];  // palette entries 4(l & 3) .. 4(l & 3) + 3 of the four rows
+    u32x2 hi;     // palette entry l >> 2 of the four rows
     u32x4 code[kTileRows][GPL];
   };
   template <int GPL>
   __device__ __forceinline__ static void fetch(const WeightPtrs& w, int N, int G, int t, const int (&g0)[GPL],
                                                int lane, Loads<GPL>& L) {
-    const u32x4* lp = static_cast<const u32x4*>(w.side) + size_t(t) * (2 * kTileRows);
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-      L.lut[r][0] = lp[2 * r];  // the same 128 bytes for every lane of the tile
-      L.lut[r][1] = lp[2 * r + 1];
-    }
+    const uint8_t* pt = static_cast<const uint8_t*>(w.side) + size_t(t) * 128;
+    const u32x4* lp = reinterpret_cast<const u32x4*>(pt + 32 * (lane & 3));
+    L.lo[0] = lp[0];
+    L.lo[1] = lp[1];
+    L.hi = *reinterpret_cast<const u32x2*>(pt + 8 * (lane >> 2));
 #pragma unroll
     for (int j = 0; j < GPL; ++j) {
       const Slot s = slot_of(G, g0[j], lane);
@@ -363,15 +365,35 @@ struct CodecPal4 {
         L.code[r][j] = __builtin_nontemporal_load(w.codes + (size_t(clamp_row(t, r, N)) * G + g0[j] + s.base) + s.gl);
     }
   }
-  // the binary16 bytes of the four palette entries selected by sel (values
-  // 0..7 in each byte) and bit 3 of each code (mask bytes 0xFF where set)
-  __device__ __forceinline__ static uint32_t lookup(const u32x4& table, uint32_t sel, uint32_t hi_mask) {
-    const uint32_t lo = __builtin_amdgcn_perm(table.y, table.x, sel);  // entries 0..7
-    const uint32_t hi = __builtin_amdgcn_perm(table.w, table.z, sel);  // entries 8..15
-    return (hi & hi_mask) | (lo & ~hi_mask);
+  // this wave's table: 256 words per row
+  __device__ __forceinline__ static uint32_t* table() {
+    extern __shared__ __align__(16) uint32_t pal4_tables[];
+    return pal4_tables + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (kLdsBytesPerWave / 4);
   }
   template <int M, int GPL, class XA>
   __device__ __forceinline__ static void compute(const Loads<GPL>& L, const XA& xa, float (&acc)[kTileRows][M]) {
+    uint32_t* tab = table();
+    const int lane = threadIdx.x & 63;
+    {
+      // entry 4l + i of row r: (binary16 of low nibble 4(l & 3) + i, of high
+      // nibble l >> 2); rows 0 and 1 share a word of each palette entry, as do
+      // rows 2 and 3
+      constexpr uint32_t kLow = 0x05040100u, kHigh = 0x07060302u;
+      const uint32_t hw[2] = {L.hi.x, L.hi.y};
+      const uint32_t lw[2][4] = {{L.lo[0].x, L.lo[0].z, L.lo[1].x, L.lo[1].z},
+                                 {L.lo[0].y, L.lo[0].w, L.lo[1].y, L.lo[1].w}};
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const uint32_t sel = (r & 1) ? kHigh : kLow;
+        u32x4 e;
+        e.x = __builtin_amdgcn_perm(hw[r >> 1], lw[r >> 1][0], sel);
+        e.y = __builtin_amdgcn_perm(hw[r >> 1], lw[r >> 1][1], sel);
+        e.z = __builtin_amdgcn_perm(hw[r >> 1], lw[r >> 1][2], sel);
+        e.w = __builtin_amdgcn_perm(hw[r >> 1], lw[r >> 1][3], sel);
+        *reinterpret_cast<u32x4*>(tab + r * 256 + 4 * lane) = e;
+      }
+    }
+    wave_lds_sync();  // the lookups read entries other lanes wrote
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
@@ -380,37 +402,19 @@ struct CodecPal4 {
     for (int j = 0; j < GPL; ++j) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint32_t x02[M], x13[M], x46[M], x57[M];  // activation pairs (k, k+2), (k+1, k+3), ... of chunk d
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const u32x4 xq = xa.x(m, j, d);
-          x02[m] = __builtin_amdgcn_perm(xq.y, xq.x, 0x05040100u);
-          x13[m] = __builtin_amdgcn_perm(xq.y, xq.x, 0x07060302u);
-          x46[m] = __builtin_amdgcn_perm(xq.w, xq.z, 0x05040100u);
-          x57[m] = __builtin_amdgcn_perm(xq.w, xq.z, 0x07060302u);
-        }
 #pragma unroll
         for (int r = 0; r < kTileRows; ++r) {
           const uint32_t w = elem(L.code[r][j], d);
-          const uint32_t sa = w & 0x07070707u, sb = (w >> 4) & 0x07070707u;
-          const uint32_t ta = (w >> 3) & 0x01010101u, tb = (w >> 7) & 0x01010101u;
-          const uint32_t ma = (ta << 8) - ta, mb = (tb << 8) - tb;  // 0xFF per byte whose code has bit 3
-          const uint32_t loA = lookup(L.lut[r][0], sa, ma), hiA = lookup(L.lut[r][1], sa, ma);
-          const uint32_t loB = lookup(L.lut[r][0], sb, mb), hiB = lookup(L.lut[r][1], sb, mb);
-          const uint32_t e02 = __builtin_amdgcn_perm(hiA, loA, 0x05010400u);  // (w_k, w_k+2)
-          const uint32_t e46 = __builtin_amdgcn_perm(hiA, loA, 0x07030602u);  // (w_k+4, w_k+6)
-          const uint32_t o13 = __builtin_amdgcn_perm(hiB, loB, 0x05010400u);  // (w_k+1, w_k+3)
-          const uint32_t o57 = __builtin_amdgcn_perm(hiB, loB, 0x07030602u);  // (w_k+5, w_k+7)
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            acc[r][m] = dot2(e02, x02[m], acc[r][m]);
-            acc[r][m] = dot2(e46, x46[m], acc[r][m]);
-            acc[r][m] = dot2(o13, x13[m], acc[r][m]);
-            acc[r][m] = dot2(o57, x57[m], acc[r][m]);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t pair = tab[r * 256 + ((w >> (8 * i)) & 0xFFu)];  // (w_k, w_k+1), k = 8d + 2i
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = dot2(pair, elem(xa.x(m, j, d), i), acc[r][m]);
           }
         }
       }
     }
+    wave_lds_sync();  // the next tile's table overwrites this one
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r)
 #pragma unroll

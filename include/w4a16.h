@@ -288,9 +288,9 @@ w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]);
  *   [N][16] are passed as `scale`; no min.
  *   packed: [0, N*K/2) codes: the canonical bytes, row after row (chunk
  *           (n, g) = the 16 bytes of group g, unchanged);
- *           [S, S + T*128) palette tiles: 128 bytes per tile t, row r at
- *           32r: the 16 entries' low bytes, then their 16 high bytes (rows
- *           at or beyond N are zero).
+ *           [S, S + T*128) palette tiles: 128 bytes per tile t, entry c
+ *           of row 4t + r at byte 8c + 2r (binary16, little-endian; rows at
+ *           or beyond N are zero).
  */
 typedef enum w4a16_codec {
   W4A16_CODEC_Q4 = 0,

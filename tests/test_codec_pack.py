@@ -5,7 +5,8 @@ layouts in include/w4a16.h, plus its error paths. No GPU.
 slots (slot p of a word holds i = 2p for p < 4, else 2(p-4)+1), the fifth-bit
 word (bit 4j + d is the code of k = 8d + 2(j mod 4) + j/4), the 8-bit halves
 (low halves of every group, then high halves; bytes 0..3 of word e hold
-i = 0, 2, 1, 3, each q + 128) and the 8- or 16-byte parameter tiles. It shares
+i = 0, 2, 1, 3, each q + 128), the 8- or 16-byte parameter tiles and the
+palette tiles (entry c of row 4t + r at byte 8c + 2r of tile t). It shares
 no code with the C++ repacker. Packing then decoding must give back the
 canonical arrays bit for bit, and every padding byte must be zero.
 """
@@ -41,14 +42,13 @@ def decode_blob(codec, blob, N, K):
     S = _round_up(code_bytes, 256)
     pads = [blob[code_bytes:S]]
     mn = None
-    if codec == "pal4":  # canonical bytes, then per tile and row: 16 low bytes, 16 high bytes of the palette
+    if codec == "pal4":  # canonical bytes, then per tile: entry c of row r at byte 8c + 2r
         codes = blob[:code_bytes].reshape(N, K // 2).copy()
         T = (N + 3) // 4
-        lt = blob[S: S + T * 128].reshape(T * 4, 2, 16).astype(np.uint16)
         assert blob.size == S + T * 128
-        lut = (lt[:, 0, :] | (lt[:, 1, :] << 8)).astype(np.uint16)
+        lut = blob[S: S + T * 128].view("<u2").reshape(T, 16, 4).transpose(0, 2, 1).reshape(4 * T, 16)
         pads.append(lut[N:])
-        return codes, lut[:N].view(np.float16), None, pads
+        return codes, lut[:N].copy().view(np.float16), None, pads
     if codec in ("q4_sym", "q5"):
         words = blob[:code_bytes].view("<u4").reshape(N, G, 4).astype(np.int64)
         q = _nibble_codes(words, N, G)
