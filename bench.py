@@ -73,16 +73,16 @@ def gemv_bytes(M, N, K, codec="q4"):
 # and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
 # only while the kernel is unchanged since the counters were taken.
 TRAFFIC = {
-    # (16,745.89 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    "gemv_kernel<1, 1, 1>": 34_348_829,
-    # (2,137,261.1 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
-    "chain_kernel<1, 2, 4>": 4_383_795_507,
-    # weight-code variants: (15,090.96 / 20,099.55 / 28,412.93 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
-    "codec_kernel<1, 1, 1, 1>": 30_959_537,
-    "codec_kernel<2, 1, 1, 1>": 41_217_127,
-    "codec_kernel<3, 1, 1, 1>": 58_252_492,
-    # palettised codes: (13,617.75 KiB x 2.000 + 52.0 KiB x 1.000)
-    "codec_kernel<4, 1, 1, 1>": 27_942_398,
+    # (16,754.59 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    "gemv_kernel<1, 1, 1>": 34_366_639,
+    # (2,137,225.4 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
+    "chain_kernel<1, 2, 4>": 4_383_722_368,
+    # weight-code variants: (15,090.47 / 20,096.05 / 28,412.36 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
+    "codec_kernel<1, 1, 1, 1>": 30_958_530,
+    "codec_kernel<2, 1, 1, 1>": 41_209_965,
+    "codec_kernel<3, 1, 1, 1>": 58_251_319,
+    # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
+    "codec_kernel<4, 1, 1, 1>": 27_932_673,
     # KV-cache attention, split pass: (41,499.66 / 48,759.26 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
     "kv_attn_kernel<8, 4>": 86_255_945,
     "kv_attn_kernel<4, 4>": 101_123_595,

@@ -298,14 +298,12 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
       LdsX<M, GPL, XG> xa{xl, xsl, {}};
 #pragma unroll
       for (int k = 0; k < GPL; ++k) xa.gl[k] = (seg - u.w.sg0) * SG + k * 64 + lane;
-      float acc[kTileRows][M];
+      float acc[kTileRows][M], v[M];
       compute_tile<M, GPL>(L, xa, acc);
-      // lane r*M + m writes the partial of row r, activation row m
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < kTileRows * M; ++i)
-        if (lane == i) v = acc[i / M][i % M];
-      if (lane < kTileRows * M) ys[(ti * u.w.e->S + seg) * kTileRows * M + lane] = v;
+      tile_sums<M>(acc, v);
+      // lane 16r + m writes the partial of row r, activation row m
+      if ((lane & 15) < M)
+        ys[(ti * u.w.e->S + seg) * kTileRows * M + (lane >> 4) * M + (lane & 15)] = pick_sum<M>(v, lane);
       if (lane == 0) __hip_atomic_fetch_add(&units_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       return true;
     };

@@ -216,8 +216,8 @@ struct RegX {
   __device__ __forceinline__ float sum(int m, int j) const { return xs[m][j]; }
 };
 
-// Wave-wide partial row sums of one tile over this wave's groups:
-// acc[r][m] = sum over the wave's groups g of
+// One lane's partial row sums of one tile over its groups (tile_sums adds
+// them over the wave): acc[r][m] = sum over the lane's groups g of
 //   scale[4t+r][g] * sum_k q*x[m][k] + min[4t+r][g] * sum_k x[m][k].
 // sum_k q*x is formed with v_dot2c_f32_f16 on binary16 subnormal pairs: the
 // packed word AND 0x000F000F is a pair of halfs whose bit patterns are the
@@ -273,10 +273,35 @@ __device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const XA& 
       }
     }
   }
+}
+
+// Wave sums of a tile's kTileRows x M lane partials, by one transposed
+// exchange per activation row m: rows 0 and 2, then rows 1 and 3, are paired
+// across the wave halves (v_permlane32_swap: lanes 0-31 end with row 0's
+// half sums, lanes 32-63 with row 2's), the two results across odd and even
+// 16-lane rows (v_permlane16_swap), which leaves output row r in lanes
+// 16r .. 16r + 15, and four DPP butterflies finish each 16-lane row. Every
+// lane of row group r ends with the same bits in v[m]: the sum over the 64
+// lanes of acc[r][m]. 10 VALU operations per m, against 32 for four
+// separate wave sums.
+template <int M>
+__device__ __forceinline__ void tile_sums(const float (&acc)[kTileRows][M], float (&v)[M]) {
+  static_assert(kTileRows == 4, "one output row per 16-lane row");
+  auto f = [](unsigned u) { return __builtin_bit_cast(float, u); };
+  auto u = [](float x) { return __builtin_bit_cast(unsigned, x); };
 #pragma unroll
-  for (int r = 0; r < kTileRows; ++r) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  for (int m = 0; m < M; ++m) {
+    const auto p = __builtin_amdgcn_permlane32_swap(u(acc[0][m]), u(acc[2][m]), false, false);
+    const float s02 = f(unsigned(p[0])) + f(unsigned(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(u(acc[1][m]), u(acc[3][m]), false, false);
+    const float s13 = f(unsigned(q[0])) + f(unsigned(q[1]));
+    const auto h = __builtin_amdgcn_permlane16_swap(u(s02), u(s13), false, false);
+    float t = f(unsigned(h[0])) + f(unsigned(h[1]));
+    t += dpp<0xB1>(t);   // quad_perm [1,0,3,2]
+    t += dpp<0x4E>(t);   // quad_perm [2,3,0,1]
+    t += dpp<0x141>(t);  // row_half_mirror
+    t += dpp<0x140>(t);  // row_mirror
+    v[m] = t;
   }
 }
 
@@ -292,19 +317,24 @@ __device__ __forceinline__ void store_y(float* p, float v) {
     *p = v;
 }
 
-// A wave that covers all of K for its tile writes the tile's 4*M results
-// itself: lane r*M + m stores y[m][4t + r].
-template <int M, bool COHERENT = false>
-__device__ __forceinline__ void store_tile(const float (&acc)[kTileRows][M], float* __restrict__ y, int N, int t,
-                                           int lane) {
-  float v = 0.f;
+// The tile_sums result of activation row m that lane `lane` stores: lane
+// 16r + m holds output row r's v[m] (M <= 16).
+template <int M>
+__device__ __forceinline__ float pick_sum(const float (&v)[M], int lane) {
+  float s = v[0];
 #pragma unroll
-  for (int i = 0; i < kTileRows * M; ++i)
-    if (lane == i) v = acc[i / M][i % M];
-  if (lane < kTileRows * M) {
-    const int n = t * kTileRows + lane / M;
-    if (n < N) store_y<COHERENT>(y + size_t(lane % M) * N + n, v);
-  }
+  for (int m = 1; m < M; ++m)
+    if ((lane & 15) == m) s = v[m];
+  return s;
+}
+
+// A wave that covers all of K for its tile writes the tile's 4*M results
+// itself from tile_sums: lane 16r + m stores y[m][4t + r].
+template <int M, bool COHERENT = false>
+__device__ __forceinline__ void store_tile(const float (&v)[M], float* __restrict__ y, int N, int t, int lane) {
+  const float s = pick_sum<M>(v, lane);
+  const int n = t * kTileRows + (lane >> 4);
+  if ((lane & 15) < M && n < N) store_y<COHERENT>(y + size_t(lane & 15) * N + n, s);
 }
 
 // Up to four activation rows the next tile's loads are issued before the

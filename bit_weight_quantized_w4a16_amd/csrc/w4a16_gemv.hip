@@ -49,15 +49,15 @@ using w4a16_host::kNumGpl;
 template <int M, int GPL, int MODE>
 __global__ void __launch_bounds__(64 * max_waves_of<CodecQ4>(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
-            float* __restrict__ y, int N, int G, int T, int nchunks, int tpb) {
-  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb);
+            float* __restrict__ y, int N, int G, int T, int nchunks, int tpb, int nwaves) {
+  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb, nwaves);
 }
 
 // ---------------------------------------------------------------------------
 // host side: instantiation table, launch-shape choice, validation
 // ---------------------------------------------------------------------------
 
-typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, float*, int, int, int, int, int);
+typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, float*, int, int, int, int, int, int);
 
 constexpr int32_t kMaxK = 1 << 20;
 
@@ -175,8 +175,8 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   const u32x4* xp = static_cast<const u32x4*>(x);
   const u32x4* cp = static_cast<const u32x4*>(packed);
   const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(packed) + codes_region);
-  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb;
-  void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg};
+  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb, w_arg = shape.waves;
+  void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg, &w_arg};
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
                          static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;

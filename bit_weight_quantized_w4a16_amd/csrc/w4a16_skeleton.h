@@ -17,7 +17,8 @@
 //                                                           float (&acc)[kTileRows][M]);
 //   static constexpr int kTileVgprs;    // VGPRs of one group slot's loads
 //
-// compute() returns wave-wide sums (every lane holds them).
+// compute() returns the lane's partial sums; the skeleton adds them over the
+// wave (tile_sums).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -167,10 +168,6 @@ struct CodecQ4Sym {
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
   }
 };
 
@@ -239,10 +236,6 @@ struct CodecQ5 {
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
   }
 };
 
@@ -321,10 +314,6 @@ struct CodecQ8Sym {
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
   }
 };
 
@@ -415,10 +404,6 @@ struct CodecPal4 {
       }
     }
     wave_lds_sync();  // the next tile's table overwrites this one
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
   }
 };
 
@@ -434,14 +419,17 @@ __host__ __device__ constexpr int max_waves_of(int M, int GPL) {
 // The kernel body
 // ---------------------------------------------------------------------------
 
+// nwaves is the workgroup's wave count, passed by the host: the device-side
+// workgroup size (blockDim.x) is a vector load from the dispatch packet, and
+// every wave would wait for it, a full memory latency, before it could issue
+// its activation loads.
 template <class C, int M, int GPL, int MODE>
 __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const WeightPtrs& wp, float* __restrict__ y,
-                                          int N, int G, int T, int nchunks, int tpb) {
+                                          int N, int G, int T, int nchunks, int tpb, int nwaves) {
   const int lane = threadIdx.x & 63;
   // wave-uniform values kept in scalar registers, so every load address is a
   // scalar base plus the one per-lane offset `lane`
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
   const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
   const int nblocks = (T + tpb - 1) / tpb;
   if (int(blockIdx.x) >= nblocks) return;
@@ -466,7 +454,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
   auto reduce_block = [&](int b) {
     __syncthreads();
     const int ntiles = min(tpb, T - b * tpb);
-    for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += blockDim.x) {
+    for (int i = threadIdx.x; i < ntiles * kTileRows * M; i += 64 * nwaves) {
       const int ti = i / (kTileRows * M);
       const int r = (i / M) % kTileRows;
       const int m = i % M;
@@ -494,13 +482,13 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
         for (int tb = 0; tb < ntiles; ++tb) {
           Loads la;
           C::template fetch<GPL>(wp, N, G, b * tpb + tb, g0, lane, la);
-          float acc[kTileRows][M];
+          float acc[kTileRows][M], v[M];
           C::template compute<M, GPL>(la, RegX<M, GPL>{xv, xs}, acc);
-          if (lane == 0) {
+          tile_sums<M>(acc, v);
+          if ((lane & 15) == 0) {  // the first lane of each 16-lane row: output row lane / 16
+            const int r = lane >> 4;
 #pragma unroll
-            for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-              for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + acc[r][m];
+            for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + v[m];
           }
         }
       }
@@ -528,16 +516,16 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
     auto finish = [&](const Loads& L, int e) {
       const int t = tile_of(e);
       if (t < T) {
-        float acc[kTileRows][M];
+        float acc[kTileRows][M], v[M];
         C::template compute<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
+        tile_sums<M>(acc, v);
         if constexpr (MODE == kDirect) {
-          store_tile<M>(acc, y, N, t, lane);
-        } else if (lane == 0) {
+          store_tile<M>(v, y, N, t, lane);
+        } else if ((lane & 15) == 0) {  // the first lane of each 16-lane row: output row lane / 16
           const int tb = e % tpb;
+          const int r = lane >> 4;
 #pragma unroll
-          for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m) part[tb][r][m][wave] = acc[r][m];
+          for (int m = 0; m < M; ++m) part[tb][r][m][wave] = v[m];
         }
       }
       if constexpr (MODE == kBlock) {
