@@ -150,19 +150,24 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
   __shared__ __attribute__((aligned(16))) _Float16 wh[kWaves][GQ][4][kBlockTokens];
   __shared__ float comb[kWaves][GQ][kPartFloats];
 
-  // per-group sums of each query head (the offset / min terms of the score)
+  // Per-group sums of each query head (the offset / min terms of the
+  // score). The GQ heads' rows are GQ * 16 chunks of 16 bytes; lane i of load
+  // c takes chunk 64c + i (head i / 16, group (i / 4) % 4), issued before the
+  // first block's loads and summed after them, so the two latencies overlap
+  // (scalar loads of the 16 groups one after another would put 16 cache
+  // round trips in front of the first block).
+  constexpr int kQLoads = (GQ * 16 + 63) / 64;
+  u32x4 qv[kQLoads];
+#pragma unroll
+  for (int c = 0; c < kQLoads; ++c) {
+    const int i = 64 * c + lane;
+    qv[c] = reinterpret_cast<const u32x4*>(q_pairs + size_t(g) * GQ * (kD / 2))[i < GQ * 16 ? i : 0];
+  }
   float qsum[GQ][4];
 #pragma unroll
-  for (int j = 0; j < GQ; ++j) {
-    const QPtr qh = q + (g * GQ + j) * (kD / 2);
+  for (int j = 0; j < GQ; ++j)
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s = dot2(qh[16 * grp + i], kOnes, s);
-      qsum[j][grp] = uniform(s);
-    }
-  }
+    for (int grp = 0; grp < 4; ++grp) qsum[j][grp] = 0.f;
 
   // Running state per query head j: the maximum m (uniform, exp2 domain) and,
   // in real units, l (the weight sum of this lane's tokens), acc (the weighted
@@ -199,6 +204,23 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     } else {
       kp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kKPar) + lane);
       vp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVPar) + lane);
+    }
+    if (b == b0 + wave) {  // this wave's first block: its loads are out, form the query sums
+      float qs[kQLoads];
+#pragma unroll
+      for (int c = 0; c < kQLoads; ++c) {
+        asm volatile("" : "+v"(qv[c]));  // keeps the sums here, after the block's loads
+        float t = dot2(qv[c].x, kOnes, 0.f);
+        t = dot2(qv[c].y, kOnes, t);
+        t = dot2(qv[c].z, kOnes, t);
+        t = dot2(qv[c].w, kOnes, t);
+        t += dpp<0xB1>(t);  // quad_perm [1,0,3,2]
+        qs[c] = t + dpp<0x4E>(t);  // quad_perm [2,3,0,1]: the group's sum in each lane of its quad
+      }
+#pragma unroll
+      for (int gi = 0; gi < GQ * 4; ++gi)
+        qsum[gi / 4][gi % 4] =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs[gi / 16]), 4 * (gi % 16)));
     }
     static_assert(kKPar * kBlockTokens == 512 || kKPar * kBlockTokens == 1024, "parameter layout");
     float vs[4], vm[4];  // this lane's token's value scales (and mins)
