@@ -83,9 +83,9 @@ TRAFFIC = {
     "codec_kernel<3, 1, 1, 1>": 58_251_319,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     "codec_kernel<4, 1, 1, 1>": 27_932_673,
-    # KV-cache attention, split pass: (41,455.12 / 48,713.17 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
-    "kv_attn_kernel<8, 4>": 86_164_723,
-    "kv_attn_kernel<4, 4>": 101_029_218,
+    # KV-cache attention, split pass: (41,441.66 / 48,748.71 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
+    "kv_attn_kernel<8, 4>": 86_137_156,
+    "kv_attn_kernel<4, 4>": 101_101_990,
 }
 
 

@@ -13,17 +13,20 @@
 //   waves takes a contiguous range of a head's blocks; its waves take the
 //   blocks round-robin. All GQ query heads that share the KV head are served
 //   by the same pass over the block, so the cache is read once for all of them.
-// * Phase 1 of a block, one lane per token: the key codes of its token (eight
-//   or four 16-byte chunks laid out so that each load instruction reads 1 KiB
-//   contiguously) are turned into binary16 subnormal pairs by masking and
-//   dotted with the query pairs, which come from scalar loads (the query is
-//   uniform across the wave); the group scale folds them into the score. An
-//   online softmax across the wave keeps the running maximum per query head,
-//   and each lane writes its token's weights p * s_v (and p * m_v) to LDS.
-// * Phase 2 of a block, one lane per two head dimensions: the value codes
-//   (16 bytes per lane per load, eight or sixteen tokens of its two dims) are
-//   converted to fp32 and accumulated with the token weights read back from
-//   LDS.
+// * The two products of a block are small dense contractions over four query
+//   heads (GQ = 4 per KV head in the 8B model), so they run on the matrix
+//   cores (v_mfma_f32_4x4x4_16b_f16, the heads as the four rows), with the
+//   codes turned into binary16 subnormal operands by masking: exact, no
+//   per-value conversions.
+// * Phase 1, one lane per token: the key codes of its token (chunks laid out
+//   so that each load instruction reads 1 KiB contiguously) against the
+//   query rows held in LDS give its scores for four heads per MFMA, group by
+//   group of 32 dims; the group scale and offset fold them. An online softmax
+//   across the wave keeps the running maximum per query head, and each lane
+//   writes its token's binary16 weights p * s_v to LDS.
+// * Phase 2, one lane per head dimension (two halves of 64 dims): the value
+//   codes of four tokens of its dim against the weights of those tokens give
+//   the weighted values of four heads per MFMA.
 // * The four waves' partial results are merged through LDS in a fixed order
 //   and each workgroup writes one partial (maximum, sum of weights, 128
 //   weighted values per query head) to the caller's workspace; a second
@@ -72,7 +75,6 @@ struct Rec<4> {
   static constexpr int kVLoads = 4;        // 16 tokens per load
 };
 
-typedef const __attribute__((address_space(4))) uint32_t* QPtr;  // read through scalar loads
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // A value every lane of the wave holds, moved to a scalar register.
@@ -82,61 +84,34 @@ __device__ __forceinline__ float uniform(float v) {
 
 __device__ __forceinline__ float half_lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFFu))); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
-__device__ __forceinline__ float byte_f(uint32_t w, int i) { return float((w >> (8 * i)) & 0xFFu); }
 
-// Score of this lane's token against query head h (in units of the raw dot
-// product, before 1/sqrt(D)): the key chunks kc, the token's group
-// parameters kp (INT8: 4 scales in 2 words; INT4: (scale, min) x 4 in 4
-// words) and the query's per-group sums qsum.
-template <int BITS>
-__device__ __forceinline__ float key_score(const u32x4 (&kc)[Rec<BITS>::kKChunks], const u32x4& kp, QPtr qh,
-                                           const float (&qsum)[4]) {
-  float score = 0.f;
-  if constexpr (BITS == 8) {
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      float dot = 0.f;
-#pragma unroll
-      for (int c = 2 * grp; c < 2 * grp + 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = elem(kc[c], e);
-          dot = dot2(w & 0x00FF00FFu, qh[8 * c + 2 * e], dot);
-          dot = dot2((w >> 8) & 0x00FF00FFu, qh[8 * c + 2 * e + 1], dot);
-        }
-      const float s = (grp & 1) ? half_hi(elem(kp, grp >> 1)) : half_lo(elem(kp, grp >> 1));
-      score = __builtin_fmaf(s * 0x1p24f, dot, score);
-      score = __builtin_fmaf(-128.f * s, qsum[grp], score);
-    }
-  } else {
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      float lo = 0.f, hi = 0.f;
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const uint32_t w = elem(kc[grp], wd), w8 = w >> 8;
-        const int qd = 16 * grp + 4 * wd;
-        lo = dot2(w & 0x000F000Fu, qh[qd], lo);
-        hi = dot2(w & 0x00F000F0u, qh[qd + 1], hi);
-        lo = dot2(w8 & 0x000F000Fu, qh[qd + 2], lo);
-        hi = dot2(w8 & 0x00F000F0u, qh[qd + 3], hi);
-      }
-      const uint32_t par = elem(kp, grp);
-      score = __builtin_fmaf(half_lo(par) * 0x1p20f, __builtin_fmaf(lo, 16.f, hi), score);
-      score = __builtin_fmaf(half_hi(par), qsum[grp], score);
-    }
-  }
-  return score;
-}
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Four binary16 numbers from two words (halves in order lo(a), hi(a), lo(b), hi(b)).
+__device__ __forceinline__ h4 halves(uint32_t a, uint32_t b) { return __builtin_bit_cast(h4, u32x2{a, b}); }
+__device__ __forceinline__ h4 lds_h4(const _Float16* p) { return *reinterpret_cast<const h4*>(p); }
+
+// v_mfma_f32_4x4x4_16b_f16: sixteen independent 4x4x4 products per wave. For
+// block b = lane / 4 the lane 4b + i holds row i of A (four k), the lane
+// 4b + j column j of B, and the result D_b[i][j] lands in register i of lane
+// 4b + j. Binary16 subnormal inputs are exact.
+__device__ __forceinline__ f4 mfma4(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0); }
+
+// The split attention pass. Both dot products run on the matrix cores with
+// four query heads as the MFMA's four rows:
+// * scores: A = four heads' query dims (from LDS, lane & 3 = head), B = this
+//   lane's token's key dims as binary16 subnormal pairs (lane = token); the
+//   result gives lane t the scores of its token for the four heads;
+// * values: A = the binary16 weights of four tokens (from LDS, lane & 3 =
+//   head), B = the value codes of four tokens for one dim (lane = dim); the
+//   result gives lane d the weighted values of dim 64h + d for the four heads.
 template <int BITS, int GQ>
 __global__ void __launch_bounds__(64 * kWaves)
 kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__ kv, float* __restrict__ part, int T,
                int nb, int bpw, float scale_log2) {
   using R = Rec<BITS>;
-  // the query (binary16 pairs [Hq][64]) is read through the constant address
-  // space: uniform, so the compiler loads it with scalar loads
-  const QPtr q = (QPtr)(reinterpret_cast<uintptr_t>(q_pairs));
+  constexpr int HG = (GQ + 3) / 4;       // groups of four query heads: the rows of one MFMA
   constexpr int kKPar = BITS == 8 ? 8 : 16;  // parameter bytes per token
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,52 +121,55 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
   const int b0 = split * bpw;
   const int b1 = min(b0 + bpw, nb);
 
-  // binary16 token weights p * s_v * 2^E per (wave, head, value group, slot)
-  __shared__ __attribute__((aligned(16))) _Float16 wh[kWaves][GQ][4][kBlockTokens];
+  // binary16 token weights p * s_v * 2^E per (wave, head, value group, token)
+  __shared__ __attribute__((aligned(16))) _Float16 wh[kWaves][4 * HG][4][kBlockTokens];
+  // this wave's copy of the query rows (heads past GQ are zero)
+  __shared__ __attribute__((aligned(16))) _Float16 qh[kWaves][4 * HG][kD];
   __shared__ float comb[kWaves][GQ][kPartFloats];
 
-  // Per-group sums of each query head (the offset / min terms of the
-  // score). The GQ heads' rows are GQ * 16 chunks of 16 bytes; lane i of load
-  // c takes chunk 64c + i (head i / 16, group (i / 4) % 4), issued before the
-  // first block's loads and summed after them, so the two latencies overlap
-  // (scalar loads of the 16 groups one after another would put 16 cache
-  // round trips in front of the first block).
-  constexpr int kQLoads = (GQ * 16 + 63) / 64;
-  u32x4 qv[kQLoads];
+  // The query: 4 * HG rows of 256 bytes, 16 chunks of 16 bytes each; lane i
+  // of load c takes chunk 64c + i (head i / 16, group (i / 4) % 4). The loads
+  // go out before the first block's loads; the per-group sums and the LDS
+  // copy are formed after them, so the two latencies overlap.
+  u32x4 qv[HG];
 #pragma unroll
-  for (int c = 0; c < kQLoads; ++c) {
+  for (int c = 0; c < HG; ++c) {
     const int i = 64 * c + lane;
     qv[c] = reinterpret_cast<const u32x4*>(q_pairs + size_t(g) * GQ * (kD / 2))[i < GQ * 16 ? i : 0];
   }
-  float qsum[GQ][4];
+  float qsum[4 * HG][4];  // per head and group: the offset / min terms of the score
 #pragma unroll
-  for (int j = 0; j < GQ; ++j)
+  for (int j = 0; j < 4 * HG; ++j)
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) qsum[j][grp] = 0.f;
+  // heads past GQ have zero weights, so the value products ignore them
+  if constexpr (GQ < 4) {
+#pragma unroll
+    for (int j = GQ; j < 4; ++j)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) wh[wave][j][grp][lane] = _Float16(0.f);
+  }
 
   // Running state per query head j: the maximum m (uniform, exp2 domain) and,
   // in real units, l (the weight sum of this lane's tokens), acc (the weighted
-  // values of this lane's two dims) and off[grp] (the offset / min term of
+  // values of dims lane and 64 + lane) and off[grp] (the offset / min term of
   // this lane's tokens for value group grp).
-  float m[GQ], l[GQ], acc[GQ][2], off[GQ][4];
+  float m[GQ], l[GQ], acc[4 * HG][2], off[GQ][4];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     m[j] = -__builtin_inff();
     l[j] = 0.f;
-    acc[j][0] = acc[j][1] = 0.f;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) off[j][grp] = 0.f;
   }
-  const int vgrp = lane >> 4;  // group of this lane's two dims in phase 2
-  // slot of this lane's token in a row of binary16 weights: INT8 keeps token
-  // order (dword k = tokens 2k, 2k+1, the pair a value word forms); INT4
-  // stores each 4-token group as (t0, t2, t1, t3), the pairs its value bytes
-  // form under the nibble masks
-  const int wpos = BITS == 8 ? lane : (lane & ~3) | ((lane & 1) << 1) | ((lane >> 1) & 1);
+#pragma unroll
+  for (int j = 0; j < 4 * HG; ++j) acc[j][0] = acc[j][1] = 0.f;
+  const int qrow = lane & 3;         // the head row this lane feeds to the MFMA's A operand
+  const int vgrp_hi = lane >> 5;     // value group of this lane's dims, minus 2h
 
   for (int b = b0 + wave; b < b1; b += kWaves) {
     const uint8_t* rec = kv + (size_t(g) * nb + b) * R::kBytes;
-    // every load of the block first
+    // every key load of the block first
     u32x4 kc[R::kKChunks], vc[R::kVLoads], kp, vp;
 #pragma unroll
     for (int c = 0; c < R::kKChunks; ++c)
@@ -205,22 +183,25 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
       kp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kKPar) + lane);
       vp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVPar) + lane);
     }
-    if (b == b0 + wave) {  // this wave's first block: its loads are out, form the query sums
-      float qs[kQLoads];
+    if (b == b0 + wave) {  // this wave's first block: its loads are out; the query sums and LDS copy
+      float qs[HG];
 #pragma unroll
-      for (int c = 0; c < kQLoads; ++c) {
-        asm volatile("" : "+v"(qv[c]));  // keeps the sums here, after the block's loads
+      for (int c = 0; c < HG; ++c) {
+        asm volatile("" : "+v"(qv[c]));  // keeps this work here, after the block's loads
         float t = dot2(qv[c].x, kOnes, 0.f);
         t = dot2(qv[c].y, kOnes, t);
         t = dot2(qv[c].z, kOnes, t);
         t = dot2(qv[c].w, kOnes, t);
-        t += dpp<0xB1>(t);  // quad_perm [1,0,3,2]
+        t += dpp<0xB1>(t);         // quad_perm [1,0,3,2]
         qs[c] = t + dpp<0x4E>(t);  // quad_perm [2,3,0,1]: the group's sum in each lane of its quad
+        const int i = 64 * c + lane;  // chunk i: head i / 16, dims 8 (i % 16) .. + 7
+        *reinterpret_cast<u32x4*>(&qh[wave][i / 16][8 * (i % 16)]) = i < GQ * 16 ? qv[c] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int gi = 0; gi < GQ * 4; ++gi)
         qsum[gi / 4][gi % 4] =
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs[gi / 16]), 4 * (gi % 16)));
+      wave_lds_sync();  // the MFMAs read rows other lanes wrote
     }
     static_assert(kKPar * kBlockTokens == 512 || kKPar * kBlockTokens == 1024, "parameter layout");
     float vs[4], vm[4];  // this lane's token's value scales (and mins)
@@ -240,15 +221,65 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     smax = uniform(wave_max(smax));
     const int E = __builtin_amdgcn_readfirstlane(14 - (smax > 0.f ? __builtin_amdgcn_frexp_expf(smax) : 0));
 
-    // phase 1: one lane per token
+    // phase 1: scores of this lane's token for every head, group by group (the
+    // key scale and offset apply per group of 32 dims)
+    float sc[4 * HG];
+#pragma unroll
+    for (int j = 0; j < 4 * HG; ++j) sc[j] = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      f4 dl[HG], dh[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) dl[hg] = dh[hg] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BITS == 8) {
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {  // dims 32 grp + 4 s4 .. + 3: word s4 % 4 of chunk 2 grp + s4 / 4
+          const uint32_t w = elem(kc[2 * grp + s4 / 4], s4 % 4);  // bytes: dims (0, 2, 1, 3), each q + 128
+          const h4 kb = halves(w & 0x00FF00FFu, (w >> 8) & 0x00FF00FFu);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg)
+            dl[hg] = mfma4(lds_h4(&qh[wave][4 * hg + qrow][32 * grp + 4 * s4]), kb, dl[hg]);
+        }
+        const float s = (grp & 1) ? half_hi(elem(kp, grp >> 1)) : half_lo(elem(kp, grp >> 1));
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sc[4 * hg + i] = __builtin_fmaf(s * 0x1p24f, dl[hg][i], sc[4 * hg + i]);
+            sc[4 * hg + i] = __builtin_fmaf(-128.f * s, qsum[4 * hg + i][grp], sc[4 * hg + i]);
+          }
+      } else {
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {  // dims 32 grp + 8 wd + 0..3 (low nibbles), + 4..7 (high nibbles)
+          const uint32_t w = elem(kc[grp], wd), w8 = w >> 8;
+          const h4 klo = halves(w & 0x000F000Fu, w8 & 0x000F000Fu);  // q * 2^-24
+          const h4 khi = halves(w & 0x00F000F0u, w8 & 0x00F000F0u);  // q * 2^-20
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            dl[hg] = mfma4(lds_h4(&qh[wave][4 * hg + qrow][32 * grp + 8 * wd]), klo, dl[hg]);
+            dh[hg] = mfma4(lds_h4(&qh[wave][4 * hg + qrow][32 * grp + 8 * wd + 4]), khi, dh[hg]);
+          }
+        }
+        const uint32_t par = elem(kp, grp);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sc[4 * hg + i] =
+                __builtin_fmaf(half_lo(par) * 0x1p20f, __builtin_fmaf(dl[hg][i], 16.f, dh[hg][i]), sc[4 * hg + i]);
+            sc[4 * hg + i] = __builtin_fmaf(half_hi(par), qsum[4 * hg + i][grp], sc[4 * hg + i]);
+          }
+      }
+    }
+
+    // online softmax per head, and the binary16 weights
     const bool valid = b * kBlockTokens + lane < T;
 #pragma unroll
     for (int j = 0; j < GQ; ++j) {
-      const float sc = valid ? key_score<BITS>(kc, kp, q + (g * GQ + j) * (kD / 2), qsum[j]) * scale_log2
-                             : -__builtin_inff();
-      const float m_new = uniform(fmaxf(m[j], wave_max(sc)));  // finite: every block has a valid token
+      const float scj = valid ? sc[j] * scale_log2 : -__builtin_inff();
+      const float m_new = uniform(fmaxf(m[j], wave_max(scj)));  // finite: every block has a valid token
       const float corr = __builtin_amdgcn_exp2f(m[j] - m_new);
-      const float p = __builtin_amdgcn_exp2f(sc - m_new);
+      const float p = __builtin_amdgcn_exp2f(scj - m_new);
       m[j] = m_new;
       l[j] = __builtin_fmaf(l[j], corr, p);
       acc[j][0] *= corr;
@@ -267,7 +298,7 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
           const float fix = vs[grp] != 0.f ? (wr - ps) * (vm[grp] * __builtin_amdgcn_rcpf(vs[grp])) : 0.f;
           off[j][grp] = __builtin_fmaf(off[j][grp], corr, __builtin_fmaf(p, vm[grp], fix));
         }
-        wh[wave][j][grp][wpos] = h;
+        wh[wave][j][grp][lane] = h;
       }
     }
     // the value codes are loaded only now: their registers are live in
@@ -277,56 +308,46 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
       vc[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rec + R::kVCodes + c * 1024) + lane);
     wave_lds_sync();  // phase 2 reads the weights other lanes wrote
 
-    // phase 2: one lane per two dims (2*lane, 2*lane + 1); the value codes are
-    // binary16 subnormal pairs over two tokens, dotted with the weight pairs
-    if constexpr (BITS == 8) {
-      float blk[GQ][2];
+    // phase 2: lane d accumulates dims d and 64 + d; A = the weights of four
+    // tokens for head row lane & 3 and the value group of the lane's block
 #pragma unroll
-      for (int j = 0; j < GQ; ++j) blk[j][0] = blk[j][1] = 0.f;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int vg = 2 * hh + vgrp_hi;
+      f4 dl[HG], dh[HG];
 #pragma unroll
-      for (int c = 0; c < R::kVLoads; ++c) {  // tokens 8c .. 8c+7; word wd = tokens 8c+2wd, +1
+      for (int hg = 0; hg < HG; ++hg) dl[hg] = dh[hg] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BITS == 8) {
 #pragma unroll
-        for (int j = 0; j < GQ; ++j) {
-          const u32x4 wp = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][8 * c]);
+        for (int s4 = 0; s4 < 16; ++s4) {  // tokens 4 s4 .. + 3: word s4 % 4 of load 4 hh + s4 / 4
+          const uint32_t w = elem(vc[4 * hh + s4 / 4], s4 % 4);  // bytes: tokens (0, 2, 1, 3), each q + 128
+          const h4 vb = halves(w & 0x00FF00FFu, (w >> 8) & 0x00FF00FFu);
 #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t w = elem(vc[c], wd);  // bytes (t0 d0, t0 d1, t1 d0, t1 d1), each q + 128
-            blk[j][0] = dot2(w & 0x00FF00FFu, elem(wp, wd), blk[j][0]);
-            blk[j][1] = dot2((w >> 8) & 0x00FF00FFu, elem(wp, wd), blk[j][1]);
+          for (int hg = 0; hg < HG; ++hg) dl[hg] = mfma4(lds_h4(&wh[wave][4 * hg + qrow][vg][4 * s4]), vb, dl[hg]);
+        }
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)  // codes were q + 128 times 2^-24, weights times 2^E
+            acc[4 * hg + i][hh] = __builtin_fmaf(dl[hg][i], __builtin_ldexpf(1.f, 24 - E), acc[4 * hg + i][hh]);
+      } else {
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {  // tokens 8 s8 .. + 7: word s8 % 4 of load 2 hh + s8 / 4
+          const uint32_t w = elem(vc[2 * hh + s8 / 4], s8 % 4), w8 = w >> 8;
+          const h4 vlo = halves(w & 0x000F000Fu, w8 & 0x000F000Fu);  // tokens 0..3, q * 2^-24
+          const h4 vhi = halves(w & 0x00F000F0u, w8 & 0x00F000F0u);  // tokens 4..7, q * 2^-20
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            dl[hg] = mfma4(lds_h4(&wh[wave][4 * hg + qrow][vg][8 * s8]), vlo, dl[hg]);
+            dh[hg] = mfma4(lds_h4(&wh[wave][4 * hg + qrow][vg][8 * s8 + 4]), vhi, dh[hg]);
           }
         }
-      }
 #pragma unroll
-      for (int j = 0; j < GQ; ++j) {  // codes were q + 128 times 2^-24, weights times 2^E
-        acc[j][0] = __builtin_fmaf(blk[j][0], __builtin_ldexpf(1.f, 24 - E), acc[j][0]);
-        acc[j][1] = __builtin_fmaf(blk[j][1], __builtin_ldexpf(1.f, 24 - E), acc[j][1]);
-      }
-    } else {
-      float lo[GQ], hi[GQ];
+        for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-      for (int j = 0; j < GQ; ++j) lo[j] = hi[j] = 0.f;
-#pragma unroll
-      for (int c = 0; c < R::kVLoads; ++c) {  // tokens 16c .. 16c+15
-#pragma unroll
-        for (int j = 0; j < GQ; ++j) {
-          const u32x4 wa = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][16 * c]);
-          const u32x4 wb = *reinterpret_cast<const u32x4*>(&wh[wave][j][vgrp][16 * c + 8]);
-#pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {  // tokens 16c + 4wd + i in byte i: (low nibble d0, high nibble d1)
-            const uint32_t w = elem(vc[c], wd), w8 = w >> 8;
-            const uint32_t p02 = wd < 2 ? elem(wa, 2 * wd) : elem(wb, 2 * wd - 4);      // weights (t0, t2)
-            const uint32_t p13 = wd < 2 ? elem(wa, 2 * wd + 1) : elem(wb, 2 * wd - 3);  // weights (t1, t3)
-            lo[j] = dot2(w & 0x000F000Fu, p02, lo[j]);
-            hi[j] = dot2(w & 0x00F000F0u, p02, hi[j]);
-            lo[j] = dot2(w8 & 0x000F000Fu, p13, lo[j]);
-            hi[j] = dot2(w8 & 0x00F000F0u, p13, hi[j]);
+          for (int i = 0; i < 4; ++i) {  // low nibbles in units of 2^-24, high of 2^-20, weights times 2^E
+            acc[4 * hg + i][hh] = __builtin_fmaf(dl[hg][i], __builtin_ldexpf(1.f, 24 - E), acc[4 * hg + i][hh]);
+            acc[4 * hg + i][hh] = __builtin_fmaf(dh[hg][i], __builtin_ldexpf(1.f, 20 - E), acc[4 * hg + i][hh]);
           }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < GQ; ++j) {  // dim d0 in units of 2^-24, d1 of 2^-20, weights times 2^E
-        acc[j][0] = __builtin_fmaf(lo[j], __builtin_ldexpf(1.f, 24 - E), acc[j][0]);
-        acc[j][1] = __builtin_fmaf(hi[j], __builtin_ldexpf(1.f, 20 - E), acc[j][1]);
       }
     }
     wave_lds_sync();  // the next block's phase 1 overwrites the weights just read
@@ -340,9 +361,8 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
     float o4[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) o4[grp] = wave_sum(off[j][grp]);
-    const float oq = vgrp == 0 ? o4[0] : vgrp == 1 ? o4[1] : vgrp == 2 ? o4[2] : o4[3];
-    comb[wave][j][2 * lane] = acc[j][0] + oq;
-    comb[wave][j][2 * lane + 1] = acc[j][1] + oq;
+    comb[wave][j][lane] = acc[j][0] + (vgrp_hi == 0 ? o4[0] : o4[1]);
+    comb[wave][j][64 + lane] = acc[j][1] + (vgrp_hi == 0 ? o4[2] : o4[3]);
     if (lane == 0) {
       comb[wave][j][kD] = m[j];
       comb[wave][j][kD + 1] = lsum;
@@ -373,11 +393,17 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
 }
 
 // One workgroup of 512 threads per query head h: merge the S partials of h's
-// KV head. The maximum is a reduction over all threads; the weighted sums are
-// split into 4 fixed slices of the partials (slice k takes s = k, k+4, ...),
-// each thread summing one dim of one slice with its loads issued 8 at a
-// time, and the slices are added in order 0..3: a fixed summation order.
-constexpr int kMergeThreads = 512, kMergeSlices = kMergeThreads / kD, kMergeUnroll = 8;
+// KV head, kMergeChunk partials at a time (one chunk for the 8B shapes).
+// Per chunk: thread t < n loads the maximum and weight sum of partial t; a
+// block reduction gives the chunk's maximum and, in LDS, each partial's
+// factor exp2(m_s - M); each thread, one dim of one of 4 fixed slices of the
+// partials (slice k takes s = k, k+4, ...), has issued its weighted-value
+// loads at the start of the chunk and sums them with those factors. The
+// slices are added in order 0..3: a fixed summation order, so the result is
+// bitwise repeatable.
+constexpr int kMergeThreads = 512, kMergeSlices = kMergeThreads / kD, kMergeUnroll = 24;
+constexpr int kMergeChunk = kMergeSlices * kMergeUnroll;  // partials per chunk
+constexpr int kMergeWaves = kMergeThreads / 64;
 static_assert(kMergeSlices == 4, "the final sum below adds four slices");
 
 template <int GQ>
@@ -389,45 +415,52 @@ __global__ void __launch_bounds__(kMergeThreads) kv_combine_kernel(const float* 
   const int d = tid % kD, k = tid / kD;
   const float* p = part + (size_t(g * S) * GQ + j) * kPartFloats;
   const size_t stride = size_t(GQ) * kPartFloats;
-  __shared__ float red[kMergeThreads / 64];
+  __shared__ float fs[kMergeChunk];
+  __shared__ float red[kMergeWaves];
   __shared__ float accs[kMergeSlices][kD];
-  __shared__ float lss[kMergeSlices];
 
-  float mx = -__builtin_inff();
-  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, p[s * stride + kD]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
-
-  float a = 0.f, ls = 0.f;
-  for (int s0 = k; s0 < S; s0 += kMergeSlices * kMergeUnroll) {
-    float mv[kMergeUnroll], av[kMergeUnroll], lv[kMergeUnroll];
+  float M = -__builtin_inff(), a = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < S; c0 += kMergeChunk) {
+    const int n = min(kMergeChunk, S - c0);
+    float av[kMergeUnroll];
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {  // clamped, unconditional loads
-      const int s = s0 + kMergeSlices * u;
-      const size_t c = size_t(s < S ? s : 0) * stride;  // partial 0 always exists (S >= 1)
-      mv[u] = p[c + kD];
-      av[u] = p[c + d];
-      lv[u] = p[c + kD + 1];
+      const int s = k + kMergeSlices * u;
+      av[u] = p[size_t(c0 + (s < n ? s : 0)) * stride + d];
     }
+    const size_t ct = size_t(c0 + (tid < n ? tid : 0)) * stride;
+    const float mv = tid < n ? p[ct + kD] : -__builtin_inff();
+    const float lv = tid < n ? p[ct + kD + 1] : 0.f;
+    // the chunk's maximum over the block
+    float cm = wave_max(mv);
+    if (lane == 0) red[wave] = cm;
+    __syncthreads();
+    cm = red[0];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const float f = s0 + kMergeSlices * u < S ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
-      a = __builtin_fmaf(f, av[u], a);
-      ls = __builtin_fmaf(f, lv[u], ls);
-    }
+    for (int w = 1; w < kMergeWaves; ++w) cm = fmaxf(cm, red[w]);
+    const float M_new = fmaxf(M, cm);  // finite: every chunk has a partial
+    const float r = __builtin_amdgcn_exp2f(M - M_new);  // 0 on the first chunk
+    const float f = tid < n ? __builtin_amdgcn_exp2f(mv - M_new) : 0.f;
+    if (tid < kMergeChunk) fs[tid] = f;
+    // the chunk's weight sum over the block, in wave order
+    const float ws = wave_sum(f * lv);
+    __syncthreads();  // every wave has read red[] and written fs[]
+    if (lane == 0) red[wave] = ws;
+    __syncthreads();
+    float cden = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) cden += red[w];
+    den = __builtin_fmaf(den, r, cden);
+    a *= r;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u)  // fs[] is 0 past n, and av[] there is partial 0's, finite
+      a = __builtin_fmaf(fs[k + kMergeSlices * u], av[u], a);
+    M = M_new;
+    __syncthreads();  // fs[] and red[] are rewritten by the next chunk
   }
   accs[k][d] = a;
-  if (d == 0) lss[k] = ls;
   __syncthreads();
-  if (k == 0) {
-    const float num = (accs[0][d] + accs[1][d]) + (accs[2][d] + accs[3][d]);
-    const float den = (lss[0] + lss[1]) + (lss[2] + lss[3]);
-    o[size_t(h) * kD + d] = num / den;
-  }
+  if (k == 0) o[size_t(h) * kD + d] = ((accs[0][d] + accs[1][d]) + (accs[2][d] + accs[3][d])) / den;
 }
 
 typedef void (*attn_fn)(const uint32_t*, const uint8_t*, float*, int, int, int, float);

@@ -304,27 +304,31 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
         const uint8_t* kc = k_codes + (t * Hkv + g) * cb;
         const uint8_t* vc = v_codes + (t * Hkv + g) * cb;
         const int64_t pi = (t * Hkv + g) * 4;  // parameters of (t, g)
+        // byte slot of element i of a 4-element word, and of a 4-bit
+        // element i of an 8-element word (low nibble for i < 4): elements
+        // (0, 2, 1, 3) in bytes 0..3, so the masks 0x00FF00FF (0x000F000F
+        // for nibbles) on the word and on the word >> 8 give elements
+        // (0, 1) and (2, 3) as binary16 pairs; the high nibbles hold 4..7
+        static constexpr int kSlot[4] = {0, 2, 1, 3};
         if (bits == 8) {
-          static constexpr int kDimOf[4] = {0, 2, 1, 3};  // dim offset held by byte slot j of a word
           for (int c = 0; c < 8; ++c)
             for (int e = 0; e < 4; ++e)
               for (int j = 0; j < 4; ++j)
-                rec[c * 1024 + tt * 16 + 4 * e + j] = uint8_t(kc[16 * c + 4 * e + kDimOf[j]] ^ 0x80u);
+                rec[c * 1024 + tt * 16 + 4 * e + kSlot[j]] = uint8_t(kc[16 * c + 4 * e + j] ^ 0x80u);
           std::memcpy(rec + 8192 + tt * 8, k_scale + pi, 8);
           std::memcpy(rec + 8704 + tt * 8, v_scale + pi, 8);
-          // values: load c = tokens 8c..8c+7, lane l = dims 2l, 2l+1, byte 2*(token % 8) + e
-          const int64_t c = tt / 8, ti = tt % 8;
-          for (int l = 0; l < 64; ++l)
-            for (int e = 0; e < 2; ++e)
-              rec[9216 + c * 1024 + l * 16 + 2 * ti + e] = uint8_t(vc[2 * l + e] ^ 0x80u);
+          // values: load 4h + tq = dims 64h .. 64h + 63 of tokens 16tq .. 16tq + 15; lane l = dim 64h + l,
+          // word e = tokens 16tq + 4e .. + 3
+          const int64_t tq = tt / 16, e = (tt % 16) / 4;
+          for (int d = 0; d < 128; ++d)
+            rec[9216 + (4 * (d / 64) + tq) * 1024 + (d % 64) * 16 + 4 * e + kSlot[tt % 4]] = uint8_t(vc[d] ^ 0x80u);
         } else {
+          auto nib = [](const uint8_t* canon, int d) { return (canon[d / 2] >> (4 * (d % 2))) & 0xF; };
+          // keys: chunk c = group c, word wd = dims 32c + 8wd .. + 7
           for (int c = 0; c < 4; ++c)
-            for (int wd = 0; wd < 4; ++wd) {
-              uint32_t v;
-              std::memcpy(&v, kc + 16 * c + 4 * wd, 4);
-              v = split_even_odd(v);
-              std::memcpy(rec + c * 1024 + tt * 16 + 4 * wd, &v, 4);
-            }
+            for (int wd = 0; wd < 4; ++wd)
+              for (int i = 0; i < 8; ++i)
+                rec[c * 1024 + tt * 16 + 4 * wd + kSlot[i % 4]] |= uint8_t(nib(kc, 32 * c + 8 * wd + i) << (4 * (i / 4)));
           uint16_t kp[8], vp[8];
           for (int grp = 0; grp < 4; ++grp) {
             kp[2 * grp] = k_scale[pi + grp];
@@ -334,9 +338,12 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
           }
           std::memcpy(rec + 4096 + tt * 16, kp, 16);
           std::memcpy(rec + 5120 + tt * 16, vp, 16);
-          // values: load c = tokens 16c..16c+15, lane l = canonical byte l (dims 2l, 2l+1), byte token % 16
-          const int64_t c = tt / 16, ti = tt % 16;
-          for (int l = 0; l < 64; ++l) rec[6144 + c * 1024 + l * 16 + ti] = vc[l];
+          // values: load 2h + th = dims 64h .. 64h + 63 of tokens 32th .. 32th + 31; lane l = dim 64h + l,
+          // word w = tokens 32th + 8w .. + 7
+          const int64_t th = tt / 32, w = (tt % 32) / 8, i = tt % 8;
+          for (int d = 0; d < 128; ++d)
+            rec[6144 + (2 * (d / 64) + th) * 1024 + (d % 64) * 16 + 4 * w + kSlot[i % 4]] |=
+                uint8_t(nib(vc, d) << (4 * (i / 4)));
         }
       }
     }
@@ -344,7 +351,7 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
   return W4A16_OK;
 }
 
-extern "C" int32_t w4a16_abi_version(void) { return 4; }
+extern "C" int32_t w4a16_abi_version(void) { return 5; }
 
 extern "C" const char* w4a16_status_string(int32_t status) {
   switch (status) {

@@ -370,23 +370,26 @@ w4a16_status w4a16_codec_launch_shape(int32_t codec, int32_t M, int32_t N, int32
  * Packed cache (what w4a16_kv_pack writes): nb = ceil(T / 64) blocks of 64
  * tokens per KV head; records of R bytes ordered [g][block], R = 17,408
  * (INT8) or 10,240 (INT4). Inside the record of block b, slot i is token
- * 64b + i; slots at or beyond T are zero.
+ * 64b + i; slots at or beyond T are zero. Codes are packed in little-endian
+ * 32-bit words: a word of four 8-bit elements holds element i in byte
+ * (0, 2, 1, 3)[i], each as q + 128; a word of eight 4-bit elements holds
+ * element i in byte (0, 2, 1, 3)[i % 4], in the low nibble for i < 4 and the
+ * high nibble for i >= 4. (Masking such a word and the word shifted right by
+ * 8 gives elements (0, 1) and (2, 3) as binary16 subnormal pairs.)
  *   INT8: [0, 8192) key codes: chunk c = dims 16c..16c+15 at 1024c, slot i's
- *         16 bytes at 1024c + 16i, little-endian word e holding dims
- *         16c + 4e + (0, 2, 1, 3) in bytes 0..3, each q + 128;
+ *         16 bytes at 1024c + 16i, word e = dims 16c + 4e .. + 3;
  *         [8192, 8704) key scales, 8 bytes per slot (groups 0..3);
  *         [8704, 9216) value scales, the same way;
- *         [9216, 17408) value codes: load c = slots 8c..8c+7 at 9216 + 1024c,
- *         lane l's 16 bytes at + 16l holding dims 2l, 2l+1 of those slots,
- *         byte 2j + e = dim 2l + e of slot 8c + j, each q + 128.
- *   INT4: [0, 4096) key codes: chunk c = group c (dims 32c..32c+31), slot i's
- *         16 bytes at 1024c + 16i in the 4-bit weight chunk layout of
- *         "Packed layout" (dims in the place of k);
+ *         [9216, 17408) value codes: load 4h + u (h = 0, 1; u = 0..3) at
+ *         9216 + 1024 (4h + u), lane l's 16 bytes at + 16l holding dim
+ *         64h + l of slots 16u .. 16u + 15, word e = slots 16u + 4e .. + 3.
+ *   INT4: [0, 4096) key codes: chunk c = group c (dims 32c..32c+31) at
+ *         1024c, slot i's 16 bytes at + 16i, word w = dims 32c + 8w .. + 7;
  *         [4096, 5120) key (scale, min) pairs, 16 bytes per slot;
  *         [5120, 6144) value (scale, min) pairs, the same way;
- *         [6144, 10240) value codes: load c = slots 16c..16c+15 at
- *         6144 + 1024c, lane l's 16 bytes at + 16l, byte j = the canonical
- *         byte l (dims 2l, 2l+1) of slot 16c + j.
+ *         [6144, 10240) value codes: load 2h + u (h, u = 0, 1) at
+ *         6144 + 1024 (2h + u), lane l's 16 bytes at + 16l holding dim
+ *         64h + l of slots 32u .. 32u + 31, word w = slots 32u + 8w .. + 7.
  */
 
 /* Bytes of one layer's packed cache (0 if bits is not 8 or 4, T < 1,

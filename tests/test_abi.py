@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(w4a16_lib):
 
 
 def test_version_and_strings(w4a16_lib):
-    assert w4.w4a16_abi_version() == 4
+    assert w4.w4a16_abi_version() == 5
     for st in range(8):
         assert w4.w4a16_status_string(st) != "unknown status"
     assert w4.w4a16_status_string(99) == "unknown status"

@@ -3,11 +3,12 @@ layout in include/w4a16.h, and the host-side checks of the attention call.
 No GPU.
 
 `decode_cache` follows the header text only: records of R bytes per
-(KV head, 64-token block); INT8 key chunks of 16 dims per token with bytes
-holding dims (0, 2, 1, 3) of each word as q + 128, value loads of 8 tokens x 2
-dims per lane; INT4 key chunks in the 4-bit weight chunk layout, value loads
-of 16 tokens per lane holding the canonical byte. It shares no code with the
-C++ packer.
+(KV head, 64-token block); words of four 8-bit elements hold elements
+(0, 2, 1, 3) in bytes 0..3 as q + 128, words of eight 4-bit elements hold
+element i in byte (0, 2, 1, 3)[i % 4], low nibble for i < 4 and high nibble
+for i >= 4; INT8 key chunks of 16 dims per token, INT4 key chunks of one group
+per token, and value loads of 16 (INT8) or 32 (INT4) tokens of one dim per
+lane, dims 64h + lane. It shares no code with the C++ packer.
 """
 import numpy as np
 import pytest
@@ -15,14 +16,23 @@ import pytest
 import bit_weight_quantized_w4a16_amd as w4
 import workload
 
+SLOT = (0, 2, 1, 3)  # byte of element i (mod 4) of a word
 
-def _nibble_chunk_decode(words):
-    """4-bit weight chunk words [..., 4] -> 32 codes [..., 32] (slot p holds i = 2p, or 2(p-4)+1)."""
-    q = np.empty(words.shape[:-1] + (4, 8), dtype=np.int64)
-    for p in range(8):
-        i = 2 * p if p < 4 else 2 * (p - 4) + 1
-        q[..., i] = (words >> (4 * p)) & 0xF
-    return q.reshape(words.shape[:-1] + (32,))
+
+def _bytes4(words):
+    """Words of four 8-bit elements [..., 4 bytes] -> elements [..., 4] (q + 128 removed)."""
+    out = np.empty(words.shape, dtype=np.int64)
+    for i in range(4):
+        out[..., i] = words[..., SLOT[i]].astype(np.int64) - 128
+    return out
+
+
+def _nibbles8(words):
+    """Words of eight 4-bit elements [..., 4 bytes] -> elements [..., 8]."""
+    out = np.empty(words.shape[:-1] + (8,), dtype=np.int64)
+    for i in range(8):
+        out[..., i] = (words[..., SLOT[i % 4]].astype(np.int64) >> (4 * (i // 4))) & 0xF
+    return out
 
 
 def decode_cache(bits, blob, T, Hkv):
@@ -32,29 +42,27 @@ def decode_cache(bits, blob, T, Hkv):
     recs = blob.reshape(Hkv, nb, R)
     Tp = nb * 64
     if bits == 8:
-        kb = recs[:, :, :8192].reshape(Hkv, nb, 8, 64, 4, 4).astype(np.int64)   # [g, b, c, slot, e, byte j]
-        k = np.empty((Hkv, nb, 64, 128), dtype=np.int64)
-        for j, off in enumerate((0, 2, 1, 3)):
-            for c in range(8):
-                for e in range(4):
-                    k[:, :, :, 16 * c + 4 * e + off] = kb[:, :, c, :, e, j] - 128
+        kb = recs[:, :, :8192].reshape(Hkv, nb, 8, 64, 4, 4)                  # [g, b, chunk c, slot, word e, byte]
+        k = _bytes4(kb).transpose(0, 1, 3, 2, 4, 5).reshape(Hkv, nb, 64, 128)  # dim 16c + 4e + i
         ks = recs[:, :, 8192:8704].copy().view("<u2").reshape(Hkv, nb, 64, 4)
         vs = recs[:, :, 8704:9216].copy().view("<u2").reshape(Hkv, nb, 64, 4)
-        vb = recs[:, :, 9216:].reshape(Hkv, nb, 8, 64, 8, 2).astype(np.int64)   # [g, b, c, lane, token j, e]
-        v = (vb - 128).transpose(0, 1, 2, 4, 3, 5).reshape(Hkv, nb, 64, 128)     # token 8c + j, dim 2l + e
+        vb = recs[:, :, 9216:].reshape(Hkv, nb, 2, 4, 64, 4, 4)              # [g, b, h, tq, lane, word e, byte]
+        v = _bytes4(vb)                                                        # token 16tq + 4e + i, dim 64h + lane
+        v = v.transpose(0, 1, 3, 5, 6, 2, 4).reshape(Hkv, nb, 64, 128)
         km = vm = None
         to_codes = lambda a: a.transpose(1, 2, 0, 3).reshape(Tp, Hkv, 128)[:T].astype(np.int8)  # noqa: E731
         k_codes, v_codes = to_codes(k), to_codes(v)
     else:
-        kw = recs[:, :, :4096].copy().view("<u4").reshape(Hkv, nb, 4, 64, 4).astype(np.int64)  # [g, b, c, slot, word]
-        kq = _nibble_chunk_decode(kw)                                                       # [g, b, c, slot, 32]
-        kq = kq.transpose(0, 1, 3, 2, 4).reshape(Hkv, nb, 64, 128)
+        kb = recs[:, :, :4096].reshape(Hkv, nb, 4, 64, 4, 4)                  # [g, b, group c, slot, word, byte]
+        kq = _nibbles8(kb).transpose(0, 1, 3, 2, 4, 5).reshape(Hkv, nb, 64, 128)  # dim 32c + 8 word + i
         k_codes = (kq[..., 0::2] | (kq[..., 1::2] << 4)).transpose(1, 2, 0, 3).reshape(Tp, Hkv, 64)[:T].astype(np.uint8)
         kp = recs[:, :, 4096:5120].copy().view("<u2").reshape(Hkv, nb, 64, 4, 2)
         vp = recs[:, :, 5120:6144].copy().view("<u2").reshape(Hkv, nb, 64, 4, 2)
         ks, km, vs, vm = kp[..., 0], kp[..., 1], vp[..., 0], vp[..., 1]
-        vb = recs[:, :, 6144:].reshape(Hkv, nb, 4, 64, 16)                       # [g, b, c, lane, token j]
-        v_codes = vb.transpose(1, 2, 4, 0, 3).reshape(Tp, Hkv, 64)[:T].astype(np.uint8)
+        vb = recs[:, :, 6144:].reshape(Hkv, nb, 2, 2, 64, 4, 4)              # [g, b, h, th, lane, word w, byte]
+        vq = _nibbles8(vb)                                                     # token 32th + 8w + i, dim 64h + lane
+        vq = vq.transpose(0, 1, 3, 5, 6, 2, 4).reshape(Hkv, nb, 64, 128)
+        v_codes = (vq[..., 0::2] | (vq[..., 1::2] << 4)).transpose(1, 2, 0, 3).reshape(Tp, Hkv, 64)[:T].astype(np.uint8)
     par = lambda a: None if a is None else a.transpose(1, 2, 0, 3).reshape(Tp, Hkv, 4)[:T].copy().view(np.float16)  # noqa: E731
     return k_codes, par(ks), par(km), v_codes, par(vs), par(vm)
 
@@ -82,16 +90,32 @@ def test_kv_pack_roundtrip_bit_exact(w4a16_lib, bits, T, Hkv):
 
 def test_kv_pack_by_hand(w4a16_lib):
     """INT8: key dims 0..3 of token 0 land in bytes 0..3 as dims 0, 2, 1, 3 (+128);
-    value dims 2l, 2l+1 of token j land at lane l, bytes 2j, 2j+1 of load 0."""
+    value dim d of token 1 lands at lane d, word 0, byte 2 of load 0.
+    INT4: key dims 0..7 of token 0 land in word 0 as bytes (e0|e4<<4, e2|e6<<4,
+    e1|e5<<4, e3|e7<<4); value dim 70 of token 9 lands in the low nibble of byte
+    2 of word 1 of lane 6, load 2 (dims 64..127, tokens 0..31)."""
     T, Hkv = 2, 1
     k = np.zeros((T, Hkv, 128), np.int8)
     k[0, 0, :4] = [-128, 1, 2, 127]
     v = np.zeros((T, Hkv, 128), np.int8)
-    v[1, 0, 6:8] = [5, -5]          # token 1, lane 3
+    v[1, 0, 6:8] = [5, -5]
     s = np.ones((T, Hkv, 4), np.float16)
     blob = w4.w4a16_kv_pack(8, k, s, None, v, s, None)
     assert list(blob[:4]) == [0, 130, 129, 255]
-    assert list(blob[9216 + 3 * 16 + 2: 9216 + 3 * 16 + 4]) == [133, 123]
+    assert blob[9216 + 6 * 16 + 2] == 133 and blob[9216 + 7 * 16 + 2] == 123
+
+    T = 10
+    k4 = np.zeros((T, Hkv, 64), np.uint8)
+    k4[0, 0, :4] = [0x21, 0x43, 0x65, 0x87]   # dims 0..7 = 1..8
+    v4 = np.zeros((T, Hkv, 64), np.uint8)
+    v4[9, 0, 35] = 0x0A                       # dim 70 (even: low nibble) of token 9
+    s4 = np.ones((T, Hkv, 4), np.float16)
+    m4 = np.zeros((T, Hkv, 4), np.float16)
+    blob = w4.w4a16_kv_pack(4, k4, s4, m4, v4, s4, m4)
+    assert list(blob[:4]) == [0x51, 0x73, 0x62, 0x84]
+    at = 6144 + 2 * 1024 + 6 * 16 + 4 * 1 + 2
+    assert blob[at] == 0x0A
+    assert np.count_nonzero(blob[6144:]) == 1
 
 
 def test_kv_pack_and_call_errors(w4a16_lib):
