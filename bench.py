@@ -19,6 +19,13 @@ weights + x + y, per GEMV), the roofline entry of the dominant kernel of the
 reported form (its launches event-timed on the launch stream) and the fp64
 oracle timed on this host's cores as a reported CPU baseline.
 
+--workload gemv4096|llama8b_layer|llama8b_verify|llama70b_step (with --m for
+the activation rows of the verify and 70B workloads) times one of the other
+configurations the same way, with separate launches: the single 4096 x 4096
+GEMV, one 8B layer, the M = 4 / 8 verify batches and the 80-layer 70B step.
+Workloads that fit the 256 MB MALL walk independently seeded copies of their
+weights, at least 512 MB per timed step, and report the time per copy.
+
 --only chain|separate times one form (for counter runs); --copy-calibration
 runs only a plain device copy of 1 GiB three times (the FETCH_SIZE /
 WRITE_SIZE scale of a kernel of known traffic). --codec q4_sym|q5|q8_sym runs
@@ -49,6 +56,17 @@ import workload  # noqa: E402
 METRIC = "W4A16 decode GEMV µs/step and effective HBM GB/s (% of peak), 8B shapes"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "llama8b_step"
+WORKLOAD_TEXT = {
+    "gemv4096": "gemv4096: one GEMV 4096->4096, plain N(0,1) activations",
+    "llama8b_layer": "llama8b_layer: one Llama-3-8B-shaped layer (qkv 4096->6144, o 4096->4096, "
+                     "gate_up 4096->28672, down 14336->4096)",
+    "llama8b_step": "llama8b_step: 32 Llama-3-8B-shaped layers x (qkv 4096->6144, o 4096->4096, "
+                    "gate_up 4096->28672, down 14336->4096)",
+    "llama8b_verify": "llama8b_verify: one Llama-3-8B-shaped layer, speculative-verify rows, "
+                      "plain N(0,1) activations",
+    "llama70b_step": "llama70b_step: 80 Llama-3-70B-shaped layers x (qkv 8192->10240, o 8192->8192, "
+                     "gate_up 8192->57344, down 28672->8192)",
+}
 
 
 # code bits per weight and parameter bytes per group of 32 weights, per codec
@@ -69,23 +87,26 @@ def gemv_bytes(M, N, K, codec="q4"):
     return N * K * bits // 8 + par * N * (K // 32) + palettes + 2 * M * K + 4 * M * N
 
 
-# HBM traffic per launch of a kernel on this workload, from rocprofv3 FETCH_SIZE
-# and WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy; kept
-# only while the kernel is unchanged since the counters were taken.
+# HBM traffic per launch of a kernel on a workload, keyed (workload, M, kernel),
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by the same counters on
+# a 1 GiB device copy; kept only while the kernel is unchanged since the
+# counters were taken.
 TRAFFIC = {
     # (16,754.59 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    "gemv_kernel<1, 1, 1>": 34_366_639,
+    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_366_639,
     # (2,137,225.4 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
-    "chain_kernel<1, 2, 4>": 4_383_722_368,
+    ("llama8b_step", 1, "chain_kernel<1, 2, 4>"): 4_383_722_368,
+    # the 70B step: (65,466.22 KiB x 2.000 + 82.0 KiB x 1.000) per dispatch
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_158_778,
     # weight-code variants: (15,090.47 / 20,096.05 / 28,412.36 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
-    "codec_kernel<1, 1, 1, 1>": 30_958_530,
-    "codec_kernel<2, 1, 1, 1>": 41_209_965,
-    "codec_kernel<3, 1, 1, 1>": 58_251_319,
+    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_958_530,
+    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_209_965,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_251_319,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
-    "codec_kernel<4, 1, 1, 1>": 27_932_673,
+    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
     # KV-cache attention, split pass: (41,441.66 / 48,748.71 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
-    "kv_attn_kernel<8, 4>": 86_137_156,
-    "kv_attn_kernel<4, 4>": 101_101_990,
+    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_137_156,
+    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 101_101_990,
 }
 
 
@@ -114,13 +135,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_inputs(torch, w4, M, dev, threads, codec="q4"):
-    """Generate, pack and upload every GEMV of the step; returns a list of dicts."""
-    items = list(workload.workload_gemvs(WORKLOAD, M))
+def rotation_sets(wl, M, codec):
+    """Independently seeded copies of a workload's weights that one timed step
+    walks through, so that at least ~512 MB is streamed per step and the data
+    cannot be served from the 256 MB MALL."""
+    step = sum(gemv_bytes(m, p.N, p.K, codec) for _, _, p, m in workload.workload_gemvs(wl, M))
+    return max(1, -(-512_000_000 // step))
+
+
+def build_inputs(torch, w4, M, dev, threads, codec="q4", wl=WORKLOAD, sets=1):
+    """Generate, pack and upload every GEMV of the step (times `sets` seeded
+    copies: copy s of a one-layer workload uses layer index s); returns a list
+    of dicts."""
+    base = list(workload.workload_gemvs(wl, M))
+    if sets > 1 and workload.WORKLOADS[wl].layers != 1:
+        raise ValueError("rotation copies are for one-layer workloads")
+    items = [(s if sets > 1 else layer, pi, p, m) for s in range(sets) for layer, pi, p, m in base]
 
     def make(item):
         layer, pi, p, m = item
-        x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, layer, pi, m)
+        x, codes, scale, mn = workload.codec_gemv_inputs(codec, wl, layer, pi, m)
         blob = w4.w4a16_codec_pack(codec, codes, scale, mn)
         return item, x, blob
 
@@ -145,12 +179,12 @@ def launch_step(w4, gemvs, stream_handle, codec="q4"):
             raise w4.W4A16Error(st, "w4a16_codec_gemv")
 
 
-def spot_check(w4, gemvs, torch, codec="q4"):
+def spot_check(w4, gemvs, torch, codec="q4", wl=WORKLOAD):
     """Sampled rows of two GEMVs of the step against the oracle (sanity only)."""
     import oracle
 
-    for g in (gemvs[2], gemvs[3]):
-        x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, g["layer"], g["proj"], g["M"])
+    for g in gemvs[2:4] if len(gemvs) >= 4 else gemvs[:2]:
+        x, codes, scale, mn = workload.codec_gemv_inputs(codec, wl, g["layer"], g["proj"], g["M"])
         rows = np.arange(0, g["N"], max(1, g["N"] // 64))
         y_ref, B = oracle.codecs_ref.gemv_rows(codec, x, codes, scale, mn, rows)
         y = g["y"].cpu().numpy()[:, rows].astype(np.float64)
@@ -158,7 +192,7 @@ def spot_check(w4, gemvs, torch, codec="q4"):
             raise AssertionError(f"bench spot check failed on {g['name']} layer {g['layer']}")
 
 
-def cpu_baseline(budget_s=12.0, codec="q4"):
+def cpu_baseline(budget_s=12.0, codec="q4", wl=WORKLOAD, M=1):
     """The fp64 oracle on whole GEMVs of the same step until ~budget_s of work."""
     import threadpoolctl
 
@@ -168,9 +202,10 @@ def cpu_baseline(budget_s=12.0, codec="q4"):
     done_bytes = 0
     done = []
     t_total = 0.0
+    step = list(workload.workload_gemvs(wl, M))
     with threadpoolctl.threadpool_limits(1):
-        for layer, pi, p, m in workload.workload_gemvs(WORKLOAD, 1):
-            x, codes, scale, mn = workload.codec_gemv_inputs(codec, WORKLOAD, layer, pi, m)
+        for layer, pi, p, m in step:
+            x, codes, scale, mn = workload.codec_gemv_inputs(codec, wl, layer, pi, m)
             t0 = time.perf_counter()
             if codec == "q4":
                 oracle.gemv(x, codes, scale, mn, threads=threads)
@@ -186,12 +221,12 @@ def cpu_baseline(budget_s=12.0, codec="q4"):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle on the first {len(done)} of the step's 128 GEMVs (layer order, "
+        "sample": f"fp64 oracle on the first {len(done)} of the step's {len(step)} GEMVs (layer order, "
                   f"{done[0]} .. {done[-1]}), "
                   f"{done_bytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, "
                   f"{threads} worker threads, BLAS threads limited to 1",
         "us_per_step_extrapolated": round(t_total / done_bytes * sum(
-            gemv_bytes(m, p.N, p.K, codec) for _, _, p, m in workload.workload_gemvs(WORKLOAD, 1)) * 1e6, 1),
+            gemv_bytes(m, p.N, p.K, codec) for _, _, p, m in step) * 1e6, 1),
     }
 
 
@@ -335,7 +370,7 @@ def main_kv(args, torch, w4, dev):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": TRAFFIC.get(kernel),
+            "traffic": TRAFFIC.get((f"llama8b_kv_int{bits}", 1, kernel)),
             "avg_launch_us": round(avg_us, 3),
             "bytes_per_launch": layer_bytes,
         },
@@ -358,13 +393,20 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time separate launches eagerly (counter runs)")
     ap.add_argument("--codec", choices=list(CODEC_BITS), default="q4",
                     help="weight code of the step (the chain runs the 4-bit code only)")
+    ap.add_argument("--workload", choices=list(workload.WORKLOADS), default=WORKLOAD,
+                    help="configuration to time (default: the 32-layer 8B decode step)")
+    ap.add_argument("--m", type=int, default=None, help="activation rows (default: the workload's first)")
     ap.add_argument("--kv", type=int, choices=[8, 4], default=None,
                     help="bench decode attention over an INT8 / INT4 KV cache instead of the GEMVs")
     args = ap.parse_args()
     codec = args.codec
-    if codec != "q4":
+    wl = args.workload
+    M = args.m if args.m is not None else workload.WORKLOADS[wl].ms[0]
+    if M not in workload.WORKLOADS[wl].ms:
+        ap.error(f"--m {M}: {wl} runs M in {workload.WORKLOADS[wl].ms}")
+    if codec != "q4" or wl != WORKLOAD:
         if args.only == "chain":
-            ap.error("the chain streams the 4-bit code only")
+            ap.error("the chain form is timed on the 4-bit 8B decode step only")
         args.only = "separate"
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,15 +430,17 @@ def main():
     if args.kv is not None:
         main_kv(args, torch, w4, dev)
         return
-    M = 1
-
     t0 = time.time()
-    gemvs = build_inputs(torch, w4, M, dev, threads=min(16, len(os.sched_getaffinity(0))), codec=codec)
+    sets = rotation_sets(wl, M, codec) if workload.WORKLOADS[wl].layers == 1 else 1
+    gemvs = build_inputs(torch, w4, M, dev, threads=min(16, len(os.sched_getaffinity(0))), codec=codec, wl=wl,
+                         sets=sets)
     torch.cuda.synchronize()
     for g in gemvs:
         g["xp"], g["pp"], g["yp"] = g["x"].data_ptr(), g["packed"].data_ptr(), g["y"].data_ptr()
-    step_bytes = sum(g["bytes"] for g in gemvs)
-    log(f"[bench] {len(gemvs)} GEMVs, {step_bytes / 1e9:.3f} GB/step, inputs ready in {time.time() - t0:.1f} s")
+    step_bytes = sum(g["bytes"] for g in gemvs) // sets  # one copy of the workload
+    log(f"[bench] {wl} M={M}: {len(gemvs) // sets} GEMVs, {step_bytes / 1e9:.3f} GB/step"
+        f"{f', {sets} seeded copies walked per timed pass' if sets > 1 else ''}, "
+        f"inputs ready in {time.time() - t0:.1f} s")
 
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
@@ -405,9 +449,9 @@ def main():
     with torch.cuda.stream(stream):
         launch_step(w4, gemvs, sh, codec)
     stream.synchronize()
-    spot_check(w4, gemvs, torch, codec)
+    spot_check(w4, gemvs, torch, codec, wl)
 
-    if codec == "q4":
+    if codec == "q4" and wl == WORKLOAD:
         # the decode step as one chained launch: plan and workspace made once
         plan = torch.from_numpy(w4.w4a16_chain_plan(
             [(g["x"], g["packed"], g["y"], g["N"], g["K"]) for g in gemvs], M)).to(dev)
@@ -445,7 +489,7 @@ def main():
                 launch_step(w4, gemvs, stream.cuda_stream, codec)
             torch.cuda.synchronize()
             replay = graph.replay
-        forms["separate"] = time_loop(torch, stream, replay, args.warmup, args.steps)
+        forms["separate"] = time_loop(torch, stream, replay, args.warmup, args.steps) / sets
         log(f"[bench] separate launches ({'eager' if args.no_graph else 'graph'}): "
             f"{forms['separate'] * 1e6:.1f} us/step")
     if args.only in (None, "chain"):
@@ -519,13 +563,14 @@ def main():
         "dtype": CODEC_DTYPE[codec],
         "data": "synthetic",
         "config": {
-            "workload": "llama8b_step: 32 Llama-3-8B-shaped layers x (qkv 4096->6144, o 4096->4096, "
-                        "gate_up 4096->28672, down 14336->4096), M=1, " + CODEC_TEXT[codec],
-            "gemvs_per_step": len(gemvs),
+            "workload": f"{WORKLOAD_TEXT[wl]}, M={M}, " + CODEC_TEXT[codec],
+            "gemvs_per_step": len(gemvs) // sets,
             "bytes_per_step": step_bytes,
             "launch": {"chain": "one w4a16_gemv_chain launch per step, products ordered on the device",
-                       "separate": "128 %s launches per step, replayed from a HIP graph"
-                                   % ("w4a16_gemv" if codec == "q4" else "w4a16_codec_gemv")}[form],
+                       "separate": "%d %s launches per step, replayed from a HIP graph%s"
+                                   % (len(gemvs) // sets, "w4a16_gemv" if codec == "q4" else "w4a16_codec_gemv",
+                                      f" over {sets} seeded copies of the weights (time per copy)"
+                                      if sets > 1 else "")}[form],
             "us_per_step_by_launch_form": {k: round(v * 1e6, 2) for k, v in forms.items()},
         },
         "roofline": {
@@ -535,14 +580,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": TRAFFIC.get(kernel),
+            "traffic": TRAFFIC.get((wl, M, kernel)),
             "avg_launch_us": round(avg_us, 3),
             "bytes_per_launch": round(per_launch),
         },
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on host cores ...")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_budget, codec)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget, codec, wl, M)
     print(json.dumps(line), flush=True)
 
 
