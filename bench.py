@@ -92,16 +92,16 @@ def gemv_bytes(M, N, K, codec="q4"):
 # a 1 GiB device copy; kept only while the kernel is unchanged since the
 # counters were taken.
 TRAFFIC = {
-    # (16,754.59 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_366_639,
+    # (16,749.95 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_357_142,
     # (2,137,225.4 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
-    ("llama8b_step", 1, "chain_kernel<1, 2, 4>"): 4_383_722_368,
-    # the 70B step: (65,466.22 KiB x 2.000 + 82.0 KiB x 1.000) per dispatch
-    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_158_778,
-    # weight-code variants: (15,090.47 / 20,096.05 / 28,412.36 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_958_530,
-    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_209_965,
-    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_251_319,
+    ("llama8b_step", 1, "chain_kernel<1, 2, 4>"): 4_383_722_283,
+    # the 70B step: (65,466.21 KiB x 2.000 + 82.0 KiB x 1.000) per dispatch
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_158_761,
+    # weight-code variants: (15,083.47 / 20,096.30 / 28,412.23 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_944_187,
+    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_210_474,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_251_053,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
     # KV-cache attention, split pass: (41,441.66 / 48,748.71 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)

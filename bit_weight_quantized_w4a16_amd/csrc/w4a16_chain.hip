@@ -211,6 +211,7 @@ __device__ __forceinline__ void cursor_settle(Cursor& u, EntryPtr ents, int coun
 // pass-local index gl[j], and that group's sum (written by the sync wave).
 template <int M, int GPL, int XG>
 struct LdsX {
+  static constexpr bool kRowOuter = false;  // each chunk is an LDS read: walk a tile chunk by chunk
   const u32x4* xl;
   const float* xsl;
   int gl[GPL];

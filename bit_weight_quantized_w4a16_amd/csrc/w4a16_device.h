@@ -210,11 +210,46 @@ __device__ __forceinline__ void load_x(const u32x4* __restrict__ x, int G, const
 // lane's group j of row m, and that group's sum.
 template <int M, int GPL>
 struct RegX {
+  static constexpr bool kRowOuter = true;  // chunks are free to re-read: walk a tile row by row
   const u32x4 (&xv)[M][GPL][4];
   const float (&xs)[M][GPL];
   __device__ __forceinline__ u32x4 x(int m, int j, int d) const { return xv[m][j][d]; }
   __device__ __forceinline__ float sum(int m, int j) const { return xs[m][j]; }
 };
+
+// Visits (row r, chunk d) of group j of a tile: row by row when the
+// accessor's chunks are free to re-read (activations in registers: one row's
+// partial sums are live at a time), chunk by chunk otherwise (activations in
+// LDS: each chunk is read once for the four rows). step(r, d, xq) gets chunk
+// d of every activation row; fold(r) runs after row r's last chunk. Each
+// (row, activation row) sees the same sequence of operations either way.
+template <int M, class XA, class Step, class Fold>
+__device__ __forceinline__ void tile_walk(const XA& xa, int j, Step&& step, Fold&& fold) {
+  if constexpr (XA::kRowOuter) {
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u32x4 xq[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+        step(r, d, xq);
+      }
+      fold(r);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u32x4 xq[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) step(r, d, xq);
+    }
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) fold(r);
+  }
+}
 
 // One lane's partial row sums of one tile over its groups (tile_sums adds
 // them over the wave): acc[r][m] = sum over the lane's groups g of
@@ -239,39 +274,33 @@ __device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const XA& 
     for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+    tile_walk<M>(
+        xa, j,
+        [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
+          const uint32_t w = elem(L.code[r][j], d);
+          const uint32_t w8 = w >> 8;
+          const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
+          const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
+          const uint32_t pc = w8 & 0x000F000Fu;  // k = 8d+4, 8d+5  -> q * 2^-24
+          const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      u32x4 xq[M];  // x[m][8d .. 8d+7] of this group
+          for (int m = 0; m < M; ++m) {
+            lo[r][m] = dot2(pa, elem(xq[m], 0), lo[r][m]);
+            hi[r][m] = dot2(pb, elem(xq[m], 1), hi[r][m]);
+            lo[r][m] = dot2(pc, elem(xq[m], 2), lo[r][m]);
+            hi[r][m] = dot2(pd, elem(xq[m], 3), hi[r][m]);
+          }
+        },
+        [&](int r) __attribute__((always_inline)) {
+          const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
+          const float sc = float(h[0]) * 0x1p20f;
+          const float mn = float(h[1]);
 #pragma unroll
-      for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const uint32_t w = elem(L.code[r][j], d);
-        const uint32_t w8 = w >> 8;
-        const uint32_t pa = w & 0x000F000Fu;   // k = 8d+0, 8d+1  -> q * 2^-24
-        const uint32_t pb = w & 0x00F000F0u;   // k = 8d+2, 8d+3  -> q * 2^-20
-        const uint32_t pc = w8 & 0x000F000Fu;  // k = 8d+4, 8d+5  -> q * 2^-24
-        const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          lo[r][m] = dot2(pa, elem(xq[m], 0), lo[r][m]);
-          hi[r][m] = dot2(pb, elem(xq[m], 1), hi[r][m]);
-          lo[r][m] = dot2(pc, elem(xq[m], 2), lo[r][m]);
-          hi[r][m] = dot2(pd, elem(xq[m], 3), hi[r][m]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-      const f16x2 h = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
-      const float sc = float(h[0]) * 0x1p20f;
-      const float mn = float(h[1]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
-        acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
-      }
-    }
+          for (int m = 0; m < M; ++m) {
+            acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+            acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+          }
+        });
   }
 }
 

@@ -148,25 +148,21 @@ struct CodecQ4Sym {
       for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+      tile_walk<M>(
+          xa, j,
+          [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
+            nibble_dots<M, false>(elem(L.code[r][j], d), 0u, 0u, xq, lo[r], hi[r]);
+          },
+          [&](int r) __attribute__((always_inline)) {
+            const float s = half_of(L.sc[j], r);
+            const float sc = s * 0x1p20f;
+            const float mn = -8.f * s;  // exact
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4 xq[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) nibble_dots<M, false>(elem(L.code[r][j], d), 0u, 0u, xq, lo[r], hi[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const float s = half_of(L.sc[j], r);
-        const float sc = s * 0x1p20f;
-        const float mn = -8.f * s;  // exact
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
-          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
-        }
-      }
+            for (int m = 0; m < M; ++m) {
+              acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+              acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+            }
+          });
     }
   }
 };
@@ -213,28 +209,22 @@ struct CodecQ5 {
       for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+      tile_walk<M>(
+          xa, j,
+          [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
+            const uint32_t h = elem(L.hb[j], r);
+            nibble_dots<M, true>(elem(L.code[r][j], d), h << (4 - d), h >> (4 + d), xq, lo[r], hi[r]);
+          },
+          [&](int r) __attribute__((always_inline)) {
+            const f16x2 hm = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
+            const float sc = float(hm[0]) * 0x1p20f;
+            const float mn = float(hm[1]);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4 xq[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
-          const uint32_t h = elem(L.hb[j], r);
-          nibble_dots<M, true>(elem(L.code[r][j], d), h << (4 - d), h >> (4 + d), xq, lo[r], hi[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const f16x2 hm = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
-        const float sc = float(hm[0]) * 0x1p20f;
-        const float mn = float(hm[1]);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
-          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
-        }
-      }
+            for (int m = 0; m < M; ++m) {
+              acc[r][m] = __builtin_fmaf(sc, __builtin_fmaf(lo[r][m], 16.f, hi[r][m]), acc[r][m]);
+              acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
+            }
+          });
     }
   }
 };
@@ -283,36 +273,31 @@ struct CodecQ8Sym {
       for (int r = 0; r < kTileRows; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) lo[r][m] = hi[r][m] = 0.f;
+      tile_walk<M>(
+          xa, j,
+          [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
+            // x chunk d: k = 8d .. 8d+7 = half d/2, code words 2(d%2), 2(d%2)+1
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {  // x chunk d: k = 8d .. 8d+7 = half d/2, code words 2(d%2), 2(d%2)+1
-        u32x4 xq[M];
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t w = elem(L.code[r][j][d / 2], 2 * (d % 2) + i);
+              const uint32_t p0 = w & 0x00FF00FFu, p1 = (w >> 8) & 0x00FF00FFu;
 #pragma unroll
-        for (int m = 0; m < M; ++m) xq[m] = xa.x(m, j, d);
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const uint32_t w = elem(L.code[r][j][d / 2], 2 * (d % 2) + i);
-            const uint32_t p0 = w & 0x00FF00FFu, p1 = (w >> 8) & 0x00FF00FFu;
+              for (int m = 0; m < M; ++m) {
+                lo[r][m] = dot2(p0, elem(xq[m], 2 * i), lo[r][m]);
+                hi[r][m] = dot2(p1, elem(xq[m], 2 * i + 1), hi[r][m]);
+              }
+            }
+          },
+          [&](int r) __attribute__((always_inline)) {
+            const float s = half_of(L.sc[j], r);
+            const float sc = s * 0x1p24f;
+            const float mn = -128.f * s;  // exact
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-              lo[r][m] = dot2(p0, elem(xq[m], 2 * i), lo[r][m]);
-              hi[r][m] = dot2(p1, elem(xq[m], 2 * i + 1), hi[r][m]);
+              acc[r][m] = __builtin_fmaf(sc, lo[r][m] + hi[r][m], acc[r][m]);
+              acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
             }
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kTileRows; ++r) {
-        const float s = half_of(L.sc[j], r);
-        const float sc = s * 0x1p24f;
-        const float mn = -128.f * s;  // exact
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          acc[r][m] = __builtin_fmaf(sc, lo[r][m] + hi[r][m], acc[r][m]);
-          acc[r][m] = __builtin_fmaf(mn, xa.sum(m, j), acc[r][m]);
-        }
-      }
+          });
     }
   }
 };
