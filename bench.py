@@ -104,9 +104,9 @@ TRAFFIC = {
     ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_251_053,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
-    # KV-cache attention, split pass: (41,441.66 / 48,748.71 KiB x 2.000 + 1,235.0 / 1,235.0 KiB x 1.000)
-    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_137_156,
-    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 101_101_990,
+    # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
+    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_135_991,
+    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_667_525,
 }
 
 

@@ -10,8 +10,8 @@
 //
 // Work decomposition (split-T "flash decoding"):
 // * The cache of a KV head is a run of 64-token blocks. A workgroup of four
-//   waves takes a contiguous range of a head's blocks; its waves take the
-//   blocks round-robin. All GQ query heads that share the KV head are served
+//   (INT8) or eight (INT4) waves takes a contiguous range of a head's blocks;
+//   its waves take the blocks round-robin. All GQ query heads that share the KV head are served
 //   by the same pass over the block, so the cache is read once for all of them.
 // * The two products of a block are small dense contractions over four query
 //   heads (GQ = 4 per KV head in the 8B model), so they run on the matrix
@@ -27,7 +27,7 @@
 // * Phase 2, one lane per head dimension (two halves of 64 dims): the value
 //   codes of four tokens of its dim against the weights of those tokens give
 //   the weighted values of four heads per MFMA.
-// * The four waves' partial results are merged through LDS in a fixed order
+// * The waves' partial results are merged through LDS in a fixed order
 //   and each workgroup writes one partial (maximum, sum of weights, 128
 //   weighted values per query head) to the caller's workspace; a second
 //   kernel merges the partials of each query head, again in a fixed order.
@@ -48,7 +48,10 @@ namespace {
 
 constexpr int kD = 128;          // head size
 constexpr int kBlockTokens = 64;  // tokens per block (one per lane in phase 1)
-constexpr int kWaves = 4;         // waves per workgroup
+// Waves per workgroup: four for INT8 caches, eight for INT4 (measured: the
+// INT4 kernel is faster in larger workgroups with fewer partials per head, the
+// INT8 one in smaller).
+constexpr int waves_of(int bits) { return bits == 8 ? 4 : 8; }
 constexpr int kPartFloats = kD + 2;  // one partial: 128 weighted values, maximum, weight sum
 
 // Bytes of one (KV head, block) record, and offsets inside it.
@@ -107,10 +110,11 @@ __device__ __forceinline__ f4 mfma4(h4 a, h4 b, f4 c) { return __builtin_amdgcn_
 //   head), B = the value codes of four tokens for one dim (lane = dim); the
 //   result gives lane d the weighted values of dim 64h + d for the four heads.
 template <int BITS, int GQ>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(64 * waves_of(BITS))
 kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__ kv, float* __restrict__ part, int T,
                int nb, int bpw, float scale_log2) {
   using R = Rec<BITS>;
+  constexpr int kWaves = waves_of(BITS);
   constexpr int HG = (GQ + 3) / 4;       // groups of four query heads: the rows of one MFMA
   constexpr int kKPar = BITS == 8 ? 8 : 16;  // parameter bytes per token
   const int lane = threadIdx.x & 63;
@@ -506,21 +510,21 @@ int resident_waves(int bits, int gq, int cus, bool have_device) {
   const int bi = bits == 8 ? 0 : 1, gi = gq == 1 ? 0 : gq == 2 ? 1 : gq == 4 ? 2 : 3;
   int occ = cache[bi][gi].load(std::memory_order_relaxed);
   if (occ <= 0) {
-    if (!have_device) return cus * 3 * kWaves;
+    if (!have_device) return cus * 3 * 4;
     const attn_fn fa = bits == 8 ? attn_for<8>(gq) : attn_for<4>(gq);
-    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fa), 64 * kWaves);
+    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fa), 64 * waves_of(bits));
     cache[bi][gi].store(occ, std::memory_order_relaxed);
   }
-  return cus * occ * kWaves;
+  return cus * occ * waves_of(bits);
 }
 
 // Blocks per workgroup: as few as keep every workgroup resident in one round
-// (each wave then walks its blocks with no wave waiting for a free slot),
-// four blocks or more per workgroup (one per wave), a multiple of four.
-int blocks_per_wg(int nb, int Hkv, int resident) {
+// (each wave then walks its blocks with no wave waiting for a free slot), a
+// multiple of the workgroup's wave count (at least one block per wave).
+int blocks_per_wg(int nb, int Hkv, int resident, int waves) {
   int64_t bw = (int64_t(nb) * Hkv + resident - 1) / resident;
   if (bw < 1) bw = 1;
-  return int(4 * bw);
+  return int(waves * bw);
 }
 
 // The most partials a launch can produce for (T, Hq): every workgroup has at
@@ -550,7 +554,7 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int gq = Hq / Hkv;
-  int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, gq, w4a16_host::cu_count(dev), true));
+  int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, gq, w4a16_host::cu_count(dev), true), waves_of(bits));
   if (const int v = w4a16_host::tune("W4A16_TUNE_KV_BPW")) bpw = v < 4 ? 4 : v / 4 * 4;  // sweep builds only
   const int S = (nb + bpw - 1) / bpw;
   const attn_fn fa = bits == 8 ? attn_for<8>(gq) : attn_for<4>(gq);
@@ -565,8 +569,8 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
   void* a1[] = {&qp, &kp, &pp, &t_arg, &nb_arg, &bpw_arg, &sc_arg};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // the events (if any) bracket the split attention pass, the dominant kernel
-  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fa), dim3(S, Hkv), dim3(64 * kWaves), a1, 0, st, start,
-                         stop, 0) != hipSuccess)
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fa), dim3(S, Hkv), dim3(64 * waves_of(bits)), a1, 0, st,
+                         start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   const float* cp = pp;
   void* a2[] = {&cp, &o, &s_arg};
@@ -610,7 +614,7 @@ extern "C" w4a16_status w4a16_kv_launch_shape(int32_t bits, int32_t T, int32_t H
   const bool have_device = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 && hipGetDevice(&dev) == hipSuccess;
   const int cus = have_device ? w4a16_host::cu_count(dev) : 256;
   const int nb = (T + kBlockTokens - 1) / kBlockTokens;
-  const int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, Hq / Hkv, cus, have_device));
+  const int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, Hq / Hkv, cus, have_device), waves_of(bits));
   out[0] = Hq / Hkv;
   out[1] = bpw;
   out[2] = (nb + bpw - 1) / bpw;
