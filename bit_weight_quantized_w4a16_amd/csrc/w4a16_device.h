@@ -347,14 +347,26 @@ __device__ __forceinline__ void store_y(float* p, float v) {
 }
 
 // The tile_sums result of activation row m that lane `lane` stores: lane
-// 16r + m holds output row r's v[m] (M <= 16).
+// 16r + m holds output row r's v[m] (M <= 16; lanes with lane % 16 >= M get
+// an unspecified value and store nothing). A tree of selects on the bits of
+// the index, whose operands pass through empty asm statements: otherwise the
+// compiler turns a select between two array elements into an indexed read of
+// a stack array, and that scratch load waits for every global load in flight.
 template <int M>
 __device__ __forceinline__ float pick_sum(const float (&v)[M], int lane) {
-  float s = v[0];
+  const int i = lane & 15;
+  float t[M];
 #pragma unroll
-  for (int m = 1; m < M; ++m)
-    if ((lane & 15) == m) s = v[m];
-  return s;
+  for (int m = 0; m < M; ++m) t[m] = v[m];
+#pragma unroll
+  for (int k = 1; k < M; k <<= 1)
+#pragma unroll
+    for (int j = 0; j + k < M; j += 2 * k) {
+      float a = t[j + k], b = t[j];
+      asm("" : "+v"(a), "+v"(b));
+      t[j] = (i & k) ? a : b;
+    }
+  return t[0];
 }
 
 // A wave that covers all of K for its tile writes the tile's 4*M results
@@ -365,10 +377,5 @@ __device__ __forceinline__ void store_tile(const float (&v)[M], float* __restric
   const int n = t * kTileRows + (lane >> 4);
   if ((lane & 15) < M && n < N) store_y<COHERENT>(y + size_t(lane & 15) * N + n, s);
 }
-
-// Up to four activation rows the next tile's loads are issued before the
-// current tile is computed (two load buffers); beyond that the kernel is
-// bound by VALU work and the registers go to the x slices instead.
-__host__ __device__ constexpr bool double_buffered(int M) { return M <= 4; }
 
 }  // namespace w4a16_dev

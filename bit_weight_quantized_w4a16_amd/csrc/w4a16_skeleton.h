@@ -39,6 +39,13 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 //            pass, partials carried in LDS).
 constexpr int kDirect = 0, kBlock = 1, kMulti = 2;
 
+// The next tile's loads are issued before the current tile is computed (two
+// load buffers) in every shape except a one-wave workgroup with more than
+// four activation rows, where the second buffer would spill (M = 8: 217
+// VGPRs and 48 bytes of scratch per lane; 210-232 VGPRs without spills in the
+// wider shapes, still two waves per SIMD).
+__host__ __device__ constexpr bool double_buffered(int M, int MODE) { return M <= 4 || MODE != kDirect; }
+
 // Regions of one packed blob, in the units the loads use.
 struct WeightPtrs {
   const u32x4* codes;  // code chunks
@@ -397,7 +404,7 @@ struct CodecPal4 {
 // shared by the waves on one SIMD.
 template <class C>
 __host__ __device__ constexpr int max_waves_of(int M, int GPL) {
-  return (16 * M * GPL + (double_buffered(M) ? 2 : 1) * C::kTileVgprs * GPL + 6 * M + 30) <= 128 ? 16 : 8;
+  return (16 * M * GPL + (double_buffered(M, kBlock) ? 2 : 1) * C::kTileVgprs * GPL + 6 * M + 30) <= 128 ? 16 : 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -522,7 +529,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
     fetch(0, la);
     fetch_x(0);  // after the first tile's loads, so both latencies overlap
     int e = 0;
-    if constexpr (double_buffered(M)) {
+    if constexpr (double_buffered(M, MODE)) {
       while (e + 2 < n_items) {
         fetch(e + 1, lb);
         __builtin_amdgcn_sched_barrier(0);
