@@ -101,7 +101,7 @@ TRAFFIC = {
     # weight-code variants: (15,083.47 / 20,096.30 / 28,412.23 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_944_187,
     ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_210_474,
-    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_251_053,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_232_208,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
     # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)

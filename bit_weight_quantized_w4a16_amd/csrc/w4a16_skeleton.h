@@ -622,13 +622,33 @@ LaunchShape choose_shape(int M, int G) {
 // each walking an equal share of the tiles. A workgroup reads its x slices
 // once per block, so wide workgroups (long K split over four or more waves, a
 // large x) take enough tiles per block for about one workgroup per CU;
-// narrower ones fill the resident slots first.
+// narrower ones fill the resident slots first. When that leaves more blocks
+// than resident workgroups, the first workgroups walk one block more than
+// the others; the tiles per block are then raised to whatever gives the
+// busiest CU the fewest tiles, with workgroup w counted on CU w % cus (7168
+// tiles over 2048 slots: 4 per block, 28 tiles on every CU, instead of 3 per
+// block and 27 or 30 tiles per CU).
 inline void grid_of(int T, int waves, bool direct, int cus, int occ, int& tpb, int& grid) {
   const int max_grid = cus * occ;
+  auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
   tpb = direct ? 1 : waves >= 4 ? T / cus : T / max_grid;
   tpb = tpb < 1 ? 1 : tpb > w4a16_dev::kTilesPerBlock ? w4a16_dev::kTilesPerBlock : tpb;
-  const int units = (T + tpb - 1) / tpb;
-  grid = units < max_grid ? units : max_grid;
+  if (!direct && cdiv(T, tpb) > max_grid) {
+    auto busiest_cu = [&](int b) {
+      const int blocks = cdiv(T, b), g = blocks < max_grid ? blocks : max_grid;
+      return b * (cdiv(g, cus) * (blocks / g) + cdiv(blocks % g, cus));
+    };
+    int best = busiest_cu(tpb);
+    for (int b = tpb + 1; b <= w4a16_dev::kTilesPerBlock; ++b) {
+      const int v = busiest_cu(b);
+      if (v < best) {
+        best = v;
+        tpb = b;
+      }
+    }
+  }
+  const int blocks = cdiv(T, tpb);
+  grid = blocks < max_grid ? blocks : max_grid;
 }
 
 }  // namespace w4a16_host
