@@ -86,6 +86,18 @@ def test_codec_llama8b_layer_sampled(w4a16_lib, codec, M):
 
 
 @pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("M,N,K", [(5, 24579, 2080), (8, 8195, 2080)])
+def test_codec_several_tiles_per_workgroup_sampled(w4a16_lib, codec, M, N, K):
+    """Workgroups walk several tiles (alternating load buffers and their tail) at M > 4."""
+    print(f"[codec shape] {codec} M={M} N={N} K={K}", flush=True)
+    x, codes, scale, mn = workload.random_codec_problem(codec, M * 977 + N, M, N, K, outliers=True)
+    y = run_codec(codec, x, codes, scale, mn)
+    rows = _sample_rows(N, M)
+    y_ref, B = C.gemv_rows(codec, x, codes, scale, mn, rows)
+    check(y[:, rows], y_ref, B, f"{codec} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("codec", CODECS)
 def test_codec_bitwise_repeatable(w4a16_lib, codec):
     x, codes, scale, mn = workload.random_codec_problem(codec, 3, 2, 1000, 4096, outliers=True)
     a = run_codec(codec, x, codes, scale, mn)

@@ -68,6 +68,21 @@ def test_small_shapes_full(w4a16_lib, M, N, K):
     check(y, y_ref, B, f"M={M} N={N} K={K}")
 
 
+# Enough tiles that a workgroup walks several of them (two load buffers
+# alternating, then a tail of one or two tiles) at 5..8 activation rows, with
+# ragged N and, at K = 4128, a ragged K slot of a three-wave split.
+SEVERAL_TILES = [(5, 24579, 2080), (6, 16387, 2080), (7, 12291, 4128), (8, 8195, 2080)]
+
+
+@pytest.mark.parametrize("M,N,K", SEVERAL_TILES)
+def test_several_tiles_per_workgroup_full(w4a16_lib, M, N, K):
+    print(f"[shape] M={M} N={N} K={K}", flush=True)
+    x, codes, scale, mn = workload.random_problem(M * 977 + N, M, N, K, outliers=True)
+    y = run_gpu(x, codes, scale, mn)
+    y_ref, B = oracle.gemv(x, codes, scale, mn, threads=8)
+    check(y, y_ref, B, f"M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M,K", [(1, 131072), (1, 131104), (8, 32800), (4, 32768)])
 def test_long_k_multi_pass(w4a16_lib, M, K):
     """K beyond one pass of a workgroup: partial sums carried across passes."""
