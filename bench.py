@@ -17,7 +17,11 @@ The faster one is the reported value. Printed: one JSON line with the whole-step
 throughput in algorithmic GB/s (N*K/2 code bytes + 4 bytes of scale/min per 32
 weights + x + y, per GEMV), the roofline entry of the dominant kernel of the
 reported form (its launches event-timed on the launch stream) and the fp64
-oracle timed on this host's cores as a reported CPU baseline.
+oracle timed on this host's cores as a reported CPU baseline. The roofline
+entry is taken against the roof the kernel would hit first: the HBM peak, or,
+when its 2*M*N*K flops take longer at the fp32 vector peak than its bytes at
+the HBM peak (M >= 7), that vector peak; the other roof's fraction is given
+beside it.
 
 --workload gemv4096|llama8b_layer|llama8b_verify|llama70b_step (with --m for
 the activation rows of the verify and 70B workloads) times one of the other
@@ -55,6 +59,9 @@ import workload  # noqa: E402
 
 METRIC = "W4A16 decode GEMV µs/step and effective HBM GB/s (% of peak), 8B shapes"
 HBM_PEAK_GBS = 8000.0
+# fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 4 flops per lane
+# per v_dot2_f32_f16 (two products and two adds), the same as packed fp32 FMA
+VALU_PEAK_TFLOPS = 157.3
 WORKLOAD = "llama8b_step"
 WORKLOAD_TEXT = {
     "gemv4096": "gemv4096: one GEMV 4096->4096, plain N(0,1) activations",
@@ -514,6 +521,7 @@ def main():
     if form == "chain":
         kernel = w4.chain_launch_shape(M)["kernel"]
         launch_bytes = [step_bytes]
+        launch_flops = [sum(2 * g["M"] * g["N"] * g["K"] for g in gemvs) // sets]
         with torch.cuda.stream(stream):
             for _ in range(args.steps):
                 a, b = timed_events()
@@ -527,6 +535,7 @@ def main():
             by_kernel[g["kernel"]] = by_kernel.get(g["kernel"], 0) + g["bytes"]
         kernel = max(by_kernel, key=by_kernel.get)
         launch_bytes = [g["bytes"] for g in gemvs if g["kernel"] == kernel]
+        launch_flops = [2 * g["M"] * g["N"] * g["K"] for g in gemvs if g["kernel"] == kernel]
         with torch.cuda.stream(stream):
             for _ in range(max(1, args.steps // 4)):
                 for g in gemvs:
@@ -543,6 +552,15 @@ def main():
     avg_us = sum(a.elapsed_time(b) for a, b in marks) / len(marks) * 1e3
     per_launch = sum(launch_bytes) / len(launch_bytes)
     achieved = per_launch / (avg_us * 1e-6) / 1e9
+    flops_per_launch = sum(launch_flops) / len(launch_flops)
+    achieved_tflops = flops_per_launch / (avg_us * 1e-6) / 1e12
+    # the roof the launch would hit first: streaming its bytes at the HBM peak,
+    # or its 2*M*N*K flops at the vector peak (from M = 7 on)
+    alu_bound = flops_per_launch / (VALU_PEAK_TFLOPS * 1e12) > per_launch / (HBM_PEAK_GBS * 1e9)
+    hbm_view = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    alu_view = {"achieved": round(achieved_tflops, 3), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4)}
     log(f"[bench] {kernel}: avg {avg_us:.2f} us per launch, {per_launch / 1e6:.2f} MB per launch, "
         f"{achieved:.1f} GB/s")
 
@@ -574,15 +592,15 @@ def main():
             "us_per_step_by_launch_form": {k: round(v * 1e6, 2) for k, v in forms.items()},
         },
         "roofline": {
-            "bound": "hbm",
+            "bound": "alu" if alu_bound else "hbm",
             "kernel": kernel,
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            **(alu_view if alu_bound else hbm_view),
             "traffic": TRAFFIC.get((wl, M, kernel)),
             "avg_launch_us": round(avg_us, 3),
             "bytes_per_launch": round(per_launch),
+            "flops_per_launch": round(flops_per_launch),
+            # the same launches against the other roof
+            ("hbm" if alu_bound else "alu"): hbm_view if alu_bound else alu_view,
         },
     }
     if not args.no_cpu_baseline:
