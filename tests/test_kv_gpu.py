@@ -2,7 +2,8 @@
 against the fp64 oracle: |o - o_ref| <= 1e-3 * sum_t p_t |v_hat_t| + 1e-5 per
 element. Ragged token counts (partial last block, fewer blocks than waves),
 every query-heads-per-KV-head ratio, the full 8B contexts of the page's KV
-budget, a sharply peaked softmax, repeatability and workspace reuse.
+budget, a merge over several chunks of partials, a sharply peaked softmax,
+repeatability and workspace reuse.
 """
 import numpy as np
 import pytest
@@ -64,6 +65,21 @@ def test_kv_full_context_8b(w4a16_lib, bits):
     o = run_kv(bits, q, cache)
     o_ref, B = A.attention(bits, q, *cache)
     check(o, o_ref, B, f"bits={bits} T={T}")
+
+
+@pytest.mark.parametrize("bits,T,Hq", [(8, 40000, 4), (4, 80000, 8)])
+def test_kv_merge_over_several_chunks(w4a16_lib, bits, T, Hq):
+    """One KV head over a long context: the split pass gives each query head
+    more partials than the merge kernel takes in one chunk (96), so the merge
+    walks several chunks and carries its running maximum across them."""
+    shape = w4.w4a16_kv_launch_shape(bits, T, Hq, 1)
+    print(f"[kv chunks] bits={bits} T={T} Hq={Hq} Hkv=1 {shape}", flush=True)
+    assert shape["workgroups_per_kv_head"] > 96, shape
+    cache = workload.kv_cache(bits, 61, 0, T, 1)
+    q = workload.kv_query(61, 0, Hq)
+    o = run_kv(bits, q, cache)
+    o_ref, B = A.attention(bits, q, *cache)
+    check(o, o_ref, B, f"bits={bits} T={T} Hq={Hq} Hkv=1")
 
 
 @pytest.mark.parametrize("bits", [8, 4])
