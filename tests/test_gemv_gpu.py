@@ -199,6 +199,30 @@ def test_fp16_extremes_in_x(w4a16_lib):
     check(y, y_ref, B, "fp16 extremes")
 
 
+def test_beyond_4gib_of_weights_sampled(w4a16_lib):
+    """A 5.4 GB packed matrix (ragged N = 262,147 rows at K = 32,768): the last
+    rows' code chunks lie more than 2^32 bytes into the blob, so every load
+    address is formed in 64 bits. Compared on sampled rows, the last eight
+    included."""
+    M, N, K = 1, 262147, 32768
+    print(f"[shape] M={M} N={N} K={K} ({w4.w4a16_packed_bytes(N, K) / 1e9:.2f} GB packed)", flush=True)
+    # seeded, non-periodic bytes drawn directly (the workload recipe's fp64
+    # draws take most of a minute at this size): codes are uniform bytes,
+    # scale and min uniform binary16 bit patterns in [0.001, 0.01] and [-0.08, 0]
+    rng = np.random.default_rng(0x4D415847)
+    codes = np.frombuffer(rng.bytes(N * K // 2), dtype=np.uint8).reshape(N, K // 2)
+    lo, hi = np.float16(0.001).view(np.uint16), np.float16(0.01).view(np.uint16)
+    scale = rng.integers(lo, hi + 1, size=(N, K // 32), dtype=np.uint16).view(np.float16)
+    mn = (rng.integers(0, np.float16(0.08).view(np.uint16) + 1, size=(N, K // 32), dtype=np.uint16)
+          | np.uint16(0x8000)).view(np.float16)
+    x = workload.activations(77, 0, 0, M, K, True)
+    assert codes.nbytes > 2**32
+    y = run_gpu(x, codes, scale, mn)
+    rows = sample_rows(N, 77, count=256)
+    y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
+    check(y[:, rows], y_ref, B, f"M={M} N={N} K={K}")
+
+
 # ------------------------------------------------------ named Llama workloads
 
 def test_gemv4096_full(w4a16_lib):
