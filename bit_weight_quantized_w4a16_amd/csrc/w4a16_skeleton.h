@@ -464,24 +464,56 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
 
   if constexpr (MODE == kMulti) {
     // passes over K outermost within a block: x of pass c is fetched once at
-    // the top of the pass and stays in registers for the block's tiles
+    // the top of the pass and stays in registers for the block's tiles. With
+    // one group per lane and the 256-register budget of at most eight waves
+    // (M >= 3), the next tile's loads are issued before the current tile is
+    // computed, as in the single-pass loop below; the 128-register budget of
+    // wider workgroups has no room for the second buffer.
+    constexpr bool kPrefetch = GPL == 1 && max_waves_of<C>(M, GPL) <= 8;
     for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
       const int ntiles = min(tpb, T - b * tpb);
       for (int c = 0; c < nchunks; ++c) {
-        fetch_x(c);
         int g0[GPL];
         bases(c, g0);
-        for (int tb = 0; tb < ntiles; ++tb) {
-          Loads la;
-          C::template fetch<GPL>(wp, N, G, b * tpb + tb, g0, lane, la);
+        auto fetch_tb = [&](int tb, Loads& L) { C::template fetch<GPL>(wp, N, G, b * tpb + tb, g0, lane, L); };
+        auto work = [&](const Loads& L, int tb) {
           float acc[kTileRows][M], v[M];
-          C::template compute<M, GPL>(la, RegX<M, GPL>{xv, xs}, acc);
+          C::template compute<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
           tile_sums<M>(acc, v);
           if ((lane & 15) == 0) {  // the first lane of each 16-lane row: output row lane / 16
             const int r = lane >> 4;
 #pragma unroll
             for (int m = 0; m < M; ++m) part[tb][r][m][wave] = (c == 0 ? 0.f : part[tb][r][m][wave]) + v[m];
           }
+        };
+        Loads la, lb;
+        fetch_tb(0, la);
+        fetch_x(c);  // after the pass's first tile loads, so both latencies overlap
+        int tb = 0;
+        if constexpr (!kPrefetch) {
+          work(la, 0);
+          for (tb = 1; tb < ntiles; ++tb) {
+            fetch_tb(tb, la);
+            work(la, tb);
+          }
+          continue;
+        }
+        while (tb + 2 < ntiles) {
+          fetch_tb(tb + 1, lb);
+          __builtin_amdgcn_sched_barrier(0);
+          work(la, tb);
+          fetch_tb(tb + 2, la);
+          __builtin_amdgcn_sched_barrier(0);
+          work(lb, tb + 1);
+          tb += 2;
+        }
+        if (ntiles - tb == 2) {
+          fetch_tb(tb + 1, lb);
+          __builtin_amdgcn_sched_barrier(0);
+          work(la, tb);
+          work(lb, tb + 1);
+        } else {
+          work(la, tb);
         }
       }
       reduce_block(b);
