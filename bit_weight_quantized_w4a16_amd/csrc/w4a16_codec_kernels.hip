@@ -132,7 +132,8 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
   const int T = (l.N + kTileRows - 1) / kTileRows;
   int tpb = 0, grid = 0;
   w4a16_host::grid_of(T, s.waves, mode == kDirect, w4a16_host::cu_count(dev),
-                      occupancy(l.M, s.gi, mode, s.waves, fn), tpb, grid);
+                      w4a16_host::resident_workgroups(l.M, s.waves, occupancy(l.M, s.gi, mode, s.waves, fn)), tpb,
+                      grid);
   const uint8_t* base = static_cast<const uint8_t*>(l.packed);
   const u32x4* xp = static_cast<const u32x4*>(l.x);
   const u32x4* cp = reinterpret_cast<const u32x4*>(base);

@@ -161,7 +161,7 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   const int T = (N + kTileRows - 1) / kTileRows;
   const bool direct = mode == kDirect;
   // all workgroups resident at once, each walking an equal share of the tiles
-  int occ = occupancy(M, shape.gi, mode, shape.waves, fn);
+  int occ = w4a16_host::resident_workgroups(M, shape.waves, occupancy(M, shape.gi, mode, shape.waves, fn));
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
   int tpb = 0, grid = 0;
   w4a16_host::grid_of(T, shape.waves, direct, w4a16_host::cu_count(dev), occ, tpb, grid);

@@ -650,6 +650,18 @@ LaunchShape choose_shape(int M, int G) {
   return best;
 }
 
+// Resident workgroups per CU that a launch uses. From four activation rows
+// on, a wave's x slice (M * 64 bytes per lane, 16 KiB at M = 4) is as large
+// as several tiles of weights, and each workgroup loads it once per block:
+// at most two waves per SIMD are kept resident, so each workgroup walks more
+// tiles per x slice (the 8B gate_up at M = 4: 4 workgroups of 7 tiles per
+// CU instead of 8 of 4). At M = 8 the register file already allows no more.
+inline int resident_workgroups(int M, int waves, int occ) {
+  if (M < 4) return occ;
+  const int cap = waves >= 8 ? 1 : 8 / waves;
+  return occ < cap ? occ : cap;
+}
+
 // Tiles per block and grid of a launch: every workgroup resident at once,
 // each walking an equal share of the tiles. A workgroup reads its x slices
 // once per block, so wide workgroups (long K split over four or more waves, a
