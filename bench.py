@@ -111,6 +111,7 @@ TRAFFIC = {
     ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_232_208,
     ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_935_856,
     ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_686_400,
+    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_825,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
     # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
