@@ -1,6 +1,7 @@
 """GPU tests of the decode-step chain (w4a16_gemv_chain) through the C ABI.
 
-* parity with the fp64 oracle on mixed shapes, every M;
+* parity with the fp64 oracle on mixed shapes, every M, and on one full
+  8B-shaped layer (sampled rows);
 * a real dependency: product 1 reads product 0's fp32 output as its binary16
   input, so running it before product 0 finished would read stale memory;
 * agreement with separate w4a16_gemv launches (bitwise where the launch
@@ -72,6 +73,24 @@ def test_chain_mixed_shapes_vs_oracle(w4a16_lib, M):
     for it, (x, codes, scale, mn) in zip(ch.items, problems):
         y_ref, B = oracle.gemv(x, codes, scale, mn)
         check(it["y"].cpu().numpy().astype(np.float64), y_ref, B, f"M={M} N={it['N']} K={it['K']}")
+    assert_workspace_clean(ch)
+
+
+def test_chain_llama8b_layer_sampled(w4a16_lib):
+    """One 8B-shaped layer (qkv, o, gate_up, down at their full sizes, M = 1)
+    through the chain kernel the bench times, compared on sampled rows."""
+    problems = [workload.gemv_inputs("llama8b_layer", 0, proj, 1) for proj in range(4)]
+    print(f"[chain] llama8b_layer M=1 {w4.chain_launch_shape(1)}", flush=True)
+    ch = Chain(problems, 1)
+    ch.plan()
+    ch.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    for it, (x, codes, scale, mn) in zip(ch.items, problems):
+        N = it["N"]
+        rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N), rng.choice(N, 256, replace=False)]))
+        y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
+        check(it["y"].cpu().numpy().astype(np.float64)[:, rows], y_ref, B, f"llama8b_layer N={N} K={it['K']}")
     assert_workspace_clean(ch)
 
 
