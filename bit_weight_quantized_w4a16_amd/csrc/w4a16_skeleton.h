@@ -666,28 +666,38 @@ inline int resident_workgroups(int M, int waves, int occ) {
 // each walking an equal share of the tiles. A workgroup reads its x slices
 // once per block, so wide workgroups (long K split over four or more waves, a
 // large x) take enough tiles per block for about one workgroup per CU;
-// narrower ones fill the resident slots first. When that leaves more blocks
-// than resident workgroups, the first workgroups walk one block more than
-// the others; the tiles per block are then raised to whatever gives the
-// busiest CU the fewest tiles, with workgroup w counted on CU w % cus (7168
-// tiles over 2048 slots: 4 per block, 28 tiles on every CU, instead of 3 per
-// block and 27 or 30 tiles per CU).
+// narrower ones fill the resident slots first. That choice stands if it
+// gives the busiest CU (workgroup w counted on CU w % cus, the first
+// workgroups walking one block more when blocks outnumber them) as few tiles
+// as any tiles-per-block count can. Otherwise the count is changed to the
+// best one: for narrow workgroups the smallest above the first choice (7168
+// tiles over 2048 slots: 4 per block, 28 tiles on every CU, not 3 per block
+// and 27 or 30 per CU), for wide ones the largest (2560 tiles of 4-wave
+// workgroups: 5 per block on 512 workgroups, 10 tiles per CU, not 8 per
+// block on 320 workgroups and 16 tiles on a fifth of the CUs).
 inline void grid_of(int T, int waves, bool direct, int cus, int occ, int& tpb, int& grid) {
   const int max_grid = cus * occ;
   auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
-  tpb = direct ? 1 : waves >= 4 ? T / cus : T / max_grid;
+  const bool wide = waves >= 4;
+  tpb = direct ? 1 : wide ? T / cus : T / max_grid;
   tpb = tpb < 1 ? 1 : tpb > w4a16_dev::kTilesPerBlock ? w4a16_dev::kTilesPerBlock : tpb;
-  if (!direct && cdiv(T, tpb) > max_grid) {
+  if (!direct) {
     auto busiest_cu = [&](int b) {
       const int blocks = cdiv(T, b), g = blocks < max_grid ? blocks : max_grid;
       return b * (cdiv(g, cus) * (blocks / g) + cdiv(blocks % g, cus));
     };
     int best = busiest_cu(tpb);
-    for (int b = tpb + 1; b <= w4a16_dev::kTilesPerBlock; ++b) {
-      const int v = busiest_cu(b);
-      if (v < best) {
-        best = v;
-        tpb = b;
+    for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b) best = busiest_cu(b) < best ? busiest_cu(b) : best;
+    if (busiest_cu(tpb) > best) {
+      const int first = tpb;
+      tpb = 0;
+      for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b) {
+        if (busiest_cu(b) != best) continue;
+        if (wide ? b > tpb : (b > first && tpb == 0)) tpb = b;
+      }
+      if (tpb == 0) {  // narrow, and every best count lies below the first choice: the largest of them
+        for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b)
+          if (busiest_cu(b) == best) tpb = b;
       }
     }
   }
