@@ -104,14 +104,14 @@ TRAFFIC = {
     # (2,137,225.4 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
     ("llama8b_step", 1, "chain_kernel<1, 2, 4>"): 4_383_722_283,
     # the 70B step: (65,466.21 KiB x 2.000 + 82.0 KiB x 1.000) per dispatch
-    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_158_761,
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_148_314,
     # weight-code variants: (15,083.47 / 20,096.30 / 28,412.23 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_944_187,
     ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_210_474,
     ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_232_208,
     ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_935_856,
     ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_686_400,
-    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_825,
+    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_570_565,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
     # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
