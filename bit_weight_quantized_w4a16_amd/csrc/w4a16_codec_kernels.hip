@@ -131,7 +131,7 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int T = (l.N + kTileRows - 1) / kTileRows;
   int tpb = 0, grid = 0;
-  w4a16_host::grid_of(T, s.waves, mode == kDirect, w4a16_host::cu_count(dev),
+  w4a16_host::grid_of(T, l.M, s.waves, mode == kDirect, w4a16_host::cu_count(dev),
                       w4a16_host::resident_workgroups(l.M, s.waves, occupancy(l.M, s.gi, mode, s.waves, fn)), tpb,
                       grid);
   const uint8_t* base = static_cast<const uint8_t*>(l.packed);

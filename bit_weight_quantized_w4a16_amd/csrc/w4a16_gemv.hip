@@ -164,7 +164,7 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   int occ = w4a16_host::resident_workgroups(M, shape.waves, occupancy(M, shape.gi, mode, shape.waves, fn));
   if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
   int tpb = 0, grid = 0;
-  w4a16_host::grid_of(T, shape.waves, direct, w4a16_host::cu_count(dev), occ, tpb, grid);
+  w4a16_host::grid_of(T, M, shape.waves, direct, w4a16_host::cu_count(dev), occ, tpb, grid);
   if (const int v = tune("W4A16_TUNE_TPB")) {  // sweep builds only
     tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
     const int units = (T + tpb - 1) / tpb, max_grid = w4a16_host::cu_count(dev) * occ;

@@ -666,16 +666,18 @@ inline int resident_workgroups(int M, int waves, int occ) {
 // each walking an equal share of the tiles. A workgroup reads its x slices
 // once per block, so wide workgroups (long K split over four or more waves, a
 // large x) take enough tiles per block for about one workgroup per CU;
-// narrower ones fill the resident slots first. That choice stands if it
-// gives the busiest CU (workgroup w counted on CU w % cus, the first
-// workgroups walking one block more when blocks outnumber them) as few tiles
-// as any tiles-per-block count can. Otherwise the count is changed to the
-// best one: for narrow workgroups the smallest above the first choice (7168
-// tiles over 2048 slots: 4 per block, 28 tiles on every CU, not 3 per block
-// and 27 or 30 per CU), for wide ones the largest (2560 tiles of 4-wave
-// workgroups: 5 per block on 512 workgroups, 10 tiles per CU, not 8 per
-// block on 320 workgroups and 16 tiles on a fifth of the CUs).
-inline void grid_of(int T, int waves, bool direct, int cus, int occ, int& tpb, int& grid) {
+// narrower ones fill the resident slots first. That choice stands if it gives
+// the busiest CU (workgroup w counted on CU w % cus, the first workgroups
+// walking one block more when blocks outnumber them) as few tiles as any
+// tiles-per-block count can and, from four activation rows on, fits in one
+// round of resident workgroups when some such count does. Otherwise the
+// count is changed to a qualifying one: for narrow workgroups the smallest
+// above the first choice (7168 tiles over 2048 slots: 4 per block, 28 tiles
+// on every CU, not 3 per block and 27 or 30 per CU), for wide ones the
+// largest (2560 tiles of 4-wave workgroups: 5 per block on 512 workgroups,
+// 10 tiles per CU, not 8 per block on 320 workgroups and 16 tiles on a fifth
+// of the CUs).
+inline void grid_of(int T, int M, int waves, bool direct, int cus, int occ, int& tpb, int& grid) {
   const int max_grid = cus * occ;
   auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
   const bool wide = waves >= 4;
@@ -686,18 +688,26 @@ inline void grid_of(int T, int waves, bool direct, int cus, int occ, int& tpb, i
       const int blocks = cdiv(T, b), g = blocks < max_grid ? blocks : max_grid;
       return b * (cdiv(g, cus) * (blocks / g) + cdiv(blocks % g, cus));
     };
+    // a count qualifies if it reaches the fewest tiles on the busiest CU and,
+    // from four activation rows on (a large x slice per wave), also fits in
+    // one round of resident workgroups if any such count does: one round
+    // loads each workgroup's x slices once
+    auto one_round = [&](int b) { return cdiv(T, b) <= max_grid; };
     int best = busiest_cu(tpb);
     for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b) best = busiest_cu(b) < best ? busiest_cu(b) : best;
-    if (busiest_cu(tpb) > best) {
+    bool round_ok = false;
+    for (int b = 1; b <= w4a16_dev::kTilesPerBlock && M >= 4; ++b) round_ok = round_ok || (busiest_cu(b) == best && one_round(b));
+    auto qualifies = [&](int b) { return busiest_cu(b) == best && (!round_ok || one_round(b)); };
+    if (!qualifies(tpb)) {
       const int first = tpb;
       tpb = 0;
       for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b) {
-        if (busiest_cu(b) != best) continue;
+        if (!qualifies(b)) continue;
         if (wide ? b > tpb : (b > first && tpb == 0)) tpb = b;
       }
-      if (tpb == 0) {  // narrow, and every best count lies below the first choice: the largest of them
+      if (tpb == 0) {  // narrow, and every qualifying count lies below the first choice: the largest of them
         for (int b = 1; b <= w4a16_dev::kTilesPerBlock; ++b)
-          if (busiest_cu(b) == best) tpb = b;
+          if (qualifies(b)) tpb = b;
       }
     }
   }
