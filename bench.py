@@ -109,8 +109,8 @@ TRAFFIC = {
     ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_944_187,
     ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_210_474,
     ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_232_208,
-    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_935_856,
-    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_686_400,
+    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_903_370,
+    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_620_582,
     ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_570_565,
     # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
     ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
