@@ -186,7 +186,8 @@ def chain_launch_shape(M: int) -> dict:
     st = lib().w4a16_chain_launch_shape(M, out)
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_chain_launch_shape")
-    return {"M": out[0], "gpl": out[1], "ring": out[2], "kernel": f"chain_kernel<{out[0]}, {out[1]}, {out[2]}>"}
+    return {"M": out[0], "ring": out[1], "compute_waves": out[2],
+            "kernel": f"chain_kernel<{out[0]}, {out[1]}, {out[2]}>"}
 
 
 def _ptr(t) -> int:

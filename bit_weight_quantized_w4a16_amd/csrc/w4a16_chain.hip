@@ -4,39 +4,53 @@
 // Why: a decode step is the same list of matrix-vector products every token
 // (the tight decode loop of the core-modules page, section 5.2), and its
 // scheduler notes (section 5.3) call for fetching the next product's weights
-// while other work runs. On an MI355X a kernel boundary costs about 1.5 us of
-// launch gap plus the ramp of the next kernel, about as long as streaming
-// 10 MB of weights; a 32-layer 8B step has 128 such boundaries.
+// while other work runs. On an MI355X a kernel boundary costs several
+// microseconds (dispatch ramp, cold first loads, drain), paid 128 times by a
+// 32-layer 8B step even when every weight byte is already cached; the weights
+// of later products never depend on earlier results, so one launch can keep
+// HBM streaming straight through the ordering points between products.
 //
-// How: one workgroup per CU, eight waves with two roles.
+// How: one workgroup per CU, twelve waves with two roles.
 //
-// * Seven compute waves only stream weights and do arithmetic. Product i's
-//   4-row tiles are split evenly over the workgroups; inside a workgroup a
-//   unit of work is (tile, K segment of 64*GPL groups), handed to the compute
-//   waves round-robin. Each wave keeps RING units' loads in registers and
-//   issues the loads of unit e+RING-1 before computing unit e, across product
-//   boundaries: weights never depend on earlier results, so HBM keeps
-//   streaming while the products' ordering points are reached. A unit's
-//   result (4 rows x M partial sums) goes to LDS; a compute wave never
-//   stores to global memory and never waits for its own stores, which on
-//   gfx9 would also wait for every weight load it has in flight.
+// * Four loader waves stream weights and nothing else. The workgroup's work
+//   is a sequence of units (product, 4-row tile, K segment of 64 groups of
+//   32 weights); a unit's bytes are 4 rows x 1 KiB of code chunks plus 1 KiB
+//   of scale/min entries. A loader keeps five units of 128-bit loads in
+//   flight in its registers and copies each unit, once it has landed, into a
+//   ring of LDS slots, unit after unit and product after product, as fast as
+//   slots free up. Loaders never wait on an ordering point, so up to the ring
+//   plus the loaders' registers of the next products' weights (about 220 KiB
+//   per CU) stream in while the current product completes.
 //
-// * One sync wave does everything that has to wait on memory: it stages each
-//   product's activations into LDS (coherent loads, since an earlier product
-//   of the same launch may have written them on another XCD), publishes them
-//   to the compute waves through an LDS counter, sums the segment partials in
-//   a fixed order and writes y with coherent stores, and takes part in the
-//   device-wide ordering between products.
+// * Eight compute waves take the units round-robin. Before a product's units
+//   they stage its activations into LDS together (each lane one group of 32
+//   values and its sum). A unit is computed from its slot and the staged
+//   activations; its 4 x M wave sums go to LDS, and the wave that completes
+//   the last segment of a tile adds the segment sums in order and stores y.
+//   The weights arrive through LDS, so a compute wave's memory counter holds
+//   only its own activation loads and y stores: waiting for those never
+//   drains weight loads.
 //
-// Ordering between products: after its y stores have completed, a
-// workgroup's sync wave adds 1 to its leaf of a two-level counter tree in the
-// caller's workspace; the last arrival at a leaf climbs to the top counter,
-// the last arrival at the top raises every leaf's flag to i+1. A sync wave
-// stages product i+1's x only after its leaf flag reaches i+1. Every wait is
-// bounded: a wait that gives up flags the workspace's error word, releases
-// the other workgroups and ends the launch (its results are then invalid),
-// so a launch whose workgroups cannot all be resident ends instead of
-// hanging. The last workgroup out resets the counters for the next call.
+// Ordering between products: when a product's units are done in a
+// workgroup, each compute wave waits for its own y stores to complete and
+// counts itself out in LDS; the last one reports to a two-level counter tree
+// in the caller's workspace (the last arrival at a leaf climbs to the top
+// counter, the last arrival at the top raises every leaf's flag to i+1) and
+// waits for its leaf flag, then lets the workgroup's compute waves stage the
+// next product's activations. Every wait is bounded: a wait that gives up
+// flags the workspace's error word, releases the other workgroups and ends
+// the launch (its results are then invalid), so a launch whose workgroups
+// cannot all be resident ends instead of hanging. The last workgroup out
+// resets the counters for the next call.
+//
+// Memory model. y is written with device-coherent stores (sc1: through to
+// memory, no L2 write-back needed); the tree's atomics and flags are
+// device-coherent too, and a wave counts itself out only after its stores are
+// acknowledged. An activation buffer that an earlier product of the plan
+// writes is read with device-coherent loads (no stale L2 line of another XCD
+// can serve it); one that no product of the plan writes is read through the
+// caches, where no stale copy can exist (the kernel's start invalidates them).
+// The host plan marks which is which.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -54,31 +68,39 @@ using namespace w4a16_dev;
 namespace {
 
 constexpr uint32_t kChainMagic = 0x48433457u;  // "W4CH"
-constexpr uint32_t kChainVersion = 3;
+constexpr uint32_t kChainVersion = 4;
 constexpr unsigned kSpinLimit = 1u << 20;      // global polls before an ordering wait gives up (~1 s)
-constexpr unsigned kLdsSpinLimit = 1u << 26;   // LDS polls before a wave gives up (several s)
+constexpr unsigned kLdsSpinLimit = 1u << 24;   // LDS polls before a wave gives up (about a second)
 constexpr int kLeaves = 16;                    // leaf counters of the ordering tree
 constexpr int kLineWords = 1024;               // 4 KiB between counters (separate memory pages)
-constexpr int kWaves = 8;                      // per workgroup
-constexpr int kComputeWaves = kWaves - 1;      // wave kWaves-1 is the sync wave
-constexpr int kXLdsBytes = 65536;              // LDS staging of one pass of x
-constexpr int kYLdsBytes = 65536;              // LDS partial sums of one block of tiles
+constexpr int kLoaderDepth = 5;                // units in flight (in registers) per loader wave
+// loader and compute waves per workgroup: eight loaders while the compute
+// waves' registers fit four waves per SIMD (128 VGPRs), else four; eight
+// compute waves
+__host__ __device__ constexpr int chain_loader_waves(int) { return 4; }
+__host__ __device__ constexpr int chain_compute_waves(int) { return 8; }
+constexpr int kRing = 24;                      // LDS ring slots (a multiple of both wave counts)
+constexpr int kSeg = 64;                       // groups per K segment (one per lane)
+constexpr int kUnitBytes = (kTileRows + 1) * kSeg * 16;  // 4 code rows + the scale/min entries
+constexpr int kXBytes = 32768;                 // LDS activations of one pass over K
+constexpr int kPartFloats = 1024;              // LDS segment sums and running sums of a block of tiles
+constexpr int kMaxBlockTiles = 32;
 constexpr int kLoadCoherent = 16;              // buffer-load cache policy: device-coherent (sc1)
+static_assert(kRing % 8 == 0 && kRing % 4 == 0,
+              "a slot is always filled by the same loader and emptied by the same compute wave");
 
-// groups per lane (the x slice stays within 32 VGPRs at M = 1 and 2)
-constexpr int chain_gpl(int M) { return M == 1 ? 2 : 1; }
-// groups of one K segment (one unit of work covers one segment of one tile)
-constexpr int chain_seg_groups(int M) { return 64 * chain_gpl(M); }
-// segments of x one LDS pass holds, and the LDS row stride of x in groups
-constexpr int chain_pass_segs(int M) { return kXLdsBytes / (64 * M) / chain_seg_groups(M); }
-constexpr int chain_x_groups(int M) { return chain_pass_segs(M) * chain_seg_groups(M); }
-// units whose loads a compute wave keeps in registers (register budget: two
-// waves per SIMD, 256 VGPRs each)
-constexpr int chain_ring(int M) { return M == 1 ? 4 : M == 2 ? 8 : M <= 4 ? 6 : M == 5 ? 4 : 3; }
+// K segments of activations one LDS pass holds, and tiles per block (a block's
+// segment sums of one pass and its running sums fit kPartFloats)
+__host__ __device__ constexpr int chain_pass_segs(int M) { return kXBytes / (M * kSeg * 64); }
+__host__ __device__ constexpr int chain_block_tiles(int M) {
+  return kPartFloats / (chain_pass_segs(M) * kTileRows * M + kTileRows * M) < kMaxBlockTiles
+             ? kPartFloats / (chain_pass_segs(M) * kTileRows * M + kTileRows * M)
+             : kMaxBlockTiles;
+}
 
 struct ChainHeader {
   uint32_t magic, version;
-  int32_t count, M, gpl, ring;
+  int32_t count, M, ring, compute_waves;
   int32_t pad[10];
 };
 static_assert(sizeof(ChainHeader) == 64, "plan header is 64 bytes");
@@ -89,27 +111,24 @@ struct ChainEntry {
   const u32x4* sm;
   float* y;
   int32_t N, G, T;  // rows, groups per row, 4-row tiles
-  int32_t S;        // K segments per tile
-  int32_t passes;   // LDS passes of x over the segments
-  int32_t TB;       // tiles per block (the LDS partials of one block fit kYLdsBytes)
+  int32_t S;        // K segments per row
+  int32_t passes;   // LDS passes of the activations over the segments
+  int32_t xcoh;     // 1: x may have been written by an earlier entry (device-coherent loads)
   int32_t pad[2];
 };
 static_assert(sizeof(ChainEntry) == 64, "plan entry is 64 bytes");
 
 // The plan never changes during a launch: it is read through the constant
-// address space, which the compiler always serves with scalar loads. Through
-// a global pointer, the y stores and the ordering operations of the kernel
-// would make it assume the plan may have changed and read it with vector
-// loads, whose completion shares the in-order counter of the weight loads in
-// flight and would drain them at every product boundary.
+// address space, which the compiler always serves with scalar loads.
 typedef const __attribute__((address_space(4))) ChainEntry* EntryPtr;
 
 // Workspace words: the tree's top counter, the exit counter and the error
 // word share the first page; leaf g's counter and flag sit on page 1 + g.
-constexpr int kTopWord = 0, kExitWord = 32, kErrorWord = 64;
+constexpr int kTopWord = 0, kExitWord = 32, kErrorWord = W4A16_CHAIN_ERROR_OFFSET / 4;
 constexpr int leaf_word(int g) { return kLineWords * (1 + g); }
 constexpr int flag_word(int g) { return kLineWords * (1 + g) + 32; }
 static_assert(kLineWords * (1 + kLeaves) * 4 == W4A16_CHAIN_WORKSPACE_BYTES, "workspace layout");
+static_assert(kErrorWord > kExitWord && kErrorWord < kLineWords, "error word on the first page");
 
 __device__ __forceinline__ unsigned ld_coherent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -120,403 +139,464 @@ __device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
 __device__ __forceinline__ void st_coherent(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// keeps the compiler from moving memory accesses across this point (no instruction)
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Product p as one workgroup sees it, walked stage by stage: a stage is
-// (block b of this workgroup's tiles, LDS pass c over K); its units are
-// (tile, segment) pairs, tile-major. All fields are wave-uniform.
-struct Walk {
-  int p, b, c, s;  // product, block, pass, running stage number
-  EntryPtr e;
-  int t0, ntile, nb;     // this workgroup's tiles of product p, blocks
-  int tb0, nt, sg0, ns;  // the stage's first tile and count, first segment and count
+// LDS of one workgroup
+struct ChainLds {
+  u32x4 ring[kRing * kUnitBytes / 16];   // unit slots: code rows 0..3, then scale/min
+  u32x4 xl[kXBytes / 16];                // activations of the pass: [m][chunk][group]
+  float xsl[kXBytes / 64];               // their group sums: [m][group]
+  float part[kPartFloats];               // [tile][segment of the pass][row][m], then running [tile][row][m]
+  int tile_cnt[kMaxBlockTiles];          // segments of the current pass done, per tile of the block
+  int ready[kRing];                      // units landed in each slot
+  int consumed[kRing];                   // units taken out of each slot
+  int done;                              // compute waves past the end of a stage, all stages so far
+  int go;                                // stages released
+  int staged;                            // compute waves done staging, all stagings so far
+  int abort;                             // a wait gave up: every wave leaves
 };
 
-__device__ __forceinline__ void walk_product(Walk& w, EntryPtr ents, int p, int nwg, int wg) {
-  w.p = p;
-  w.e = ents + p;
-  const int T = w.e->T, TB = w.e->TB;
-  const int q = T / nwg, rem = T - q * nwg;
-  w.t0 = wg * q + (wg < rem ? wg : rem);
-  w.ntile = q + (wg < rem ? 1 : 0);
-  w.nb = w.ntile > 0 ? (w.ntile + TB - 1) / TB : 1;  // a workgroup with no tiles still walks one empty stage
-  w.b = 0;
-  w.c = 0;
+// One stage of a workgroup's walk: block b of its tiles of product p, pass c
+// over K. All fields are wave-uniform (scalar registers).
+struct Stage {
+  int p, b, c;
+  EntryPtr e;
+  int N, G, T, S, passes, xcoh;
+  int t0, ntile, nb;  // this workgroup's tiles of p: first, count, blocks
+  int tb0, nt;        // the stage's first tile and tile count
+  int sg0, ns;        // its first segment and segment count
+  int ubase;          // running index (within the workgroup) of its first unit
+  unsigned inv;       // ceil(2^32 / workgroups)
+};
+
+template <int M>
+__device__ __forceinline__ void stage_set(Stage& s) {
+  constexpr int TB = chain_block_tiles(M), XS = chain_pass_segs(M);
+  s.tb0 = s.t0 + s.b * TB;
+  const int left = s.ntile - s.b * TB;
+  s.nt = left < TB ? (left > 0 ? left : 0) : TB;
+  s.sg0 = s.c * XS;
+  s.ns = s.S - s.sg0 < XS ? s.S - s.sg0 : XS;
+}
+
+// q = T / nwg, r = T % nwg from the launch-wide reciprocal inv = ceil(2^32 / nwg)
+// (scalar multiply-high and one correction step: a division here would be
+// emulated in vector registers and pull the walk out of scalar registers)
+__device__ __forceinline__ void split_tiles(int T, int nwg, unsigned inv, int& q, int& r) {
+  if (nwg == 1) {
+    q = T;
+    r = 0;
+    return;
+  }
+  q = int(__umulhi(unsigned(T), inv));
+  r = T - q * nwg;
+  if (r < 0) {
+    --q;
+    r += nwg;
+  }
+  if (r >= nwg) {
+    ++q;
+    r -= nwg;
+  }
 }
 
 template <int M>
-__device__ __forceinline__ void walk_stage(Walk& w) {
-  constexpr int SP = chain_pass_segs(M);
-  const int TB = w.e->TB, S = w.e->S;
-  w.tb0 = w.t0 + w.b * TB;
-  const int left = w.ntile - w.b * TB;
-  w.nt = left < TB ? (left > 0 ? left : 0) : TB;
-  w.sg0 = w.c * SP;
-  w.ns = S - w.sg0 < SP ? S - w.sg0 : SP;
+__device__ __forceinline__ void stage_product(Stage& s, EntryPtr ents, int p, int nwg, int wg) {
+  constexpr int TB = chain_block_tiles(M);
+  s.p = p;
+  s.e = ents + p;
+  s.N = s.e->N;
+  s.G = s.e->G;
+  s.T = s.e->T;
+  s.S = s.e->S;
+  s.passes = s.e->passes;
+  s.xcoh = s.e->xcoh;
+  int q, rem;
+  split_tiles(s.T, nwg, s.inv, q, rem);
+  s.t0 = wg * q + (wg < rem ? wg : rem);
+  s.ntile = q + (wg < rem ? 1 : 0);
+  s.nb = s.ntile > 0 ? (s.ntile + TB - 1) / TB : 1;  // a workgroup with no tiles walks one empty stage
+  s.b = 0;
+  s.c = 0;
+  stage_set<M>(s);
 }
 
 // next stage; false past the last product
 template <int M>
-__device__ __forceinline__ bool walk_next(Walk& w, EntryPtr ents, int count, int nwg, int wg) {
-  ++w.s;
-  if (++w.c == w.e->passes) {
-    w.c = 0;
-    if (++w.b == w.nb) {
-      if (w.p + 1 >= count) {
-        w.p = count;
-        return false;
-      }
-      walk_product(w, ents, w.p + 1, nwg, wg);
+__device__ __forceinline__ bool stage_next(Stage& s, EntryPtr ents, int count, int nwg, int wg) {
+  s.ubase += s.nt * s.ns;
+  if (++s.c == s.passes) {
+    s.c = 0;
+    if (++s.b == s.nb) {
+      if (s.p + 1 >= count) return false;
+      stage_product<M>(s, ents, s.p + 1, nwg, wg);
+      return true;
     }
   }
-  walk_stage<M>(w);
+  stage_set<M>(s);
   return true;
 }
 
-// A compute wave's position: a stage, and unit ti * ns + si of it, i.e. tile
-// tb0 + ti and segment sg0 + si (wave v takes units v, v + 7, ... of every
-// stage). Kept as (ti, si) and moved with scalar adds: an integer division
-// here would be emulated in vector registers right next to the weight loads.
-struct Cursor {
-  Walk w;
-  int ti, si;
-};
-
-// unit index (ti, si) + n within a stage of ns segments per tile
-__device__ __forceinline__ void unit_add(int& ti, int& si, int ns, int n) {
-  si += n;
-  if (ns == 1) {
-    ti += si;
-    si = 0;
-  } else {
-    while (si >= ns) {
-      si -= ns;
-      ++ti;
-    }
-  }
+// first unit index i >= 0 of a stage with (ubase + i) % n == k, as (tile, segment)
+__device__ __forceinline__ int first_unit(int ubase, int k, int n) {
+  const int r = (k - ubase) % n;
+  return r < 0 ? r + n : r;
 }
-
-// move past stages where this wave has no unit
-template <int M>
-__device__ __forceinline__ void cursor_settle(Cursor& u, EntryPtr ents, int count, int nwg, int wg,
-                                              int wave) {
-  while (u.w.p < count && u.ti >= u.w.nt) {
-    if (!walk_next<M>(u.w, ents, count, nwg, wg)) break;
-    u.ti = 0;
-    u.si = 0;
-    unit_add(u.ti, u.si, u.w.ns, wave);
+// (ti, si) + n units, ns segments per tile
+__device__ __forceinline__ void unit_step(int& ti, int& si, int ns, int n) {
+  si += n;
+  while (si >= ns) {
+    si -= ns;
+    ++ti;
   }
 }
 
 // Activations read from LDS as they are used: chunk d of row m's group at
-// pass-local index gl[j], and that group's sum (written by the sync wave).
-template <int M, int GPL, int XG>
+// pass-local index gl, and that group's sum. LDS holds them chunk-major,
+// [m][chunk][group], so the 64 lanes of a wave (64 consecutive groups) read
+// 1 KiB of consecutive bytes per chunk, free of bank conflicts.
+template <int M, int XG>
 struct LdsX {
   static constexpr bool kRowOuter = false;  // each chunk is an LDS read: walk a tile chunk by chunk
   const u32x4* xl;
   const float* xsl;
-  int gl[GPL];
-  __device__ __forceinline__ u32x4 x(int m, int j, int d) const { return xl[(m * XG + gl[j]) * 4 + d]; }
-  __device__ __forceinline__ float sum(int m, int j) const { return xsl[m * XG + gl[j]]; }
+  int gl;
+  __device__ __forceinline__ u32x4 x(int m, int, int d) const { return xl[(m * 4 + d) * XG + gl]; }
+  __device__ __forceinline__ float sum(int m, int) const { return xsl[m * XG + gl]; }
 };
 
-// step(k) for k = K .. RING-1 with k a compile-time constant (the ring's
-// buffer indices must be constants; a pragma cannot unroll a loop this size
-// with an exit in it); false as soon as one step ends the walk
-template <int K, int RING, class Step>
+// step(k) for k = K .. N-1 with k a compile-time constant (register-ring
+// buffer indices must be constants); false as soon as one step ends the walk
+template <int K, int N, class Step>
 __device__ __forceinline__ bool ring_steps(Step& step) {
-  if constexpr (K == RING) {
+  if constexpr (K == N) {
     return true;
   } else {
     if (!step(std::integral_constant<int, K>{})) return false;
-    return ring_steps<K + 1, RING>(step);
+    return ring_steps<K + 1, N>(step);
   }
 }
 
-template <int M, int GPL, int RING>
-__global__ void __launch_bounds__(64 * kWaves)
+template <int M, int RING, int NCW>
+__global__ void __launch_bounds__(64 * (chain_loader_waves(M) + NCW))
 chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int count) {
+  static_assert(RING == kRing && NCW == chain_compute_waves(M), "one ring; the compute waves of M");
+  constexpr int XS = chain_pass_segs(M);
+  constexpr int XG = XS * kSeg;  // groups of one LDS pass
+  constexpr int TB = chain_block_tiles(M);
+  constexpr int NL = chain_loader_waves(M);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
   if (hdr->magic != kChainMagic || hdr->version != kChainVersion || hdr->count != count || hdr->M != M ||
-      hdr->gpl != GPL || hdr->ring != RING)
+      hdr->ring != RING || hdr->compute_waves != NCW)
     return;  // every workgroup sees the same header, so all leave together
   const EntryPtr ents = (EntryPtr)(reinterpret_cast<uintptr_t>(hdr + 1));
+  const unsigned inv = __builtin_amdgcn_readfirstlane(nwg > 1 ? 0xFFFFFFFFu / unsigned(nwg) + 1u : 0u);
 
-  constexpr int SG = chain_seg_groups(M);
-  constexpr int XG = chain_x_groups(M);
-  __shared__ u32x4 xl[kXLdsBytes / 16];  // x of the current pass: [m][XG groups][32 halfs]
-  __shared__ float xsl[kXLdsBytes / 64];  // the pass's group sums: [m][XG groups]
-  __shared__ float ys[kYLdsBytes / 4];   // partials of the current block: [tile][segment][row][m]
-  __shared__ int x_epoch;                // stages whose x is in xl
-  __shared__ int units_done;             // units written to ys so far
-  __shared__ int s_abort;
+  __shared__ ChainLds L;
+  for (int i = threadIdx.x; i < kRing; i += blockDim.x) L.ready[i] = L.consumed[i] = 0;
+  for (int i = threadIdx.x; i < kMaxBlockTiles; i += blockDim.x) L.tile_cnt[i] = 0;
+  if (threadIdx.x == 0) L.done = L.go = L.staged = L.abort = 0;
+  __syncthreads();  // the only workgroup barrier: nothing is in flight yet
 
+  auto lds_aborted = [&]() __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(&L.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
+  };
+
+  if (wave < NL) {
+    // ------------------------------------------------------------- loader wave
+    // A ring of D units in registers: the loads of the unit D-1 ahead go out
+    // before the oldest unit is copied into its LDS slot (the copy waits for
+    // that unit's loads only, and for its slot to be free). Weight bytes in
+    // flight live in these registers; the LDS ring holds landed units only.
+    constexpr int D = kLoaderDepth;
+    const int voff = lane * 16;
+    struct Cur {
+      Stage s;
+      int i, ti, si;
+      int valid;  // -1 inside the walk, 0 past its end (every load then reads nothing)
+    };
+    auto settle = [&](Cur& c) __attribute__((always_inline)) {
+      while (c.valid && c.i >= c.s.nt * c.s.ns) {
+        if (!stage_next<M>(c.s, ents, count, nwg, wg)) {
+          c.valid = 0;
+          break;
+        }
+        c.i = first_unit(c.s.ubase, wave, NL);
+        c.ti = 0;
+        c.si = 0;
+        unit_step(c.ti, c.si, c.s.ns, c.i);
+      }
+    };
+    auto advance = [&](Cur& c) __attribute__((always_inline)) {
+      c.i += NL;
+      unit_step(c.ti, c.si, c.s.ns, NL);
+      settle(c);
+    };
+    auto fetch = [&](const Cur& c, TileLoads<1>& T) __attribute__((always_inline)) {
+      const int g0[1] = {(c.s.sg0 + c.si) * kSeg};
+      fetch_tile_rows<1>(c.s.e->codes, c.s.e->sm, c.s.N, c.s.G, (c.s.tb0 + c.ti) & c.valid, g0, voff, c.valid, T);
+    };
+    int ok = 1;  // 0 once a wait gave up (every later copy is skipped)
+    // copy a landed unit into its slot once the slot's previous unit was
+    // taken out, then publish it; nothing past the end of the walk
+    auto copy = [&](const Cur& c, const TileLoads<1>& T) __attribute__((always_inline)) {
+      const int u = c.s.ubase + c.i;
+      const int slot = u % RING, k = u / RING;
+      unsigned spins = 0;
+      int go = c.valid & ok;
+      while (go && __builtin_amdgcn_readfirstlane(__hip_atomic_load(&L.consumed[slot], __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_WORKGROUP)) < k) {
+        if (lds_aborted()) {
+          ok = go = 0;
+        } else if (++spins > kLdsSpinLimit) {  // starved: make every wave of the workgroup leave
+          __hip_atomic_store(&L.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (lane == 0) add_coherent(ws + kErrorWord, 1u);
+          ok = go = 0;
+        } else {
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      if (go) {
+        compiler_fence();
+        u32x4* dst = L.ring + slot * (kUnitBytes / 16);
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) dst[r * 64 + lane] = T.code[r][0];
+        dst[kTileRows * 64 + lane] = T.sm[0];
+        compiler_fence();  // LDS operations complete in order: the data before the flag
+        if (lane == 0) __hip_atomic_store(&L.ready[slot], k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+    Cur F;
+    F.s.ubase = 0;
+    F.s.inv = inv;
+    stage_product<M>(F.s, ents, 0, nwg, wg);
+    F.valid = -1;
+    F.i = first_unit(0, wave, NL);
+    F.ti = 0;
+    F.si = 0;
+    unit_step(F.ti, F.si, F.s.ns, F.i);
+    settle(F);
+    Cur C = F;
+    TileLoads<1> B[D];
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k) {
+      fetch(F, B[k]);
+      advance(F);
+    }
+    // every step runs (a copy past the end does nothing); the walk's end is
+    // tested once per two rotations of the ring, so no buffer is live across
+    // an exit in the middle of the rotation
+    auto step = [&](auto kc) __attribute__((always_inline)) -> bool {
+      constexpr int k = decltype(kc)::value % D;
+      fetch(F, B[(k + D - 1) % D]);
+      advance(F);
+      __builtin_amdgcn_sched_barrier(0);
+      copy(C, B[k]);
+      advance(C);
+      return true;
+    };
+    do {
+      ring_steps<0, 2 * D>(step);
+    } while (C.valid && ok);
+    return;
+  }
+
+  // --------------------------------------------------------------- compute wave
+  const int cw = wave - NL;
+  // ordering tree: workgroup b reports to leaf b % leaves
+  const int leaves = nwg < kLeaves ? nwg : kLeaves;
+  const int leaf = wg % leaves;
+  const unsigned leaf_size = unsigned((nwg - leaf + leaves - 1) / leaves);
+  bool aborted = false;
+  auto give_up = [&]() {
+    aborted = true;
+    if (lane == 0) {
+      add_coherent(ws + kErrorWord, 1u);
+      __hip_atomic_store(&L.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  };
   // Poll an LDS counter until it reaches v; false: the launch is being
-  // abandoned. Every lane reads the same word; taking lane 0's value keeps the
-  // loop's exit (and so everything after it) wave-uniform in the compiler's
-  // eyes, which keeps the walk in scalar registers and its plan reads scalar.
+  // abandoned. Taking lane 0's value keeps everything after the loop
+  // wave-uniform in the compiler's eyes.
   auto lds_wait_ge = [&](const int* p, int v) __attribute__((always_inline)) -> bool {
     unsigned spins = 0;
-    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < v) {
-      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&s_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
-        return false;
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v) {
+      if (lds_aborted()) return false;
       if (++spins > kLdsSpinLimit) {
-        __hip_atomic_store(&s_abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        give_up();
         return false;
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    compiler_fence();
     return true;
   };
-
-  if (wave < kComputeWaves) {
-    // ------------------------------------------------------------ compute wave
-    const int voff = lane * 16;  // this lane's byte offset in every weight descriptor
-    auto fetch = [&](const Cursor& u, TileLoads<GPL>& L) __attribute__((always_inline)) {
-      // -1 inside the walk, 0 past its end (every load then out of range)
-      const int valid = ~((count - 1 - u.w.p) >> 31);
-      const int seg = u.w.sg0 + u.si;
-      int g0[GPL];
-#pragma unroll
-      for (int k = 0; k < GPL; ++k) g0[k] = seg * SG + k * 64;
-      const EntryPtr e = u.w.e;
-      fetch_tile_rows<GPL>(e->codes, e->sm, e->N, e->G, (u.w.tb0 + u.ti) & valid, g0, voff, valid, L);
-    };
-
-    int cur_s = -1;
-
-    // compute unit u from its loads; false when the walk is over
-    auto consume = [&](const Cursor& u, const TileLoads<GPL>& L) __attribute__((always_inline)) -> bool {
-      if (u.w.p >= count) return false;
-      if (u.w.s != cur_s) {
-        if (!lds_wait_ge(&x_epoch, u.w.s + 1)) return false;
-        cur_s = u.w.s;
-      }
-      const int ti = u.ti;
-      const int seg = u.w.sg0 + u.si;
-      LdsX<M, GPL, XG> xa{xl, xsl, {}};
-#pragma unroll
-      for (int k = 0; k < GPL; ++k) xa.gl[k] = (seg - u.w.sg0) * SG + k * 64 + lane;
-      float acc[kTileRows][M], v[M];
-      compute_tile<M, GPL>(L, xa, acc);
-      tile_sums<M>(acc, v);
-      // lane 16r + m writes the partial of row r, activation row m
-      if ((lane & 15) < M)
-        ys[(ti * u.w.e->S + seg) * kTileRows * M + (lane >> 4) * M + (lane & 15)] = pick_sum<M>(v, lane);
-      if (lane == 0) __hip_atomic_fetch_add(&units_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      return true;
-    };
-
-    Cursor F;
-    F.w.s = 0;
-    walk_product(F.w, ents, 0, nwg, wg);
-    walk_stage<M>(F.w);
-    F.ti = 0;
-    F.si = 0;
-    unit_add(F.ti, F.si, F.w.ns, wave);
-    cursor_settle<M>(F, ents, count, nwg, wg, wave);
-    Cursor C = F;
-    auto advance = [&](Cursor& u) __attribute__((always_inline)) {
-      unit_add(u.ti, u.si, u.w.ns, kComputeWaves);
-      cursor_settle<M>(u, ents, count, nwg, wg, wave);
-    };
-
-    // Ring of RING load buffers in a fixed rotation: the loads of the unit
-    // RING-1 ahead are issued before each unit is computed, so RING-1 units
-    // stay in flight while one is computed. Every fetch is unconditional
-    // (past the end it reads nothing), so no buffer is merged behind a branch.
-    TileLoads<GPL> L[RING];
-#pragma unroll
-    for (int k = 0; k < RING - 1; ++k) {
-      fetch(F, L[k]);
-      advance(F);
-    }
-    lds_barrier();  // the sync wave has initialised the LDS counters
-    auto step = [&](auto kc) __attribute__((always_inline)) -> bool {
-      constexpr int k = decltype(kc)::value % RING;
-      fetch(F, L[(k + RING - 1) % RING]);
-      advance(F);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!consume(C, L[k])) return false;
-      advance(C);
-      return true;
-    };
-    // two rotations per loop trip: the compiler's wait counts at the top of
-    // the loop are conservative (one unit in flight instead of RING-1)
-    while (ring_steps<0, 2 * RING>(step)) {
-    }
-  } else {
-    // --------------------------------------------------------------- sync wave
-    // ordering tree: workgroup b reports to leaf b % leaves
-    const int leaves = nwg < kLeaves ? nwg : kLeaves;
-    const int leaf = wg % leaves;
-    const unsigned leaf_size = unsigned((nwg - leaf + leaves - 1) / leaves);
+  // wait until products 0..i-1 are complete everywhere; false: give up
+  auto wait_for = [&](int i) -> bool {
+    int ok = 1;
     if (lane == 0) {
-      x_epoch = 0;
-      units_done = 0;
-      s_abort = 0;
+      unsigned spins = 0;
+      while (ld_coherent(ws + flag_word(leaf)) < unsigned(i)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          ok = 0;
+          break;
+        }
+      }
     }
-    lds_barrier();
+    compiler_fence();
+    return __builtin_amdgcn_readfirstlane(ok) != 0;
+  };
+  // this workgroup's results of product i are written: report to the tree;
+  // the last report of a leaf climbs to the top, the last at the top raises
+  // every leaf's flag to i+1
+  auto arrive = [&](int i) {
+    if (lane == 0) {
+      const unsigned old = add_coherent(ws + leaf_word(leaf), 1u);
+      if (old == unsigned(i + 1) * leaf_size - 1u) {
+        const unsigned top = add_coherent(ws + kTopWord, 1u);
+        if (top == unsigned(i + 1) * unsigned(leaves) - 1u)
+          for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(i + 1));
+      }
+    }
+  };
 
-    bool aborted = false;
-    int arrived = 0;
-    auto give_up = [&]() {
-      aborted = true;
-      if (lane == 0) {
-        add_coherent(ws + kErrorWord, 1u);
-        __hip_atomic_store(&s_abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    };
-    // wait until products 0..i-1 are complete everywhere; false: give up
-    auto wait_for = [&](int i) -> bool {
-      int ok = 1;
-      if (lane == 0) {
-        unsigned spins = 0;
-        while (ld_coherent(ws + flag_word(leaf)) < unsigned(i)) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > kSpinLimit) {
-            ok = 0;
-            break;
-          }
-        }
-      }
-      return __builtin_amdgcn_readfirstlane(ok) != 0;
-    };
-    // this workgroup's results of product i are written: report to the tree;
-    // the last report of a leaf climbs to the top, the last at the top raises
-    // every leaf's flag to i+1
-    auto arrive = [&](int i) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent y stores are complete
-      if (lane == 0) {
-        const unsigned old = add_coherent(ws + leaf_word(leaf), 1u);
-        if (old == unsigned(i + 1) * leaf_size - 1u) {
-          const unsigned top = add_coherent(ws + kTopWord, 1u);
-          if (top == unsigned(i + 1) * unsigned(leaves) - 1u)
-            for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(i + 1));
-        }
-      }
-      ++arrived;
-    };
-    // the stage's pass of activations, global -> LDS, with each group's sum;
-    // groups of the pass's last segment past G read as zeros. All loads of a
-    // batch are issued before the first is used: staging sits between an
-    // ordering point and the compute of the next product. The first product's
-    // activations were written before the launch and are read through the
-    // caches; every later product's may have been written by an earlier
-    // product of this launch on another XCD and are read device-coherently.
-    auto stage_x = [&](const Walk& w, auto policy) {
-      constexpr int kPolicy = decltype(policy)::value;
-      const EntryPtr e = w.e;
-      const int G = e->G;
-      const int gb = w.sg0 * SG;                               // first group of the pass
-      const int ng = G - gb < w.ns * SG ? G - gb : w.ns * SG;  // groups of x in the pass
-      const int chunks = ng * 4;                               // 16-byte chunks per activation row
-      const int total = M * chunks;
-      const __amdgpu_buffer_rsrc_t rx = make_rsrc(e->x, M * G * 64);
-      constexpr int kBatch = 16;
-      for (int base = 0; base < total; base += 64 * kBatch) {
-        u32x4 v[kBatch];
-        int mk[kBatch], rk[kBatch];
-        int m = (base + lane) / chunks, r = base + lane - m * chunks;  // chunk r of activation row m
+  // this wave's share of the stage's activations, global -> LDS, with each
+  // group's sum: lane item c*64 + lane + j*NCW*64 is group (item % XG) of the
+  // pass for activation row item / XG (at most one item per lane: M * XS <= 8)
+  auto stage_x = [&](const Stage& s) {
+    const int gb = s.sg0 * kSeg;
+    const int item = cw * 64 + lane;
+    if (item < M * XG) {
+      const int m = item / XG, lg = item - m * XG;
+      const int g = gb + lg;
+      u32x4 v[4] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+      if (lg < s.ns * kSeg && g < s.G) {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(s.e->x, M * s.G * 64);
+        const int off = (m * s.G + g) * 64;
+        if (s.xcoh) {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          mk[k] = m;
-          rk[k] = r;
-          // past the end: an offset beyond the buffer reads zeros and no memory
-          const int off = m < M ? ((m * G + gb) * 4 + r) * 16 : M * G * 64;
-          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kPolicy);
-          r += 64;
-          while (r >= chunks) {
-            r -= chunks;
-            ++m;
-          }
-        }
+          for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + q * 16, 0, kLoadCoherent);
+        } else {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          // lanes 4g..4g+3 hold group g's four chunks: its sum in the fixed tree
-          float t = chunk_sum(v[k]);
-          t += dpp<0xB1>(t);  // (c0 + c1), (c2 + c3)
-          t += dpp<0x4E>(t);  // (c0 + c1) + (c2 + c3)
-          if (mk[k] < M) {
-            xl[mk[k] * XG * 4 + rk[k]] = v[k];
-            if ((lane & 3) == 0) xsl[mk[k] * XG + rk[k] / 4] = t;
-          }
+          for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + q * 16, 0, 0);
         }
       }
-      const int pad = w.ns * SG - ng;  // groups past G in the last segment
-      for (int idx = lane; idx < M * pad * 4; idx += 64) {
-        const int m = idx / (pad * 4), r = idx - m * (pad * 4);
-        xl[m * XG * 4 + chunks + r] = u32x4{0, 0, 0, 0};
-        if ((r & 3) == 0) xsl[m * XG + ng + r / 4] = 0.f;
-      }
-    };
-    // the block's partials, summed over segments in order, to y
-    auto flush = [&](const Walk& w) {
-      const EntryPtr e = w.e;
-      const int S = e->S, N = e->N;
-      for (int idx = lane; idx < w.nt * kTileRows * M; idx += 64) {
-        const int ti = idx / (kTileRows * M);
-        const int rm = idx - ti * (kTileRows * M);
-        const int n = (w.tb0 + ti) * kTileRows + rm / M;
-        float s = 0.f;
-        for (int seg = 0; seg < S; ++seg) s += ys[(ti * S + seg) * kTileRows * M + rm];
-        if (n < N) store_y<true>(e->y + size_t(rm % M) * N + n, s);
-      }
-    };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) L.xl[(m * 4 + q) * XG + lg] = v[q];
+      L.xsl[m * XG + lg] = group_sum(v);
+    }
+  };
 
-    Walk w;
-    w.s = 0;
-    walk_product(w, ents, 0, nwg, wg);
-    walk_stage<M>(w);
-    int units = 0;
-    int staged_p = -1, staged_c = -1;
-    while (true) {
-      const int p = w.p;
-      if (w.b == 0 && w.c == 0 && p > 0) {  // a new product: every earlier one must be complete
-        if (!wait_for(p)) {
+  Stage s;
+  s.ubase = 0;
+  s.inv = inv;
+  stage_product<M>(s, ents, 0, nwg, wg);
+  int stages = 0, stagings = 0;
+  do {
+    // activations: once per product when one pass holds all of K, else per stage
+    if (s.nt > 0 && (s.passes > 1 || s.b == 0)) {
+      stage_x(s);
+      compiler_fence();
+      ++stagings;
+      if (lane == 0) __hip_atomic_fetch_add(&L.staged, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (!lds_wait_ge(&L.staged, stagings * NCW)) break;
+    }
+    // this wave's units of the stage
+    const int units = s.nt * s.ns;
+    int i = first_unit(s.ubase, cw, NCW);
+    int ti = 0, si = 0;
+    unit_step(ti, si, s.ns, i);
+    bool ok = true;
+    for (; i < units; i += NCW) {
+      const int u = s.ubase + i;
+      const int slot = u % RING, k = u / RING;
+      if (!lds_wait_ge(&L.ready[slot], k + 1)) {
+        ok = false;
+        break;
+      }
+      TileLoads<1> T;
+      const u32x4* src = L.ring + slot * (kUnitBytes / 16);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) T.code[r][0] = src[r * 64 + lane];
+      T.sm[0] = src[kTileRows * 64 + lane];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's bytes are in registers
+      compiler_fence();
+      if (lane == 0) __hip_atomic_store(&L.consumed[slot], k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      float acc[kTileRows][M], v[M];
+      compute_tile<M, 1>(T, LdsX<M, XG>{L.xl, L.xsl, si * kSeg + lane}, acc);
+      tile_sums<M>(acc, v);
+      // lane 16r + m holds output row r's sum for activation row m
+      float* part = L.part + (ti * XS + si) * (kTileRows * M);
+      if ((lane & 15) < M) part[(lane >> 4) * M + (lane & 15)] = pick_sum<M>(v, lane);
+      compiler_fence();
+      int old = 0;
+      if (lane == 0) old = __hip_atomic_fetch_add(&L.tile_cnt[ti], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old == s.ns - 1) {
+        // the tile's last segment of this pass: add the pass's segment sums
+        // in order to the running sum of the earlier passes
+        compiler_fence();
+        float* run = L.part + TB * XS * (kTileRows * M) + ti * (kTileRows * M);
+        const float* seg = L.part + ti * XS * (kTileRows * M);
+        if ((lane & 15) < M) {
+          const int rm = (lane >> 4) * M + (lane & 15);
+          float acc_y = s.c == 0 ? 0.f : run[rm];
+          for (int sp = 0; sp < s.ns; ++sp) acc_y += seg[sp * (kTileRows * M) + rm];
+          const int n = (s.tb0 + ti) * kTileRows + (lane >> 4);
+          if (s.c == s.passes - 1) {
+            if (n < s.N) store_y<true>(s.e->y + size_t(lane & 15) * s.N + n, acc_y);
+          } else {
+            run[rm] = acc_y;
+          }
+        }
+        if (lane == 0) L.tile_cnt[ti] = 0;
+      }
+      unit_step(ti, si, s.ns, NCW);
+    }
+    if (!ok) break;
+    // end of the stage: count out; the last compute wave of the workgroup
+    // takes the ordering point when the stage ends a product
+    const bool product_end = s.c == s.passes - 1 && s.b == s.nb - 1;
+    if (product_end) __builtin_amdgcn_s_waitcnt(0);  // this wave's y stores are complete
+    compiler_fence();
+    ++stages;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&L.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == stages * NCW - 1) {
+      if (product_end && s.p + 1 < count) {
+        arrive(s.p);
+        if (!wait_for(s.p + 1)) {
           give_up();
           break;
         }
       }
-      if (w.nt > 0 && (p != staged_p || w.c != staged_c)) {
-        if (p == 0)
-          stage_x(w, std::integral_constant<int, 0>{});
-        else
-          stage_x(w, std::integral_constant<int, kLoadCoherent>{});
-        staged_p = p;
-        staged_c = w.c;
-      }
-      units += w.nt * w.ns;
-      if (lane == 0) __hip_atomic_store(&x_epoch, w.s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (!lds_wait_ge(&units_done, units)) {
-        give_up();
-        break;
-      }
-      const bool block_done = w.c == w.e->passes - 1;
-      const bool product_done = block_done && w.b == w.nb - 1;
-      if (block_done && w.nt > 0) flush(w);
-      if (!walk_next<M>(w, ents, count, nwg, wg)) break;
-      if (product_done) arrive(p);
+      if (lane == 0) __hip_atomic_store(&L.go, stages, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    if (!lds_wait_ge(&L.go, stages)) break;
+  } while (stage_next<M>(s, ents, count, nwg, wg));
 
-    // Count out. After giving up, first release every waiter (results of this
-    // call are then invalid and the error word says so). The last workgroup
-    // out resets every counter and flag for the next call. A single product
-    // touches no counter and skips this.
-    if (lane == 0 && count > 1) {
-      if (aborted || arrived < count - 1)
-        for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(count));
-      const unsigned prev = add_coherent(ws + kExitWord, 1u);
-      if (prev == unsigned(nwg) - 1u) {
-        st_coherent(ws + kTopWord, 0u);
-        for (int l = 0; l < leaves; ++l) {
-          st_coherent(ws + leaf_word(l), 0u);
-          st_coherent(ws + flag_word(l), 0u);
-        }
-        st_coherent(ws + kExitWord, 0u);
+  // Count out (one wave per workgroup: the first compute wave, past the last
+  // stage, after which this workgroup touches no counter). A wave that gave
+  // up first releases every waiter (results of this call are then invalid
+  // and the error word says so). The last workgroup out resets every counter
+  // and flag for the next call. A single product touches no counter.
+  if (aborted && lane == 0 && count > 1)
+    for (int l = 0; l < leaves; ++l) st_coherent(ws + flag_word(l), unsigned(count));
+  if (cw == 0 && lane == 0 && count > 1) {
+    const unsigned prev = add_coherent(ws + kExitWord, 1u);
+    if (prev == unsigned(nwg) - 1u) {
+      st_coherent(ws + kTopWord, 0u);
+      for (int l = 0; l < leaves; ++l) {
+        st_coherent(ws + leaf_word(l), 0u);
+        st_coherent(ws + flag_word(l), 0u);
       }
+      st_coherent(ws + kExitWord, 0u);
     }
   }
 }
@@ -525,7 +605,7 @@ typedef void (*chain_fn)(const ChainHeader*, unsigned*, int);
 
 template <int M>
 constexpr chain_fn chain_instance() {
-  return &chain_kernel<M, chain_gpl(M), chain_ring(M)>;
+  return &chain_kernel<M, kRing, chain_compute_waves(M)>;
 }
 
 chain_fn chain_for(int M) {
@@ -586,9 +666,9 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
   h.version = kChainVersion;
   h.count = count;
   h.M = M;
-  h.gpl = chain_gpl(M);
-  h.ring = chain_ring(M);
-  const int sg = chain_seg_groups(M), sp = chain_pass_segs(M);
+  h.ring = kRing;
+  h.compute_waves = chain_compute_waves(M);
+  const int xs = chain_pass_segs(M);
   uint8_t* out = static_cast<uint8_t*>(plan);
   std::memcpy(out, &h, sizeof(h));
   for (int32_t i = 0; i < count; ++i) {
@@ -604,10 +684,15 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
     c.N = e.N;
     c.G = G;
     c.T = (e.N + kTileRows - 1) / kTileRows;
-    c.S = (G + sg - 1) / sg;
-    c.passes = (c.S + sp - 1) / sp;
-    // one tile's partials fit: S * 4 * M floats <= kYLdsBytes for every K <= w4a16_max_k
-    c.TB = kYLdsBytes / (c.S * kTileRows * M * int(sizeof(float)));
+    c.S = (G + kSeg - 1) / kSeg;
+    c.passes = (c.S + xs - 1) / xs;
+    // an x that an earlier entry writes is read device-coherently
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(e.x);
+    for (int32_t j = 0; j < i && !c.xcoh; ++j)
+      c.xcoh = ranges_overlap(reinterpret_cast<uintptr_t>(entries[j].y), size_t(M) * size_t(entries[j].N) * 4, xa,
+                              size_t(M) * size_t(e.K) * 2)
+                   ? 1
+                   : 0;
     std::memcpy(out + sizeof(ChainHeader) + size_t(i) * sizeof(ChainEntry), &c, sizeof(c));
   }
   return W4A16_OK;
@@ -617,8 +702,8 @@ extern "C" w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]) {
   if (!out) return W4A16_ERR_NULL;
   if (M < 1 || M > kMaxM) return W4A16_ERR_SHAPE;
   out[0] = M;
-  out[1] = chain_gpl(M);
-  out[2] = chain_ring(M);
+  out[1] = kRing;
+  out[2] = chain_compute_waves(M);
   return W4A16_OK;
 }
 
@@ -635,7 +720,7 @@ w4a16_status chain_enqueue(const void* plan, int32_t count, int32_t M, void* wor
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   int occ = g_chain_occupancy[M].load(std::memory_order_relaxed);
   if (occ <= 0) {
-    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * kWaves);
+    occ = w4a16_host::occupancy_of(reinterpret_cast<const void*>(fn), 64 * (chain_loader_waves(M) + chain_compute_waves(M)));
     g_chain_occupancy[M].store(occ, std::memory_order_relaxed);
   }
   // every workgroup must be resident at once: the grid is the occupancy limit
@@ -644,7 +729,8 @@ w4a16_status chain_enqueue(const void* plan, int32_t count, int32_t M, void* wor
   unsigned* wp = static_cast<unsigned*>(workspace);
   int n_arg = count;
   void* args[] = {&hp, &wp, &n_arg};
-  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * kWaves), args, 0,
+  const int block = 64 * (chain_loader_waves(M) + chain_compute_waves(M));
+  if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), args, 0,
                          static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;

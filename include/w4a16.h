@@ -175,6 +175,10 @@ typedef struct w4a16_chain_entry {
 
 /* Bytes of the device workspace of w4a16_gemv_chain. */
 #define W4A16_CHAIN_WORKSPACE_BYTES 69632
+/* Byte offset in that workspace of the uint32 error word: nonzero once an
+ * ordering wait of a chain launch gave up (that call's results are invalid;
+ * zero-fill the workspace again before the next call). */
+#define W4A16_CHAIN_ERROR_OFFSET 256
 
 /* Bytes of the plan for `count` entries (0 if count < 1 or too large). */
 size_t w4a16_chain_plan_bytes(int32_t count);

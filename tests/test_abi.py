@@ -151,11 +151,11 @@ def test_launch_shape_host_logic(w4a16_lib):
 def test_chain_launch_shape(w4a16_lib):
     for M in range(1, 9):
         s = w4.chain_launch_shape(M)
-        assert s["M"] == M and s["gpl"] in (1, 2) and 1 <= s["ring"] <= 16
-        assert s["kernel"] == f"chain_kernel<{M}, {s['gpl']}, {s['ring']}>"
+        assert s["M"] == M and s["ring"] % 8 == 0 and s["compute_waves"] == 8
+        assert s["kernel"] == f"chain_kernel<{M}, {s['ring']}, {s['compute_waves']}>"
         plan = w4.w4a16_chain_plan([(0x7F0000000000, 0x7F0001000000, 0x7F0040000000, 64, 64)], M)
         hdr = plan[:64].view("<i4")
-        assert (hdr[4], hdr[5]) == (s["gpl"], s["ring"])    # the plan is made for that kernel
+        assert (hdr[4], hdr[5]) == (s["ring"], s["compute_waves"])    # the plan is made for that kernel
     for M in (0, 9):
         with pytest.raises(w4.W4A16Error):
             w4.chain_launch_shape(M)
@@ -178,28 +178,29 @@ def _plan_fields(plan, count):
 def test_chain_plan_layout(w4a16_lib):
     B = 0x7F0000000000
     entries = [
-        (B, B + 2**24, B + 2**30, 6144, 4096),                    # one segment of 128 groups
-        (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # four segments
-        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # seven segments, one LDS pass
+        (B, B + 2**24, B + 2**30, 6144, 4096),                    # two segments of 64 groups
+        (B + 2**20, B + 2**26, B + 2**30 + 2**20, 4096, 14336),   # seven segments, one LDS pass
+        (B + 2**21, B + 2**28, B + 2**30 + 2**21, 10, 28672),     # fourteen segments, two passes
+        (B + 2**30 + 2**20, B + 2**29, B + 2**31, 64, 64),        # x is the second entry's y
     ]
     plan = w4.w4a16_chain_plan(entries, 1)
-    assert plan.size == w4.w4a16_chain_plan_bytes(3) == 64 + 3 * 64
-    hdr, ents = _plan_fields(plan, 3)
+    assert plan.size == w4.w4a16_chain_plan_bytes(4) == 64 + 4 * 64
+    hdr, ents = _plan_fields(plan, 4)
     shape = w4.chain_launch_shape(1)
-    assert (hdr[0], hdr[1], hdr[2], hdr[3]) == (0x48433457, 3, 3, 1)
-    assert (hdr[4], hdr[5]) == (shape["gpl"], shape["ring"]) == (2, 4)
+    assert (hdr[0], hdr[1], hdr[2], hdr[3]) == (0x48433457, 4, 4, 1)
+    assert (hdr[4], hdr[5]) == (shape["ring"], shape["compute_waves"]) == (24, 8)
     for (x, p, y, N, K), e in zip(entries, ents):
-        ex, ecodes, esm, ey, eN, eG, eT, S, passes, TB = e
+        ex, ecodes, esm, ey, eN, eG, eT, S, passes, xcoh = e
         assert (ex, ecodes, ey, eN, eG, eT) == (x, p, y, N, K // 32, (N + 3) // 4)
         assert esm == p + (N * K // 2 + 255) // 256 * 256
-        assert S * 128 >= K // 32 > (S - 1) * 128             # M = 1: segments of 64 lanes x 2 groups
-        assert TB * S * 4 * 4 <= 65536 < (TB + 1) * S * 4 * 4  # one block's partials fill the LDS stage
-    assert [e[7:] for e in ents] == [(1, 1, 4096), (4, 1, 1024), (7, 1, 585)]
+        assert S * 64 >= K // 32 > (S - 1) * 64               # segments of 64 groups, one per lane
+    # M = 1: 8 segments of activations per LDS pass; only the last x is written by an earlier entry
+    assert [e[7:] for e in ents] == [(2, 1, 0), (7, 1, 0), (14, 2, 0), (1, 1, 1)]
     plan8 = w4.w4a16_chain_plan(entries[:2], 8)
     hdr8, e8 = _plan_fields(plan8, 2)
-    assert (hdr8[4], hdr8[5]) == (1, w4.chain_launch_shape(8)["ring"])
-    # M = 8: segments of 64 groups, 2 per 64 KiB pass of x, partials of 4 x 8 per segment
-    assert [e[7:] for e in e8] == [(2, 1, 256), (7, 4, 73)]
+    assert (hdr8[3], hdr8[4]) == (8, w4.chain_launch_shape(8)["ring"])
+    # M = 8: one segment of 8 activation rows per pass
+    assert [e[7:] for e in e8] == [(2, 2, 0), (7, 7, 0)]
 
 
 def test_chain_plan_errors(w4a16_lib):
