@@ -194,6 +194,28 @@ def _ptr(t) -> int:
     return int(t.data_ptr()) if hasattr(t, "data_ptr") else int(t)
 
 
+def _device_tensors(where: str, **tensors) -> None:
+    """Raise ValueError unless every named tensor is a contiguous GPU tensor
+    and all of them sit on the same device: the library receives bare device
+    addresses, so a host tensor or a strided view would be read as garbage
+    (or fault the GPU) rather than refused. Byte buffers (packed blobs,
+    plans) must be uint8. Nothing here touches the GPU."""
+    device = None
+    for name, t in tensors.items():
+        if not hasattr(t, "is_cuda") or not hasattr(t, "data_ptr"):
+            raise ValueError(f"{where}: {name} must be a torch tensor on the GPU")
+        if not t.is_cuda:
+            raise ValueError(f"{where}: {name} is on {t.device}, not on a GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{where}: {name} is on {t.device}, the other tensors on {device}")
+        if name in ("packed", "kv", "plan") and str(t.dtype) != "torch.uint8":
+            raise ValueError(f"{where}: {name} must be a uint8 byte buffer, not {t.dtype}")
+
+
 def w4a16_gemv_raw(x_ptr: int, packed_ptr: int, y_ptr: int, M: int, N: int, K: int, stream: int = 0) -> int:
     """Direct C call with raw pointers; returns the status code."""
     return int(lib().w4a16_gemv(x_ptr, packed_ptr, y_ptr, M, N, K, stream))
@@ -216,6 +238,7 @@ def w4a16_gemv(x, packed, y, stream=None) -> None:
         raise TypeError("x must be float16 and y float32")
     if x.dim() != 2 or y.dim() != 2:
         raise ValueError("x must be [M, K] and y [M, N]")
+    _device_tensors("w4a16_gemv", x=x, packed=packed, y=y)
     M, K = int(x.shape[0]), int(x.shape[1])
     N = int(y.shape[-1])
     if tuple(y.shape) != (M, N):
@@ -225,8 +248,6 @@ def w4a16_gemv(x, packed, y, stream=None) -> None:
         raise W4A16Error(W4A16_ERR_SHAPE, "w4a16_gemv")
     if packed.numel() * packed.element_size() < need:
         raise ValueError(f"packed blob has {packed.numel() * packed.element_size()} bytes, needs {need}")
-    if not (x.is_contiguous() and y.is_contiguous()):
-        raise ValueError("x and y must be contiguous")
     if stream is None:
         import torch  # only for the current stream handle
 
@@ -290,6 +311,7 @@ def w4a16_gemv_chain_timed_raw(plan_ptr: int, count: int, M: int, workspace_ptr:
 
 def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None) -> None:
     """Enqueue a planned decode-step chain (plan and workspace are device tensors)."""
+    _device_tensors("w4a16_gemv_chain", plan=plan, workspace=workspace)
     if stream is None:
         import torch
 
@@ -383,8 +405,7 @@ def w4a16_codec_gemv(codec, x, packed, y, stream=None) -> None:
         raise TypeError("x must be float16 and y float32")
     if x.dim() != 2 or y.dim() != 2 or int(y.shape[0]) != int(x.shape[0]):
         raise ValueError("x must be [M, K] and y [M, N]")
-    if not (x.is_contiguous() and y.is_contiguous()):
-        raise ValueError("x and y must be contiguous")
+    _device_tensors("w4a16_codec_gemv", x=x, packed=packed, y=y)
     M, K, N = int(x.shape[0]), int(x.shape[1]), int(y.shape[1])
     need = w4a16_codec_packed_bytes(codec, N, K)
     if need == 0:
@@ -474,8 +495,7 @@ def w4a16_kv_attention(bits: int, q, kv, o, T: int, Hkv: int, workspace, stream=
         raise TypeError("q must be float16 and o float32")
     if q.dim() != 2 or tuple(o.shape) != tuple(q.shape) or int(q.shape[1]) != 128:
         raise ValueError("q and o must be [Hq, 128]")
-    if not (q.is_contiguous() and o.is_contiguous()):
-        raise ValueError("q and o must be contiguous")
+    _device_tensors("w4a16_kv_attention", q=q, kv=kv, o=o, workspace=workspace)
     Hq = int(q.shape[0])
     need = w4a16_kv_packed_bytes(bits, T, Hkv)
     if need == 0 or kv.numel() * kv.element_size() < need:

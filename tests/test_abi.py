@@ -243,3 +243,46 @@ def test_chain_call_rejects_before_any_hip_call(w4a16_lib):
     assert L.w4a16_gemv_chain(B, 1, 1, B + 4100, W, None) == w4.W4A16_ERR_ALIGN
     assert L.w4a16_gemv_chain(B, 1, 1, B + 4096, W - 1, None) == w4.W4A16_ERR_SIZE
     assert L.w4a16_gemv_chain(B, 1, 1, B + 4096, 256, None) == w4.W4A16_ERR_SIZE
+
+
+# ------------------------------------------------------ binding argument checks
+def test_binding_refuses_host_and_strided_tensors_before_any_gpu_call(w4a16_lib):
+    """The library takes bare device addresses: the binding refuses host
+    tensors, non-tensors and mismatched byte buffers with ValueError before
+    anything reaches it (these run on a machine without a GPU)."""
+    torch = pytest.importorskip("torch")
+    M, N, K = 1, 8, 64
+    x = torch.zeros((M, K), dtype=torch.float16)
+    y = torch.zeros((M, N), dtype=torch.float32)
+    packed = torch.zeros(w4.w4a16_packed_bytes(N, K), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w4.w4a16_gemv(x, packed, y)
+    with pytest.raises(ValueError, match="torch tensor"):
+        w4._device_tensors("w4a16_gemv", packed=packed.numpy())
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w4.w4a16_codec_gemv("q8_sym", x, packed, y)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w4.w4a16_gemv_chain(packed, 1, 1, torch.zeros(16, dtype=torch.int32))
+    q = torch.zeros((4, 128), dtype=torch.float16)
+    o = torch.zeros((4, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w4.w4a16_kv_attention(8, q, packed, o, 1, 1, torch.zeros(16))
+    # the per-tensor rules, checked directly (no GPU needed to build the fakes)
+
+    class Fake:
+        def __init__(self, device="cuda:0", contiguous=True, dtype="torch.uint8"):
+            self.is_cuda, self.device, self.dtype, self._c = True, device, dtype, contiguous
+
+        def is_contiguous(self):
+            return self._c
+
+        def data_ptr(self):
+            return 0x7F0000000000
+
+    w4._device_tensors("t", x=Fake(dtype="torch.float16"), packed=Fake())
+    with pytest.raises(ValueError, match="contiguous"):
+        w4._device_tensors("t", x=Fake(), packed=Fake(contiguous=False))
+    with pytest.raises(ValueError, match="uint8"):
+        w4._device_tensors("t", packed=Fake(dtype="torch.int32"))
+    with pytest.raises(ValueError, match="other tensors"):
+        w4._device_tensors("t", x=Fake(device="cuda:0"), y=Fake(device="cuda:1"))

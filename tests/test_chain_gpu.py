@@ -17,6 +17,7 @@ import pytest
 import bit_weight_quantized_w4a16_amd as w4
 import oracle
 import workload
+from parity import check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -47,14 +48,6 @@ class Chain:
         w4.w4a16_gemv_chain(self.plan_dev, len(self.items), self.M if M is None else M, self.workspace, stream)
 
 
-def check(y, y_ref, B, label):
-    ok = oracle.within_tolerance(y, y_ref, B)
-    if not ok.all():
-        bad = np.argwhere(~ok)[:5]
-        pytest.fail(f"{label}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. "
-                    f"{[(tuple(i), y[tuple(i)], y_ref[tuple(i)]) for i in bad]}")
-
-
 def assert_workspace_clean(ch):
     ws = ch.workspace.cpu().numpy()
     assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == 0, "an ordering wait gave up"
@@ -72,7 +65,8 @@ def test_chain_mixed_shapes_vs_oracle(w4a16_lib, M):
     torch.cuda.synchronize()
     for it, (x, codes, scale, mn) in zip(ch.items, problems):
         y_ref, B = oracle.gemv(x, codes, scale, mn)
-        check(it["y"].cpu().numpy().astype(np.float64), y_ref, B, f"M={M} N={it['N']} K={it['K']}")
+        check(it["y"].cpu().numpy().astype(np.float64), y_ref, B, f"M={M} N={it['N']} K={it['K']}",
+              inputs=(x, codes, scale, mn))
     assert_workspace_clean(ch)
 
 
@@ -90,7 +84,8 @@ def test_chain_llama8b_layer_sampled(w4a16_lib):
         N = it["N"]
         rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N), rng.choice(N, 256, replace=False)]))
         y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
-        check(it["y"].cpu().numpy().astype(np.float64)[:, rows], y_ref, B, f"llama8b_layer N={N} K={it['K']}")
+        check(it["y"].cpu().numpy().astype(np.float64)[:, rows], y_ref, B, f"llama8b_layer N={N} K={it['K']}",
+              inputs=(x, codes, scale, mn), rows=rows)
     assert_workspace_clean(ch)
 
 
@@ -127,7 +122,8 @@ def test_chain_honours_read_after_write(w4a16_lib):
         y0 = ch.items[0]["y"].cpu().numpy()
         assert np.array_equal(y0, y0_exact)
         y_ref, B = oracle.gemv(p1[0], p1[1], p1[2], p1[3])
-        check(ch.items[1]["y"].cpu().numpy().astype(np.float64), y_ref, B, f"dependent product, rep {rep}")
+        check(ch.items[1]["y"].cpu().numpy().astype(np.float64), y_ref, B, f"dependent product, rep {rep}",
+              inputs=(p1[0], p1[1], p1[2], p1[3]))
         assert_workspace_clean(ch)
 
 

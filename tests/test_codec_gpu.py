@@ -12,6 +12,7 @@ import pytest
 import bit_weight_quantized_w4a16_amd as w4
 import oracle
 import workload
+from parity import check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -30,14 +31,6 @@ def run_codec(codec, x, codes, scale, mn):
     return y.cpu().numpy().astype(np.float64)
 
 
-def check(y, y_ref, B, label):
-    ok = oracle.within_tolerance(y, y_ref, B)
-    if not ok.all():
-        bad = np.argwhere(~ok)[:5]
-        detail = [(tuple(i), y[tuple(i)], y_ref[tuple(i)], oracle.tolerance(B)[tuple(i)]) for i in bad]
-        pytest.fail(f"{label}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. {detail}")
-
-
 SMALL = [
     (1, 1, 32), (1, 5, 160), (2, 17, 2080), (3, 33, 4096), (4, 7, 4128), (5, 9, 8192),
     (6, 65, 2048), (7, 12, 6176), (8, 4097, 256), (1, 4097, 4096), (8, 13, 14336), (1, 9, 16416),
@@ -51,7 +44,7 @@ def test_codec_small_shapes_full(w4a16_lib, codec, M, N, K):
     x, codes, scale, mn = workload.random_codec_problem(codec, M * 131 + N * 7 + K, M, N, K, outliers=(K >= 1000))
     y = run_codec(codec, x, codes, scale, mn)
     y_ref, B = C.gemv(codec, x, codes, scale, mn)
-    check(y, y_ref, B, f"{codec} M={M} N={N} K={K}")
+    check(y, y_ref, B, f"{codec} M={M} N={N} K={K}", inputs=(x, codes, scale, mn), codec=codec)
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -62,7 +55,7 @@ def test_codec_long_k_multi_pass(w4a16_lib, codec, M, K):
     x, codes, scale, mn = workload.random_codec_problem(codec, K + M, M, N, K, outliers=True)
     y = run_codec(codec, x, codes, scale, mn)
     y_ref, B = C.gemv(codec, x, codes, scale, mn)
-    check(y, y_ref, B, f"{codec} M={M} K={K}")
+    check(y, y_ref, B, f"{codec} M={M} K={K}", inputs=(x, codes, scale, mn), codec=codec)
 
 
 def _sample_rows(N, seed, count=256):
@@ -82,7 +75,7 @@ def test_codec_llama8b_layer_sampled(w4a16_lib, codec, M):
         y = run_codec(codec, x, codes, scale, mn)
         rows = _sample_rows(p.N, pi)
         y_ref, B = C.gemv_rows(codec, x, codes, scale, mn, rows)
-        check(y[:, rows], y_ref, B, f"{codec} M={M} {p.name}")
+        check(y[:, rows], y_ref, B, f"{codec} M={M} {p.name}", inputs=(x, codes, scale, mn), rows=rows, codec=codec)
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -94,7 +87,7 @@ def test_codec_several_tiles_per_workgroup_sampled(w4a16_lib, codec, M, N, K):
     y = run_codec(codec, x, codes, scale, mn)
     rows = _sample_rows(N, M)
     y_ref, B = C.gemv_rows(codec, x, codes, scale, mn, rows)
-    check(y[:, rows], y_ref, B, f"{codec} M={M} N={N} K={K}")
+    check(y[:, rows], y_ref, B, f"{codec} M={M} N={N} K={K}", inputs=(x, codes, scale, mn), rows=rows, codec=codec)
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -130,8 +123,10 @@ def test_pal4_kernel_with_an_affine_palette_matches_the_q4_kernel(w4a16_lib):
     ya = run_codec("q4", x, codes, np.repeat(s[:, None], G, 1).astype(np.float16),
                    np.repeat(m[:, None], G, 1).astype(np.float16))
     y_ref, B = C.gemv("pal4", x, codes, lut)
-    check(yp, y_ref, B, "pal4 affine palette")
-    check(ya, y_ref, B, "q4 with the palette's scale and min")
+    check(yp, y_ref, B, "pal4 affine palette", inputs=(x, codes, lut, None), codec="pal4")
+    check(ya, y_ref, B, "q4 with the palette's scale and min",
+          inputs=(x, codes, np.repeat(s[:, None], G, 1).astype(np.float16),
+                  np.repeat(m[:, None], G, 1).astype(np.float16)))
 
 
 def test_codec_q4_is_w4a16_gemv(w4a16_lib):

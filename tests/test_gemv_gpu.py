@@ -12,6 +12,7 @@ import pytest
 import bit_weight_quantized_w4a16_amd as w4
 import oracle
 import workload
+from parity import check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -33,14 +34,6 @@ def run_gpu(x, codes, scale, mn, stream=None):
     w4.w4a16_gemv(xd, packed, y, stream)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
-
-
-def check(y, y_ref, B, label):
-    ok = oracle.within_tolerance(y, y_ref, B)
-    if not ok.all():
-        bad = np.argwhere(~ok)[:5]
-        detail = [(tuple(i), y[tuple(i)], y_ref[tuple(i)], oracle.tolerance(B)[tuple(i)]) for i in bad]
-        pytest.fail(f"{label}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. {detail}")
 
 
 def sample_rows(N, seed, count=384):
@@ -65,7 +58,7 @@ def test_small_shapes_full(w4a16_lib, M, N, K):
     x, codes, scale, mn = workload.random_problem(M * 131 + N * 7 + K, M, N, K, outliers=(K >= 1000))
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(y, y_ref, B, f"M={M} N={N} K={K}")
+    check(y, y_ref, B, f"M={M} N={N} K={K}", inputs=(x, codes, scale, mn))
 
 
 # Enough tiles that a workgroup walks several of them (two load buffers
@@ -80,7 +73,7 @@ def test_several_tiles_per_workgroup_full(w4a16_lib, M, N, K):
     x, codes, scale, mn = workload.random_problem(M * 977 + N, M, N, K, outliers=True)
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn, threads=8)
-    check(y, y_ref, B, f"M={M} N={N} K={K}")
+    check(y, y_ref, B, f"M={M} N={N} K={K}", inputs=(x, codes, scale, mn))
 
 
 @pytest.mark.parametrize("M,K", [(1, 131072), (1, 131104), (8, 32800), (4, 32768)])
@@ -91,7 +84,7 @@ def test_long_k_multi_pass(w4a16_lib, M, K):
     x, codes, scale, mn = workload.random_problem(K + M, M, N, K, outliers=True)
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(y, y_ref, B, f"M={M} N={N} K={K}")
+    check(y, y_ref, B, f"M={M} N={N} K={K}", inputs=(x, codes, scale, mn))
 
 
 # --------------------------------------------------------- closed forms, edges
@@ -113,7 +106,7 @@ def test_zero_codes_closed_form(w4a16_lib):
     xs = x.astype(np.float64).reshape(M, K // 32, 32).sum(axis=2)
     expect = xs @ mn.astype(np.float64).T
     _, B = oracle.gemv(x, codes, scale, mn)
-    check(y, expect, B, "zero codes")
+    check(y, expect, B, "zero codes", inputs=(x, codes, scale, mn))
 
 
 def test_one_hot_x_picks_weights(w4a16_lib):
@@ -155,7 +148,7 @@ def test_bitwise_repeatable_and_stream_ordered(w4a16_lib):
     for y in ys[1:]:
         assert np.array_equal(a.view(np.uint32), y.cpu().numpy().view(np.uint32))
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(a.astype(np.float64), y_ref, B, "stream")
+    check(a.astype(np.float64), y_ref, B, "stream", inputs=(x, codes, scale, mn))
 
 
 def test_timed_launch_matches_and_times_the_kernel(w4a16_lib):
@@ -186,7 +179,7 @@ def test_y_is_overwritten_not_accumulated(w4a16_lib):
     w4.w4a16_gemv(xd, packed, y)
     torch.cuda.synchronize()
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(y.cpu().numpy().astype(np.float64), y_ref, B, "overwrite")
+    check(y.cpu().numpy().astype(np.float64), y_ref, B, "overwrite", inputs=(x, codes, scale, mn))
 
 
 def test_fp16_extremes_in_x(w4a16_lib):
@@ -196,7 +189,7 @@ def test_fp16_extremes_in_x(w4a16_lib):
     x[1, ::3] = np.float16(2 ** -20)          # many subnormals
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(y, y_ref, B, "fp16 extremes")
+    check(y, y_ref, B, "fp16 extremes", inputs=(x, codes, scale, mn))
 
 
 def test_beyond_4gib_of_weights_sampled(w4a16_lib):
@@ -220,7 +213,7 @@ def test_beyond_4gib_of_weights_sampled(w4a16_lib):
     y = run_gpu(x, codes, scale, mn)
     rows = sample_rows(N, 77, count=256)
     y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
-    check(y[:, rows], y_ref, B, f"M={M} N={N} K={K}")
+    check(y[:, rows], y_ref, B, f"M={M} N={N} K={K}", inputs=(x, codes, scale, mn), rows=rows)
 
 
 # ------------------------------------------------------ named Llama workloads
@@ -229,7 +222,7 @@ def test_gemv4096_full(w4a16_lib):
     x, codes, scale, mn = workload.gemv_inputs("gemv4096", 0, 0, 1)
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn)
-    check(y, y_ref, B, "gemv4096")
+    check(y, y_ref, B, "gemv4096", inputs=(x, codes, scale, mn))
 
 
 @pytest.mark.parametrize("proj", [0, 1, 2, 3])
@@ -238,7 +231,7 @@ def test_llama8b_layer_full(w4a16_lib, proj):
     print(f"[shape] llama8b_layer proj={proj} N={codes.shape[0]} K={x.shape[1]}", flush=True)
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn, threads=8)
-    check(y, y_ref, B, f"llama8b_layer proj {proj}")
+    check(y, y_ref, B, f"llama8b_layer proj {proj}", inputs=(x, codes, scale, mn))
 
 
 @pytest.mark.parametrize("M", [4, 8])
@@ -248,7 +241,7 @@ def test_llama8b_verify_full(w4a16_lib, M, proj):
     print(f"[shape] llama8b_verify M={M} proj={proj} N={codes.shape[0]} K={x.shape[1]}", flush=True)
     y = run_gpu(x, codes, scale, mn)
     y_ref, B = oracle.gemv(x, codes, scale, mn, threads=8)
-    check(y, y_ref, B, f"llama8b_verify M={M} proj {proj}")
+    check(y, y_ref, B, f"llama8b_verify M={M} proj {proj}", inputs=(x, codes, scale, mn))
 
 
 @pytest.mark.parametrize("layer", [0, 31])
@@ -259,7 +252,7 @@ def test_llama8b_step_sampled(w4a16_lib, layer, proj):
     y = run_gpu(x, codes, scale, mn)
     rows = sample_rows(codes.shape[0], layer * 4 + proj)
     y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
-    check(y[:, rows], y_ref, B, f"llama8b_step layer {layer} proj {proj}")
+    check(y[:, rows], y_ref, B, f"llama8b_step layer {layer} proj {proj}", inputs=(x, codes, scale, mn), rows=rows)
 
 
 @pytest.mark.parametrize("M", [1, 8])
@@ -272,4 +265,4 @@ def test_llama70b_sampled(w4a16_lib, M, proj):
     y = run_gpu(x, codes, scale, mn)
     rows = sample_rows(codes.shape[0], 100 + proj)
     y_ref, B = oracle.gemv_rows(x, codes, scale, mn, rows)
-    check(y[:, rows], y_ref, B, f"llama70b M={M} proj {proj}")
+    check(y[:, rows], y_ref, B, f"llama70b M={M} proj {proj}", inputs=(x, codes, scale, mn), rows=rows)

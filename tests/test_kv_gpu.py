@@ -11,6 +11,7 @@ import pytest
 import bit_weight_quantized_w4a16_amd as w4
 import oracle
 import workload
+from kv_sentinel import sentinel_closed_form
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -80,6 +81,21 @@ def test_kv_merge_over_several_chunks(w4a16_lib, bits, T, Hq):
     o = run_kv(bits, q, cache)
     o_ref, B = A.attention(bits, q, *cache)
     check(o, o_ref, B, f"bits={bits} T={T} Hq={Hq} Hkv=1")
+
+
+@pytest.mark.parametrize("bits,T,Hq,Hkv", [(8, 38863, 32, 8), (4, 77726, 32, 8), (8, 40000, 4, 1), (4, 80000, 8, 1)])
+def test_kv_sentinel_every_block_counted_once(w4a16_lib, bits, T, Hq, Hkv):
+    """Zero keys (every token weighs 1/T) and values that are zero except one
+    channel per 64-token block: a block the kernel skipped or counted twice
+    moves its channel by at least 8 %, far outside the 0.1 % tolerance. At the
+    full 8B contexts and at the one-KV-head shapes whose merge walks several
+    chunks of partials."""
+    print(f"[kv sentinel] bits={bits} T={T} Hq={Hq} Hkv={Hkv}", flush=True)
+    cache = workload.kv_sentinel_cache(bits, T, Hkv)
+    q = workload.kv_query(81, 0, Hq)
+    o = run_kv(bits, q, cache)
+    o_ref, B = sentinel_closed_form(bits, T, Hq, Hkv)
+    check(o, o_ref, B, f"sentinel bits={bits} T={T} Hq={Hq} Hkv={Hkv}")
 
 
 @pytest.mark.parametrize("bits", [8, 4])

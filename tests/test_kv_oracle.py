@@ -152,3 +152,143 @@ def test_kv_recipe_shapes():
         assert cache[0].shape == ((5, 8, 128) if bits == 8 else (5, 8, 64))
         assert cache[1].shape == (5, 8, 4) and (cache[2] is None) == (bits == 8)
     assert workload.kv_query(1, 0).shape == (32, 128)
+
+
+# --------------------------------------------------------------------------
+# Temperature: a hand-derived two-token case (tests/golden/kv_two_token.json)
+# --------------------------------------------------------------------------
+import json  # noqa: E402
+import os  # noqa: E402
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_two_token.json")))
+
+
+def _two_token_inputs(case):
+    """The fixture's cache: one query head, one KV head, two tokens."""
+    bits = case["bits"]
+    q = np.zeros((1, D), np.float16)
+    q[0, 0] = 1.0
+    if bits == 8:
+        kc = np.zeros((2, 1, D), np.int8)
+        kc[0, 0, 0] = case["k_code0"]
+        vc = np.zeros((2, 1, D), np.int8)
+        vc[0] = case["v_code0"]
+        vc[1] = case["v_code1"]
+        km = vm = None
+    else:
+        kc = np.zeros((2, 1, D // 2), np.uint8)
+        kc[0, 0, 0] = case["k_code0"]                       # low nibble: dim 0
+        vc = np.zeros((2, 1, D // 2), np.uint8)
+        vc[0] = case["v_code0"] | (case["v_code0"] << 4)
+        vc[1] = case["v_code1"] | (case["v_code1"] << 4)
+        km = np.full((2, 1, 4), case["k_min"], np.float16)
+        vm = np.full((2, 1, 4), case["v_min"], np.float16)
+    ks = np.full((2, 1, 4), case["k_scale"], np.float16)
+    vs = np.full((2, 1, 4), case["v_scale"], np.float16)
+    return bits, q, (kc, ks, km, vc, vs, vm)
+
+
+def _golden_matches(case, attention):
+    bits, q, cache = _two_token_inputs(case)
+    o, B = attention(bits, q, *cache)
+    return np.allclose(o, case["o"], rtol=1e-13, atol=0) and np.allclose(B, case["B"], rtol=1e-13, atol=0)
+
+
+def test_two_token_golden_values_are_their_closed_forms():
+    d = GOLDEN["delta"]
+    assert d == pytest.approx(8 / math.sqrt(128), rel=1e-15)
+    p0 = 1 / (1 + math.exp(-d))
+    c8, c4 = GOLDEN["cases"]
+    assert c8["o"] == pytest.approx(math.tanh(d / 2), rel=1e-15) and c8["B"] == 1.0
+    assert c4["o"] == pytest.approx(1.875 * p0 - 1, rel=1e-15)
+    assert c4["B"] == pytest.approx(1 - 0.125 * p0, rel=1e-15)
+
+
+@pytest.mark.parametrize("case", GOLDEN["cases"], ids=lambda c: f"int{c['bits']}")
+def test_two_token_golden(case):
+    assert _golden_matches(case, A.attention)
+
+
+class _NumpyWithSqrt:
+    """numpy, except for sqrt: a planted mistake in the oracle's temperature."""
+
+    def __init__(self, sqrt):
+        self._sqrt = sqrt
+
+    def __getattr__(self, name):
+        return self._sqrt if name == "sqrt" else getattr(np, name)
+
+
+@pytest.mark.parametrize("mutant", [lambda x: 1.0, lambda x: x, lambda x: x ** 0.25],
+                         ids=["no temperature", "1/D", "D^-1/4"])
+def test_two_token_golden_catches_a_wrong_temperature(monkeypatch, mutant):
+    monkeypatch.setattr(A, "np", _NumpyWithSqrt(mutant))
+    assert not any(_golden_matches(case, A.attention) for case in GOLDEN["cases"])
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_constant_score_shift_invariance(bits):
+    """Adding the same amount to every token's score leaves the weights alone:
+    give every token the same key value in dim 127, then change the query in
+    that dim."""
+    q, (kc, ks, km, vc, vs, vm) = _problem(bits, 90, 4, 1, seed=9)
+    ks = ks.copy()
+    ks[:, :, 3] = 0.25
+    kc = kc.copy()
+    if bits == 8:
+        kc[:, :, 127] = 6
+    else:
+        kc[:, :, 63] = (kc[:, :, 63] & 0x0F) | (6 << 4)     # high nibble: dim 127
+        km = km.copy()
+        km[:, :, 3] = -0.5
+    o, B = A.attention(bits, q, kc, ks, km, vc, vs, vm)
+    q2 = q.copy()
+    q2[:, 127] = (q2[:, 127].astype(np.float32) + 2.0).astype(np.float16)
+    o2, B2 = A.attention(bits, q2, kc, ks, km, vc, vs, vm)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(B2, B, rtol=1e-12, atol=1e-14)
+    q3 = q.copy()
+    q3[:, 5] = (q3[:, 5].astype(np.float32) + 2.0).astype(np.float16)   # a dim the keys differ in
+    o3, _ = A.attention(bits, q3, kc, ks, km, vc, vs, vm)
+    assert np.abs(o3 - o).max() > 1e-6
+
+
+# --------------------------------------------------------------------------
+# Sentinel cache: every block of 64 tokens visible on its own
+# --------------------------------------------------------------------------
+from kv_sentinel import sentinel_closed_form  # noqa: E402
+
+@pytest.mark.parametrize("bits,T,Hq,Hkv", [(8, 3001, 32, 8), (4, 2222, 16, 2), (4, 300, 8, 1)])
+def test_sentinel_cache_oracle_is_its_closed_form(bits, T, Hq, Hkv):
+    cache = workload.kv_sentinel_cache(bits, T, Hkv)
+    q = workload.kv_query(77, 0, Hq)
+    o, B = A.attention(bits, q, *cache)
+    o_cf, B_cf = sentinel_closed_form(bits, T, Hq, Hkv)
+    np.testing.assert_allclose(o, o_cf, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(B, B_cf, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits,T,Hkv", [(8, 38863, 8), (4, 77726, 8), (8, 40000, 1), (4, 80000, 1)])
+def test_sentinel_cache_shows_every_block(bits, T, Hkv):
+    """At the full 8B contexts and the one-KV-head merge shapes, removing any
+    single block (or counting it twice) moves its channel by far more than the
+    tolerance: each block carries at least 8 % of its channel (a tenth of
+    it with one KV head over 80,000 tokens), against a 0.1 % tolerance."""
+    nb = -(-T // workload.KV_BLOCK)
+    share = np.zeros((Hkv, D))
+    counts = np.zeros((Hkv, D))
+    for b in range(nb):
+        g, d = workload.kv_sentinel_channel(b, Hkv)
+        counts[g, d] += min(T, (b + 1) * workload.KV_BLOCK) - b * workload.KV_BLOCK
+    worst = 1.0
+    for b in range(nb):
+        g, d = workload.kv_sentinel_channel(b, Hkv)
+        n = min(T, (b + 1) * workload.KV_BLOCK) - b * workload.KV_BLOCK
+        worst = min(worst, n / counts[g, d])
+        share[g, d] = max(share[g, d], n / counts[g, d])
+    o, B = sentinel_closed_form(bits, T, Hkv, Hkv)
+    tol = A.tolerance(B)
+    # the smallest block moves its channel by worst * o, against a tolerance of 1e-3 * o + 1e-5
+    marked = counts > 0
+    assert worst >= 0.08, worst
+    assert (worst * o[marked] > 10 * tol[marked]).all()

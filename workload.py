@@ -213,6 +213,44 @@ def kv_cache(bits: int, wid: int, layer: int, T: int, Hkv: int = KV_HKV):
     return tuple(out)
 
 
+KV_BLOCK = 64  # tokens per block of the sentinel recipe (the kernel's unit of work)
+KV_SENTINEL_CODE = 3  # the one nonzero value code of the sentinel cache
+
+
+def kv_sentinel_channel(b: int, Hkv: int) -> tuple:
+    """(KV head, dim) that token block b of the sentinel cache marks: block b
+    marks channel b mod (Hkv * 128), so a channel is marked by at most
+    ceil(blocks / (Hkv * 128)) blocks."""
+    ch = b % (Hkv * KV_D)
+    return ch // KV_D, ch % KV_D
+
+
+def kv_sentinel_cache(bits: int, T: int, Hkv: int = KV_HKV):
+    """A cache in which every block of 64 tokens is visible on its own: all
+    keys are zero (so every token gets the same attention weight), all values
+    are zero except that each token of block b holds KV_SENTINEL_CODE in the
+    one channel kv_sentinel_channel(b) marks. Scales 0.25, mins 0 (binary16)."""
+    if bits not in (8, 4) or T < 1 or Hkv < 1:
+        raise ValueError("bits must be 8 or 4, T and Hkv positive")
+    G = KV_D // GROUP
+    if bits == 8:
+        kc = np.zeros((T, Hkv, KV_D), np.int8)
+        vc = np.zeros((T, Hkv, KV_D), np.int8)
+    else:
+        kc = np.zeros((T, Hkv, KV_D // 2), np.uint8)
+        vc = np.zeros((T, Hkv, KV_D // 2), np.uint8)
+    for b in range(-(-T // KV_BLOCK)):
+        g, d = kv_sentinel_channel(b, Hkv)
+        t0, t1 = b * KV_BLOCK, min(T, (b + 1) * KV_BLOCK)
+        if bits == 8:
+            vc[t0:t1, g, d] = KV_SENTINEL_CODE
+        else:
+            vc[t0:t1, g, d // 2] = KV_SENTINEL_CODE << (4 * (d % 2))
+    scale = np.full((T, Hkv, G), 0.25, np.float16)
+    mn = None if bits == 8 else np.zeros((T, Hkv, G), np.float16)
+    return kc, scale, mn, vc, scale.copy(), None if mn is None else mn.copy()
+
+
 def kv_query(wid: int, layer: int, Hq: int = KV_HQ) -> np.ndarray:
     """Seeded query q binary16 [Hq, 128]."""
     return _rng(wid, layer, 0, _T_KV + 9).standard_normal(size=(Hq, KV_D)).astype(np.float16)
