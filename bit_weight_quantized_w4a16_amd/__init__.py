@@ -53,10 +53,20 @@ EXPORTS = (
     "w4a16_kv_attention",
     "w4a16_kv_attention_timed",
     "w4a16_kv_launch_shape",
+    "w4a16_blob_check",
+    "w4a16_blob_mismatches",
 )
 
 W4A16_CHAIN_WORKSPACE_BYTES = 69632
-W4A16_CHAIN_ERROR_OFFSET = 256  # uint32: nonzero once an ordering wait gave up
+W4A16_CHAIN_MAX_ENTRIES = 1048576
+W4A16_CHAIN_ERROR_OFFSET = 256  # uint32 error word of the chain workspace, a set of these bits:
+W4A16_CHAIN_ERR_WAIT = 1        # an ordering wait gave up
+W4A16_CHAIN_ERR_PLAN = 2        # the plan header does not match (count, M)
+W4A16_CHAIN_ERR_BLOB = 4        # an entry's blob header does not match its (N, K)
+
+W4A16_BLOB_MAGIC = 0x36313457   # first four bytes of every packed weight blob
+W4A16_LAYOUT_VERSION = 6
+W4A16_BLOB_HEADER_BYTES = 256
 
 
 class ChainEntry(ctypes.Structure):
@@ -130,6 +140,10 @@ def lib() -> ctypes.CDLL:
     L.w4a16_kv_launch_shape.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_status_string.argtypes = [c_i32]
+    L.w4a16_blob_check.restype = c_i32
+    L.w4a16_blob_check.argtypes = [c_vp, c_sz, c_i32, c_i32, c_i32]
+    L.w4a16_blob_mismatches.restype = c_i32
+    L.w4a16_blob_mismatches.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     _lib = L
     return L
 
@@ -148,6 +162,25 @@ def w4a16_status_string(status: int) -> str:
 
 def w4a16_packed_bytes(N: int, K: int) -> int:
     return int(lib().w4a16_packed_bytes(int(N), int(K)))
+
+
+def w4a16_blob_check(blob: np.ndarray, codec, N: int, K: int) -> int:
+    """Status of w4a16_blob_check on a host blob (W4A16_OK if it is a blob of
+    this layout for (codec, N, K) and holds all of its bytes)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    if blob.nbytes < W4A16_BLOB_HEADER_BYTES:
+        return W4A16_ERR_SIZE
+    return int(lib().w4a16_blob_check(blob.ctypes.data, blob.nbytes, codec_id(codec), int(N), int(K)))
+
+
+def w4a16_blob_mismatches() -> int:
+    """Launches on the current device since the last call whose blob header
+    did not match their call (they wrote nothing); resets the count."""
+    out = ctypes.c_uint32(0)
+    st = lib().w4a16_blob_mismatches(ctypes.byref(out))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_blob_mismatches")
+    return int(out.value)
 
 
 def w4a16_pack(codes: np.ndarray, scale: np.ndarray, mn: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:

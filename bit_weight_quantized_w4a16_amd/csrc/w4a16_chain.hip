@@ -68,7 +68,7 @@ using namespace w4a16_dev;
 namespace {
 
 constexpr uint32_t kChainMagic = 0x48433457u;  // "W4CH"
-constexpr uint32_t kChainVersion = 4;
+constexpr uint32_t kChainVersion = 5;
 constexpr unsigned kSpinLimit = 1u << 20;      // global polls before an ordering wait gives up (~1 s)
 constexpr unsigned kLdsSpinLimit = 1u << 24;   // LDS polls before a wave gives up (about a second)
 constexpr int kLeaves = 16;                    // leaf counters of the ordering tree
@@ -86,6 +86,7 @@ constexpr int kXBytes = 32768;                 // LDS activations of one pass ov
 constexpr int kPartFloats = 1024;              // LDS segment sums and running sums of a block of tiles
 constexpr int kMaxBlockTiles = 32;
 constexpr int kLoadCoherent = 16;              // buffer-load cache policy: device-coherent (sc1)
+constexpr int32_t kMaxChain = W4A16_CHAIN_MAX_ENTRIES;
 static_assert(kRing % 8 == 0 && kRing % 4 == 0,
               "a slot is always filled by the same loader and emptied by the same compute wave");
 
@@ -136,6 +137,9 @@ __device__ __forceinline__ unsigned ld_coherent(const unsigned* p) {
 __device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void or_coherent(unsigned* p, unsigned v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_coherent(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -155,6 +159,7 @@ struct ChainLds {
   int go;                                // stages released
   int staged;                            // compute waves done staging, all stagings so far
   int abort;                             // a wait gave up: every wave leaves
+  int bad_blob;                          // some entry's blob header does not match it: nothing is stored
 };
 
 // One stage of a workgroup's walk: block b of its tiles of product p, pass c
@@ -291,15 +296,18 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
   if (hdr->magic != kChainMagic || hdr->version != kChainVersion || hdr->count != count || hdr->M != M ||
-      hdr->ring != RING || hdr->compute_waves != NCW)
-    return;  // every workgroup sees the same header, so all leave together
+      hdr->ring != RING || hdr->compute_waves != NCW) {
+    // every workgroup sees the same header, so all leave together
+    if (wg == 0 && threadIdx.x == 0) or_coherent(ws + kErrorWord, W4A16_CHAIN_ERR_PLAN);
+    return;
+  }
   const EntryPtr ents = (EntryPtr)(reinterpret_cast<uintptr_t>(hdr + 1));
   const unsigned inv = __builtin_amdgcn_readfirstlane(nwg > 1 ? 0xFFFFFFFFu / unsigned(nwg) + 1u : 0u);
 
   __shared__ ChainLds L;
   for (int i = threadIdx.x; i < kRing; i += blockDim.x) L.ready[i] = L.consumed[i] = 0;
   for (int i = threadIdx.x; i < kMaxBlockTiles; i += blockDim.x) L.tile_cnt[i] = 0;
-  if (threadIdx.x == 0) L.done = L.go = L.staged = L.abort = 0;
+  if (threadIdx.x == 0) L.done = L.go = L.staged = L.abort = L.bad_blob = 0;
   __syncthreads();  // the only workgroup barrier: nothing is in flight yet
 
   auto lds_aborted = [&]() __attribute__((always_inline)) {
@@ -354,7 +362,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
           ok = go = 0;
         } else if (++spins > kLdsSpinLimit) {  // starved: make every wave of the workgroup leave
           __hip_atomic_store(&L.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (lane == 0) add_coherent(ws + kErrorWord, 1u);
+          if (lane == 0) or_coherent(ws + kErrorWord, W4A16_CHAIN_ERR_WAIT);
           ok = go = 0;
         } else {
           __builtin_amdgcn_s_sleep(2);
@@ -415,7 +423,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   auto give_up = [&]() {
     aborted = true;
     if (lane == 0) {
-      add_coherent(ws + kErrorWord, 1u);
+      or_coherent(ws + kErrorWord, W4A16_CHAIN_ERR_WAIT);
       __hip_atomic_store(&L.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   };
@@ -468,14 +476,17 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   // this wave's share of the stage's activations, global -> LDS, with each
   // group's sum: lane item c*64 + lane + j*NCW*64 is group (item % XG) of the
   // pass for activation row item / XG (at most one item per lane: M * XS <= 8)
-  auto stage_x = [&](const Stage& s) {
+  // `between` runs (on the whole wave) once the loads are issued, before
+  // their data is needed
+  auto stage_x = [&](const Stage& s, auto&& between) {
     const int gb = s.sg0 * kSeg;
     const int item = cw * 64 + lane;
-    if (item < M * XG) {
-      const int m = item / XG, lg = item - m * XG;
-      const int g = gb + lg;
-      u32x4 v[4] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-      if (lg < s.ns * kSeg && g < s.G) {
+    const bool mine = item < M * XG;
+    const int m = item / XG, lg = item - m * XG;
+    const int g = gb + lg;
+    u32x4 v[4] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    {
+      if (mine && lg < s.ns * kSeg && g < s.G) {
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(s.e->x, M * s.G * 64);
         const int off = (m * s.G + g) * 64;
         if (s.xcoh) {
@@ -486,11 +497,46 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
           for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + q * 16, 0, 0);
         }
       }
+    }
+    between();
+    if (mine) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) L.xl[(m * 4 + q) * XG + lg] = v[q];
       L.xsl[m * XG + lg] = group_sum(v);
     }
   };
+
+  // Every entry's blob header, checked once, at the compute waves' first
+  // staging, behind that staging's activation loads (lane l of compute wave
+  // cw takes entries 64 (cw + r NCW) + l). A mismatch anywhere marks the
+  // workgroup's LDS flag before the wave joins the staging count, and every
+  // y store of the launch is made after such a count and skipped if the flag
+  // is set: a plan naming a wrong blob writes no y at all. The check costs
+  // about one memory latency (the entry's blob address, then its header) at
+  // the start of the launch and nothing in its loops.
+  bool checked = false;
+  auto check_blobs = [&]() __attribute__((always_inline)) {
+    if (checked) return;
+    checked = true;
+    typedef const __attribute__((address_space(1))) uint32_t* GlobalWords;
+    bool any = false;
+    for (int p0 = cw * 64; p0 < count; p0 += NCW * 64) {
+      const int p = p0 + lane;
+      bool bad = false;
+      if (p < count) {
+        const GlobalWords h =
+            (GlobalWords)(reinterpret_cast<uintptr_t>(ents[p].codes) - uintptr_t(W4A16_BLOB_HEADER_BYTES));
+        bad = h[0] != W4A16_BLOB_MAGIC || h[1] != head_version_codec(W4A16_CODEC_Q4) ||
+              h[2] != uint32_t(ents[p].N) || h[3] != uint32_t(ents[p].G * kGroup);
+      }
+      any = any || __ballot(bad) != 0;
+    }
+    if (any && lane == 0) {
+      __hip_atomic_store(&L.bad_blob, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (wg == 0) or_coherent(ws + kErrorWord, W4A16_CHAIN_ERR_BLOB);
+    }
+  };
+  bool blob_ok = false;
 
   Stage s;
   s.ubase = 0;
@@ -500,11 +546,12 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   do {
     // activations: once per product when one pass holds all of K, else per stage
     if (s.nt > 0 && (s.passes > 1 || s.b == 0)) {
-      stage_x(s);
+      stage_x(s, check_blobs);
       compiler_fence();
       ++stagings;
       if (lane == 0) __hip_atomic_fetch_add(&L.staged, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (!lds_wait_ge(&L.staged, stagings * NCW)) break;
+      blob_ok = __hip_atomic_load(&L.bad_blob, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
     }
     // this wave's units of the stage
     const int units = s.nt * s.ns;
@@ -549,7 +596,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
           for (int sp = 0; sp < s.ns; ++sp) acc_y += seg[sp * (kTileRows * M) + rm];
           const int n = (s.tb0 + ti) * kTileRows + (lane >> 4);
           if (s.c == s.passes - 1) {
-            if (n < s.N) store_y<true>(s.e->y + size_t(lane & 15) * s.N + n, acc_y);
+            if (n < s.N && blob_ok) store_y<true>(s.e->y + size_t(lane & 15) * s.N + n, acc_y);
           } else {
             run[rm] = acc_y;
           }
@@ -624,8 +671,6 @@ chain_fn chain_for(int M) {
 
 std::atomic<int> g_chain_occupancy[kMaxM + 1];
 
-constexpr int32_t kMaxChain = 1 << 20;
-
 }  // namespace
 
 extern "C" size_t w4a16_chain_plan_bytes(int32_t count) {
@@ -675,11 +720,12 @@ extern "C" w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32
     const w4a16_chain_entry& e = entries[i];
     const int G = e.K / kGroup;
     const size_t codes_region = (size_t(e.N) * size_t(e.K) / 2 + 255) / 256 * 256;
+    const uint8_t* base = static_cast<const uint8_t*>(e.packed);
     ChainEntry c;
     std::memset(&c, 0, sizeof(c));
     c.x = static_cast<const u32x4*>(e.x);
-    c.codes = static_cast<const u32x4*>(e.packed);
-    c.sm = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(e.packed) + codes_region);
+    c.codes = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES);  // the header precedes the codes
+    c.sm = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES + codes_region);
     c.y = e.y;
     c.N = e.N;
     c.G = G;

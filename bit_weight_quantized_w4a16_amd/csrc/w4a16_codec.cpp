@@ -68,3 +68,23 @@ extern "C" w4a16_status w4a16_codec_launch_shape(int32_t codec, int32_t M, int32
     default: return w4a16_codecs::shape_pal4(M, K, out);
   }
 }
+
+extern "C" w4a16_status w4a16_blob_mismatches(uint32_t* count) {
+  if (!count) return W4A16_ERR_NULL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  unsigned* words[] = {w4a16_host::q4_mismatch_word(dev), w4a16_codecs::mismatch_word_q4_sym(dev),
+                       w4a16_codecs::mismatch_word_q5(dev), w4a16_codecs::mismatch_word_q8_sym(dev),
+                       w4a16_codecs::mismatch_word_pal4(dev)};
+  if (hipDeviceSynchronize() != hipSuccess) return W4A16_ERR_HIP;
+  uint32_t total = 0;
+  for (unsigned* w : words) {
+    unsigned v = 0;
+    if (!w || hipMemcpy(&v, w, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess || hipMemset(w, 0, sizeof(v)) != hipSuccess)
+      return W4A16_ERR_HIP;
+    total += v;
+  }
+  if (hipDeviceSynchronize() != hipSuccess) return W4A16_ERR_HIP;
+  *count = total;
+  return W4A16_OK;
+}

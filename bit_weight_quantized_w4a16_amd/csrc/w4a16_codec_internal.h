@@ -14,10 +14,11 @@ namespace w4a16_codecs {
 
 // Region layout of one packed blob of a codec (byte offsets; see include/w4a16.h).
 struct Regions {
-  size_t codes;  // bytes of the code region before its 256-byte padding
-  size_t aux;    // offset of the fifth-bit tiles (5-bit code), else 0
-  size_t side;   // offset of the scale (and min) tiles
-  size_t total;  // w4a16_codec_packed_bytes
+  size_t codes_at;  // offset of the code region (just past the blob header)
+  size_t codes;     // bytes of the code region before its 256-byte padding
+  size_t aux;       // offset of the fifth-bit tiles (5-bit code), else 0
+  size_t side;      // offset of the scale (and min) tiles
+  size_t total;     // w4a16_codec_packed_bytes
 };
 // false if the codec is unknown or (N, K) is out of range
 bool regions(int codec, int32_t N, int32_t K, Regions& r);
@@ -42,5 +43,11 @@ w4a16_status shape_q4_sym(int M, int K, int32_t shape[3]);
 w4a16_status shape_q5(int M, int K, int32_t shape[3]);
 w4a16_status shape_q8_sym(int M, int K, int32_t shape[3]);
 w4a16_status shape_pal4(int M, int K, int32_t shape[3]);
+// Each codec module's count of launches whose blob header did not match
+// their call, on device dev (current); nullptr if it cannot be located.
+unsigned* mismatch_word_q4_sym(int dev);
+unsigned* mismatch_word_q5(int dev);
+unsigned* mismatch_word_q8_sym(int dev);
+unsigned* mismatch_word_pal4(int dev);
 
 }  // namespace w4a16_codecs

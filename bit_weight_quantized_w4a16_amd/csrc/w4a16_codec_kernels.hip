@@ -42,6 +42,10 @@ using Codec = CodecPal4;
 #error "unknown W4A16_CODEC_ID"
 #endif
 
+// Launches of this module whose blob header did not match their call, one
+// word per device (reached from the host through hipGetSymbolAddress).
+__device__ unsigned blob_mismatch_count;
+
 // CODEC is the codec's id (it names the kernel in profiles:
 // codec_kernel<codec, M, groups per lane, mode>).
 template <int CODEC, int M, int GPL, int MODE>
@@ -49,7 +53,8 @@ __global__ void __launch_bounds__(64 * max_waves_of<Codec>(M, GPL))
 codec_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ aux,
              const void* __restrict__ side, float* __restrict__ y, int N, int G, int T, int nchunks, int tpb,
              int nwaves) {
-  gemv_body<Codec, M, GPL, MODE>(x, WeightPtrs{codes, aux, side}, y, N, G, T, nchunks, tpb, nwaves);
+  gemv_body<Codec, M, GPL, MODE>(x, WeightPtrs{codes, aux, side}, y, N, G, T, nchunks, tpb, nwaves,
+                                 &blob_mismatch_count);
 }
 
 typedef void (*kernel_fn)(const u32x4*, const u32x4*, const u32x4*, const void*, float*, int, int, int, int, int,
@@ -136,7 +141,7 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
                       grid);
   const uint8_t* base = static_cast<const uint8_t*>(l.packed);
   const u32x4* xp = static_cast<const u32x4*>(l.x);
-  const u32x4* cp = reinterpret_cast<const u32x4*>(base);
+  const u32x4* cp = reinterpret_cast<const u32x4*>(base + reg.codes_at);
   const u32x4* ap = reg.aux ? reinterpret_cast<const u32x4*>(base + reg.aux) : nullptr;
   const void* sp = base + reg.side;
   float* y = l.y;
@@ -148,20 +153,29 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
   return W4A16_OK;
 }
 
+unsigned* mismatch_word(int dev) {
+  static std::atomic<unsigned*> cache[w4a16_host::kMaxDevices];
+  return w4a16_host::device_word(reinterpret_cast<const void*>(&blob_mismatch_count), cache, dev);
+}
+
 }  // namespace
 
 namespace w4a16_codecs {
 #if W4A16_CODEC_ID == 1
 w4a16_status enqueue_q4_sym(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_q4_sym(int M, int K, int32_t out[3]) { return shape(M, K, out); }
+unsigned* mismatch_word_q4_sym(int dev) { return mismatch_word(dev); }
 #elif W4A16_CODEC_ID == 2
 w4a16_status enqueue_q5(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_q5(int M, int K, int32_t out[3]) { return shape(M, K, out); }
+unsigned* mismatch_word_q5(int dev) { return mismatch_word(dev); }
 #elif W4A16_CODEC_ID == 3
 w4a16_status enqueue_q8_sym(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_q8_sym(int M, int K, int32_t out[3]) { return shape(M, K, out); }
+unsigned* mismatch_word_q8_sym(int dev) { return mismatch_word(dev); }
 #else
 w4a16_status enqueue_pal4(const Launch& l, const Regions& r) { return enqueue(l, r); }
 w4a16_status shape_pal4(int M, int K, int32_t out[3]) { return shape(M, K, out); }
+unsigned* mismatch_word_pal4(int dev) { return mismatch_word(dev); }
 #endif
 }  // namespace w4a16_codecs

@@ -11,6 +11,8 @@
 
 #include <cstdint>
 
+#include "w4a16.h"
+
 namespace w4a16_dev {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -123,6 +125,37 @@ constexpr int kLoadNT = 2;  // buffer-load cache policy: non-temporal stream
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
+}
+
+// The first 16 bytes of a packed blob's header (layout in include/w4a16.h):
+// magic, layout version | codec << 16, N, K.
+struct BlobHead {
+  uint32_t w[4];
+};
+__host__ __device__ constexpr uint32_t head_version_codec(int codec) {
+  return uint32_t(W4A16_LAYOUT_VERSION) | (uint32_t(codec) << 16);
+}
+
+// The header read through the constant address space (a blob is never
+// written during a launch): one scalar load, which the caller issues at the
+// start of the kernel.
+__device__ __forceinline__ BlobHead read_head(const void* blob) {
+  typedef const __attribute__((address_space(4))) uint32_t* Words;
+  const Words p = (Words)(reinterpret_cast<uintptr_t>(blob));
+  return BlobHead{{p[0], p[1], p[2], p[3]}};
+}
+
+// Does the header name this codec, N and K? Called where a result is stored.
+// The empty asm statement marks copies of the header words as changed there,
+// so the compiler cannot hoist the comparison, and with it the wait for the
+// scalar load, to the entry of the loop around the store: there the wait
+// would hold back the next tile's loads by a full memory latency, while at
+// the store it is long over. (Scalar loads share their counter with LDS
+// traffic, so the first LDS wait after the load would take it anyway.)
+__device__ __forceinline__ bool head_matches(const BlobHead& h, int codec, int N, int K) {
+  uint32_t m = h.w[0], v = h.w[1], n = h.w[2], k = h.w[3];
+  asm volatile("" : "+s"(m), "+s"(v), "+s"(n), "+s"(k));
+  return m == W4A16_BLOB_MAGIC && v == head_version_codec(codec) && n == uint32_t(N) && k == uint32_t(K);
 }
 
 // fetch_tile with buffer loads and no per-lane address arithmetic: every

@@ -44,13 +44,19 @@ using w4a16_host::gpl_allowed;
 using w4a16_host::kGplOptions;
 using w4a16_host::kNumGpl;
 
+// Launches of this module whose blob header did not match their call, one
+// word per device (each device holds its own copy; host code reaches it only
+// through the address hipGetSymbolAddress returns for that device).
+__device__ unsigned blob_mismatch_count;
+
 // The 4-bit group-affine GEMV: the shared skeleton with the device header's
 // tile loads and dot products.
 template <int M, int GPL, int MODE>
 __global__ void __launch_bounds__(64 * max_waves_of<CodecQ4>(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
             float* __restrict__ y, int N, int G, int T, int nchunks, int tpb, int nwaves) {
-  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb, nwaves);
+  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb, nwaves,
+                                   &blob_mismatch_count);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,7 +139,6 @@ namespace {
 w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M, int32_t N, int32_t K,
                           void* stream, hipEvent_t start, hipEvent_t stop) {
   using w4a16_host::ranges_overlap;
-  using w4a16_host::tune;
   if (!x || !packed || !y) return W4A16_ERR_NULL;
   if (M < 1 || M > kMaxM || N < 1 || K < kGroup || K % kGroup || K > w4a16_max_k(M)) return W4A16_ERR_SHAPE;
   const size_t packed_bytes = w4a16_packed_bytes(N, K);
@@ -147,11 +152,7 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
     return W4A16_ERR_OVERLAP;
 
   const int G = K / kGroup;
-  LaunchShape shape = w4a16_host::choose_shape<CodecQ4>(M, G);
-  if (const int g = tune("W4A16_TUNE_GPL")) {  // sweep builds only
-    for (int gi = 0; gi < kNumGpl; ++gi)
-      if (kGplOptions[gi] == g && gpl_allowed(M, g)) shape = w4a16_host::shape_for_gpl<CodecQ4>(M, G, gi);
-  }
+  const LaunchShape shape = w4a16_host::choose_shape<CodecQ4>(M, G);
   if (shape.gi < 0) return W4A16_ERR_SHAPE;
   const int mode = w4a16_host::mode_of(shape.waves, shape.nchunks);
   kernel_fn fn = kernel_for_mode(mode, M, shape.gi);
@@ -161,20 +162,15 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   const int T = (N + kTileRows - 1) / kTileRows;
   const bool direct = mode == kDirect;
   // all workgroups resident at once, each walking an equal share of the tiles
-  int occ = w4a16_host::resident_workgroups(M, shape.waves, occupancy(M, shape.gi, mode, shape.waves, fn));
-  if (const int o = tune("W4A16_TUNE_OCC")) occ = o < occ ? o : occ;
+  const int occ = w4a16_host::resident_workgroups(M, shape.waves, occupancy(M, shape.gi, mode, shape.waves, fn));
   int tpb = 0, grid = 0;
   w4a16_host::grid_of(T, M, shape.waves, direct, w4a16_host::cu_count(dev), occ, tpb, grid);
-  if (const int v = tune("W4A16_TUNE_TPB")) {  // sweep builds only
-    tpb = v > kTilesPerBlock ? kTilesPerBlock : v;
-    const int units = (T + tpb - 1) / tpb, max_grid = w4a16_host::cu_count(dev) * occ;
-    grid = units < max_grid ? units : max_grid;
-  }
-
+  // regions after the header: codes, then the scale/min tiles
   const size_t codes_region = (size_t(N) * size_t(K) / 2 + 255) / 256 * 256;
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
   const u32x4* xp = static_cast<const u32x4*>(x);
-  const u32x4* cp = static_cast<const u32x4*>(packed);
-  const u32x4* sp = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(packed) + codes_region);
+  const u32x4* cp = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES);
+  const u32x4* sp = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES + codes_region);
   int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb, w_arg = shape.waves;
   void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg, &w_arg};
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
@@ -184,6 +180,15 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
 }
 
 }  // namespace
+
+namespace w4a16_host {
+
+unsigned* q4_mismatch_word(int dev) {
+  static std::atomic<unsigned*> cache[kMaxDevices];
+  return device_word(reinterpret_cast<const void*>(&blob_mismatch_count), cache, dev);
+}
+
+}  // namespace w4a16_host
 
 extern "C" w4a16_status w4a16_gemv(const void* x, const void* packed, float* y, int32_t M, int32_t N,
                                    int32_t K, void* stream) {

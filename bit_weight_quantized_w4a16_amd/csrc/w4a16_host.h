@@ -5,13 +5,13 @@
 
 #include <atomic>
 #include <cstdint>
-#include <cstdlib>
 
 namespace w4a16_host {
 
+constexpr int kMaxDevices = 64;
+
 // Compute-unit count of a device, cached per device (0 = not yet queried).
 inline int cu_count(int dev) {
-  constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
   if (dev < 0 || dev >= kMaxDevices) return 256;
   int c = cache[dev].load(std::memory_order_relaxed);
@@ -32,14 +32,24 @@ inline int occupancy_of(const void* fn, int block_threads, size_t dynamic_lds = 
 
 inline bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; }
 
-#ifdef W4A16_TUNING
-// Sweep builds only: integer overrides from the environment (0 = unset).
-inline int tune(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
+// Device address of a __device__ word of the calling translation unit
+// (`symbol` is the address of its host-side stand-in, which is not itself a
+// device address) on device `dev`, which must be current:
+// every device holds its own copy. Cached per device in `cache`; nullptr if
+// it cannot be located.
+inline unsigned* device_word(const void* symbol, std::atomic<unsigned*> (&cache)[kMaxDevices], int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  unsigned* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, symbol) != hipSuccess || !a) return nullptr;
+  p = static_cast<unsigned*>(a);
+  cache[dev].store(p, std::memory_order_release);
+  return p;
 }
-#else
-constexpr int tune(const char*) { return 0; }
-#endif
+
+// The single-GEMV module's count of launches whose blob header did not
+// match their call, on device dev (current); nullptr if it cannot be located.
+unsigned* q4_mismatch_word(int dev);
 
 }  // namespace w4a16_host

@@ -554,8 +554,7 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
   const int gq = Hq / Hkv;
-  int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, gq, w4a16_host::cu_count(dev), true), waves_of(bits));
-  if (const int v = w4a16_host::tune("W4A16_TUNE_KV_BPW")) bpw = v < 4 ? 4 : v / 4 * 4;  // sweep builds only
+  const int bpw = blocks_per_wg(nb, Hkv, resident_waves(bits, gq, w4a16_host::cu_count(dev), true), waves_of(bits));
   const int S = (nb + bpw - 1) / bpw;
   const attn_fn fa = bits == 8 ? attn_for<8>(gq) : attn_for<4>(gq);
   const comb_fn fc = comb_for(gq);

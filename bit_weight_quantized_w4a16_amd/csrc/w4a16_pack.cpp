@@ -33,9 +33,25 @@ inline uint32_t split_even_odd(uint32_t v) {
   return e | (o << 16);
 }
 
+constexpr int64_t kHead = W4A16_BLOB_HEADER_BYTES;
+
 int64_t codes_region_bytes(int64_t N, int64_t K) {
   int64_t c = N * K / 2;
   return (c + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+}
+
+// The blob header (layout in include/w4a16.h): the fields the kernels
+// compare, the blob's size, zeros to 256 bytes.
+void write_header(uint8_t* o, int32_t codec, int32_t N, int32_t K, uint64_t total) {
+  std::memset(o, 0, size_t(kHead));
+  const uint32_t magic = W4A16_BLOB_MAGIC;
+  const uint16_t version = W4A16_LAYOUT_VERSION, cid = uint16_t(codec);
+  std::memcpy(o, &magic, 4);
+  std::memcpy(o + 4, &version, 2);
+  std::memcpy(o + 6, &cid, 2);
+  std::memcpy(o + 8, &N, 4);
+  std::memcpy(o + 12, &K, 4);
+  std::memcpy(o + 16, &total, 8);
 }
 
 template <class F>
@@ -65,7 +81,7 @@ extern "C" size_t w4a16_packed_bytes(int32_t N, int32_t K) {
   int64_t G = K / kGroup;
   if (int64_t(N) * G > INT32_MAX) return 0;
   int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
-  return size_t(codes_region_bytes(N, K) + T * G * 16);
+  return size_t(kHead + codes_region_bytes(N, K) + T * G * 16);
 }
 
 extern "C" w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, const uint16_t* min,
@@ -79,7 +95,8 @@ extern "C" w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, 
   const int64_t row_bytes = int64_t(K) / 2;
   const int64_t S = codes_region_bytes(N, K);
   const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
-  uint8_t* o = static_cast<uint8_t*>(out);
+  write_header(static_cast<uint8_t*>(out), W4A16_CODEC_Q4, N, K, need);
+  uint8_t* o = static_cast<uint8_t*>(out) + kHead;
 
   // codes: same byte footprint as the canonical array, words re-ordered in place
   parallel_rows(N, row_bytes, [&](int64_t r0, int64_t r1) {
@@ -129,7 +146,8 @@ bool regions(int codec, int32_t N, int32_t K, Regions& r) {
   if (int64_t(N) * G > INT32_MAX) return false;
   const int64_t T = (int64_t(N) + kTileRows - 1) / kTileRows;
   const int64_t code_bytes = int64_t(N) * G * (codec == W4A16_CODEC_Q8_SYM ? 32 : 16);
-  const int64_t S = (code_bytes + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+  const int64_t S = kHead + (code_bytes + kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+  r.codes_at = size_t(kHead);
   r.codes = size_t(code_bytes);
   r.aux = codec == W4A16_CODEC_Q5 ? size_t(S) : 0;
   r.side = size_t(S + (codec == W4A16_CODEC_Q5 ? T * G * 16 : 0));
@@ -180,13 +198,15 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
     for (int64_t i = 0; i < total; ++i)
       if (codes[i] > 31) return W4A16_ERR_FORMAT;
   }
-  uint8_t* o = static_cast<uint8_t*>(out);
-  std::memset(o + reg.codes, 0, reg.total - reg.codes);  // padding and tiles past N
+  uint8_t* const blob = static_cast<uint8_t*>(out);
+  write_header(blob, codec, N, K, reg.total);
+  std::memset(blob + reg.codes_at + reg.codes, 0, reg.total - reg.codes_at - reg.codes);  // padding, tiles past N
+  uint8_t* o = blob + reg.codes_at;  // the code region
   if (codec == W4A16_CODEC_PAL4) {
     // codes: the canonical bytes, row after row; palettes: per tile, entry c
     // of row r at byte 8c + 2r (binary16, little-endian)
     std::memcpy(o, codes, size_t(N) * size_t(K / 2));
-    uint8_t* lt = o + reg.side;
+    uint8_t* lt = blob + reg.side;
     for (int64_t n = 0; n < N; ++n)
       for (int c = 0; c < 16; ++c) {
         const uint16_t e = scale[n * 16 + c];
@@ -236,7 +256,7 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
 
   // fifth-bit tiles (5-bit code)
   if (codec == W4A16_CODEC_Q5) {
-    uint8_t* hb = o + reg.aux;
+    uint8_t* hb = blob + reg.aux;
     parallel_rows(T, G * 128, [&](int64_t t0, int64_t t1) {
       for (int64_t t = t0; t < t1; ++t)
         for (int64_t g = 0; g < G; ++g) {
@@ -253,7 +273,7 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
   }
 
   // scale (and min) tiles
-  uint8_t* side = o + reg.side;
+  uint8_t* side = blob + reg.side;
   parallel_rows(T, G * 16, [&](int64_t t0, int64_t t1) {
     for (int64_t t = t0; t < t1; ++t)
       for (int64_t g = 0; g < G; ++g) {
@@ -351,8 +371,22 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
   return W4A16_OK;
 }
 
-extern "C" int32_t w4a16_abi_version(void) { return 5; }
+extern "C" w4a16_status w4a16_blob_check(const void* blob, size_t bytes, int32_t codec, int32_t N, int32_t K) {
+  if (!blob) return W4A16_ERR_NULL;
+  w4a16_codecs::Regions reg;
+  if (!w4a16_codecs::regions(codec, N, K, reg)) return W4A16_ERR_SHAPE;
+  if (bytes < size_t(kHead)) return W4A16_ERR_SIZE;
+  uint8_t want[kHead];
+  write_header(want, codec, N, K, reg.total);
+  if (std::memcmp(blob, want, size_t(kHead)) != 0) return W4A16_ERR_FORMAT;
+  return bytes < reg.total ? W4A16_ERR_SIZE : W4A16_OK;
+}
 
+extern "C" int32_t w4a16_abi_version(void) { return W4A16_LAYOUT_VERSION; }
+
+// The statuses are the refusals a runtime owes its caller under the contract
+// table of the core-modules page (section 5.7): an input it does not cover is
+// turned away with a reason, never run.
 extern "C" const char* w4a16_status_string(int32_t status) {
   switch (status) {
     case W4A16_OK: return "ok";
@@ -362,7 +396,7 @@ extern "C" const char* w4a16_status_string(int32_t status) {
     case W4A16_ERR_SIZE: return "output buffer smaller than required";
     case W4A16_ERR_OVERLAP: return "y overlaps x or the packed weights";
     case W4A16_ERR_HIP: return "the HIP runtime reported an error";
-    case W4A16_ERR_FORMAT: return "unknown codec, or a code outside its codec's range";
+    case W4A16_ERR_FORMAT: return "unknown codec, a code outside its codec's range, or a blob header that does not match";
     default: return "unknown status";
   }
 }

@@ -16,6 +16,7 @@
 //   template <int M, int GPL, class XA> static void compute(const Loads<GPL>&, const XA&,
 //                                                           float (&acc)[kTileRows][M]);
 //   static constexpr int kTileVgprs;    // VGPRs of one group slot's loads
+//   static constexpr int kCodec;        // the codec id its blobs' headers carry
 //
 // compute() returns the lane's partial sums; the skeleton adds them over the
 // wave (tile_sums).
@@ -81,6 +82,7 @@ __device__ __forceinline__ float half_of(const u32x2& v, int r) {
 // 4-bit group-affine code (w_hat = s*q + m): the tile loads and dot products
 // of the device header, unchanged.
 struct CodecQ4 {
+  static constexpr int kCodec = W4A16_CODEC_Q4;
   static constexpr int kTileVgprs = 20;
   template <int GPL>
   using Loads = TileLoads<GPL>;
@@ -123,6 +125,7 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, uint32_t fa, uint32_t fb
 // Symmetric 4-bit code (w_hat = s*(q - 8)): the 4-bit code chunks, and one
 // 8-byte entry of four binary16 scales per (tile, group).
 struct CodecQ4Sym {
+  static constexpr int kCodec = W4A16_CODEC_Q4_SYM;
   static constexpr int kTileVgprs = 18;
   template <int GPL>
   struct Loads {
@@ -182,6 +185,7 @@ struct CodecQ4Sym {
 // bits of its first two nibble pairs at 4/20 and 8/24, and shifted right by
 // 4 + d those of the last two.
 struct CodecQ5 {
+  static constexpr int kCodec = W4A16_CODEC_Q5;
   static constexpr int kTileVgprs = 24;
   template <int GPL>
   struct Loads {
@@ -245,6 +249,7 @@ struct CodecQ5 {
 // (k+2, k+3). The offset is removed with the group's activation sum:
 // s * sum u*x - 128 s * sum x.
 struct CodecQ8Sym {
+  static constexpr int kCodec = W4A16_CODEC_Q8_SYM;
   static constexpr int kTileVgprs = 34;
   template <int GPL>
   struct Loads {
@@ -322,6 +327,7 @@ struct CodecQ8Sym {
 // it returns lines up with the activation pair (x_k, x_k+1) of the same word,
 // so it goes straight into v_dot2.
 struct CodecPal4 {
+  static constexpr int kCodec = W4A16_CODEC_PAL4;
   static constexpr int kTileVgprs = 26;
   static constexpr int kLdsBytesPerWave = kTileRows * 256 * 4;
   template <int GPL>
@@ -415,9 +421,19 @@ __host__ __device__ constexpr int max_waves_of(int M, int GPL) {
 // workgroup size (blockDim.x) is a vector load from the dispatch packet, and
 // every wave would wait for it, a full memory latency, before it could issue
 // its activation loads.
+//
+// The packed blob's header sits just before its code region (wp.codes). Its
+// first 16 bytes (one scalar load at the start) are compared where results
+// are stored: a blob whose header does not name this codec, N and K (a stale
+// layout, another matrix, another codec) makes every workgroup skip its y
+// stores, and workgroup 0 counts the launch in *mismatch, a word of the
+// kernel's own module. The weight loads never wait for the check, the header
+// words live in scalar registers (vector registers set the occupancy here),
+// and the kernel arguments are those of a kernel without the check.
 template <class C, int M, int GPL, int MODE>
 __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const WeightPtrs& wp, float* __restrict__ y,
-                                          int N, int G, int T, int nchunks, int tpb, int nwaves) {
+                                          int N, int G, int T, int nchunks, int tpb, int nwaves,
+                                          unsigned* __restrict__ mismatch) {
   const int lane = threadIdx.x & 63;
   // wave-uniform values kept in scalar registers, so every load address is a
   // scalar base plus the one per-lane offset `lane`
@@ -425,6 +441,18 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
   const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
   const int nblocks = (T + tpb - 1) / tpb;
   if (int(blockIdx.x) >= nblocks) return;
+  // Every kernel argument is in registers before the header's scalar load
+  // goes out: scalar loads complete out of order, so the wait for an
+  // argument loaded after it would wait for the header as well.
+  asm volatile("" ::"s"(x), "s"(wp.codes), "s"(wp.aux), "s"(wp.side), "s"(y), "s"(N), "s"(G), "s"(T), "s"(nchunks),
+               "s"(tpb), "s"(nwaves));
+  const BlobHead head = read_head(reinterpret_cast<const uint8_t*>(wp.codes) - W4A16_BLOB_HEADER_BYTES);
+  auto head_ok = [&]() { return head_matches(head, C::kCodec, N, G * kGroup); };
+  // after the last store: one count per launch whose header did not match
+  auto count_mismatch = [&]() {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && !head_ok())
+      __hip_atomic_fetch_add(mismatch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
 
   auto bases = [&](int c, int (&g0)[GPL]) {
 #pragma unroll
@@ -451,7 +479,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
       const int r = (i / M) % kTileRows;
       const int m = i % M;
       const int n = (b * tpb + ti) * kTileRows + r;
-      if (n < N) {
+      if (n < N && head_ok()) {
         float s = 0.f;
         for (int w = 0; w < nwaves; ++w) s += part[ti][r][m][w];
         y[size_t(m) * N + n] = s;
@@ -518,6 +546,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
       }
       reduce_block(b);
     }
+    count_mismatch();
     return;
   } else {
     // Items e = 0 .. n_items-1 of this workgroup: tile tb = e % tpb of its
@@ -544,7 +573,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
         C::template compute<M, GPL>(L, RegX<M, GPL>{xv, xs}, acc);
         tile_sums<M>(acc, v);
         if constexpr (MODE == kDirect) {
-          store_tile<M>(v, y, N, t, lane);
+          if (head_ok()) store_tile<M>(v, y, N, t, lane);
         } else if ((lane & 15) == 0) {  // the first lane of each 16-lane row: output row lane / 16
           const int tb = e % tpb;
           const int r = lane >> 4;
@@ -586,6 +615,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
         finish(la, e);
       }
     }
+    count_mismatch();
   }
 }
 

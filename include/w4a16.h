@@ -26,8 +26,17 @@
  *   y[m][n]     = sum_k w_hat[n][k] * x[m][k]      (x binary16 [M][K], y fp32)
  *
  * Packed layout (what w4a16_pack writes and w4a16_gemv reads):
- *   G  = K / 32 groups per row, T = ceil(N / 4) row tiles.
- *   [0, N*K/2)           codes: row-major [N][G] chunks of 16 bytes; chunk
+ *   G  = K / 32 groups per row, T = ceil(N / 4) row tiles. Every blob of
+ *   every codec starts with the same 256-byte header, then its regions at the
+ *   offsets given below relative to byte H = 256:
+ *   [0, 256)             header, little endian: uint32 magic
+ *                        W4A16_BLOB_MAGIC at byte 0, uint16
+ *                        W4A16_LAYOUT_VERSION at 4, uint16 codec at 6
+ *                        (W4A16_CODEC_*; 0 for w4a16_pack), int32 N at 8,
+ *                        int32 K at 12, uint64 blob bytes at 16, zeros up to
+ *                        byte 256. The kernels compare bytes 0..15 with the
+ *                        call's codec, N and K (see w4a16_gemv).
+ *   H + [0, N*K/2)       codes: row-major [N][G] chunks of 16 bytes; chunk
  *                        (n, g) holds k = 32g .. 32g+31. Inside a chunk, the
  *                        little-endian 32-bit word d (bytes 4d..4d+3) holds
  *                        k = 32g + 8d + i, i = 0..7, with nibble slot p
@@ -35,12 +44,12 @@
  *                        i = 2(p-4)+1 for p >= 4: the four even i in the low
  *                        half-word, the four odd i in the high half-word,
  *                        each in increasing order.
- *   [S, S + T*G*16)      S = N*K/2 rounded up to a multiple of 256. Scale/min
+ *   H + [S, S + T*G*16)  S = N*K/2 rounded up to a multiple of 256. Scale/min
  *                        tiles: [T][G] entries of 16 bytes; entry (t, g) holds
  *                        rows 4t .. 4t+3, row r in bytes 4r..4r+3 as
  *                        (binary16 scale, binary16 min), little endian. Rows
  *                        at or beyond N are zero.
- *   Total size: w4a16_packed_bytes(N, K) = S + T*G*16.
+ *   Total size: w4a16_packed_bytes(N, K) = 256 + S + T*G*16.
  *
  * Status codes are returned, never raised; nothing aborts.
  */
@@ -62,21 +71,54 @@ typedef enum w4a16_status {
   W4A16_ERR_SIZE = 4,     /* an output buffer is smaller than required */
   W4A16_ERR_OVERLAP = 5,  /* y overlaps x or the packed weights */
   W4A16_ERR_HIP = 6,      /* the HIP runtime reported an error */
-  W4A16_ERR_FORMAT = 7    /* unknown codec, or a code outside its codec's range */
+  W4A16_ERR_FORMAT = 7    /* unknown codec, a code outside its codec's range, or a
+                             blob header that does not match the call */
 } w4a16_status;
 
-/* Version of this ABI and of the packed layout; bumped on any change. */
+/* First four bytes of every packed weight blob ("W416" in ASCII). */
+#define W4A16_BLOB_MAGIC 0x36313457u
+/* Version of the packed layouts, stored in every blob header. */
+#define W4A16_LAYOUT_VERSION 6
+/* Bytes of the header that starts every packed weight blob. */
+#define W4A16_BLOB_HEADER_BYTES 256
+
+/* Version of this ABI (equal to W4A16_LAYOUT_VERSION); bumped on any change. */
 int32_t w4a16_abi_version(void);
 
 /* Largest K accepted by w4a16_gemv for a given M (0 if M is outside 1..8). */
 int32_t w4a16_max_k(int32_t M);
 
 /*
- * Bytes of the packed blob for an N x K weight matrix (see "Packed layout").
+ * Bytes of the packed blob for an N x K weight matrix (see "Packed layout"):
+ * the size of the one-off re-layout the packer of the core-modules page
+ * (section 5.1, quantisation) produces, which the memory manager's weight
+ * budget (section 5.4) has to hold, about 0.63 bytes per weight.
  * Returns 0 if N < 1, K < 32, K % 32 != 0, or N * K / 32 does not fit the
  * kernels' 31-bit chunk index.
  */
 size_t w4a16_packed_bytes(int32_t N, int32_t K);
+
+/*
+ * w4a16_blob_check - host only: is `blob` (a host copy of at least its first
+ * 256 bytes; `bytes` = how many bytes the caller holds or will upload) a
+ * packed blob of this layout version for (codec, N, K)? The format refusal
+ * of the core-modules page's contract table (section 5.7: a runtime refuses
+ * a model file it cannot run), for loaders to call before uploading.
+ * Returns W4A16_OK; W4A16_ERR_NULL for a NULL blob; W4A16_ERR_SHAPE for an
+ * unknown codec or bad N/K; W4A16_ERR_FORMAT if the magic, version, codec,
+ * N, K or recorded size differ; W4A16_ERR_SIZE if bytes is below the blob's
+ * size (only the first 256 bytes are read).
+ */
+w4a16_status w4a16_blob_check(const void* blob, size_t bytes, int32_t codec, int32_t N, int32_t K);
+
+/*
+ * w4a16_blob_mismatches - launches on the current device whose packed blob's
+ * header did not match their call (codec, N, K or layout version), counted
+ * since the previous call of this function, which resets the count. Those
+ * launches wrote nothing to y. Synchronises the current device first.
+ * Errors: NULL -> W4A16_ERR_NULL; a HIP failure -> W4A16_ERR_HIP.
+ */
+w4a16_status w4a16_blob_mismatches(uint32_t* count);
 
 /*
  * w4a16_pack - host-side repacker (init time; not on the per-token path).
@@ -87,7 +129,8 @@ size_t w4a16_packed_bytes(int32_t N, int32_t K);
  *   scale  host binary16 bits [N][K/32]                         (read only)
  *   min    host binary16 bits [N][K/32]                         (read only)
  *   out    host buffer of at least w4a16_packed_bytes(N, K) bytes, owned
- *          by the caller; written completely (padding is zeroed).
+ *          by the caller; written completely (header, then regions; padding
+ *          is zeroed).
  * The caller then copies `out` to device memory, 256-byte aligned.
  * Uses worker threads for large inputs; touches no GPU.
  * Errors: NULL pointer -> W4A16_ERR_NULL; bad N/K -> W4A16_ERR_SHAPE;
@@ -119,9 +162,14 @@ w4a16_status w4a16_pack(const uint8_t* codes, const uint16_t* scale, const uint1
  * W4A16_ERR_NULL; M, N or K out of range -> W4A16_ERR_SHAPE; misaligned
  * pointer -> W4A16_ERR_ALIGN; y's byte range intersecting x's or the packed
  * blob's -> W4A16_ERR_OVERLAP; a launch the HIP runtime rejects ->
- * W4A16_ERR_HIP. Faults inside the kernel (e.g. a packed blob shorter than
- * w4a16_packed_bytes) are not detectable here and surface at the caller's
- * next synchronisation.
+ * W4A16_ERR_HIP. The blob header is checked on the device, by one scalar load
+ * issued beside the first weight loads: if its magic, layout version, codec,
+ * N or K differ from this call's, the kernel writes nothing to y and counts
+ * the launch in w4a16_blob_mismatches. The weight loads are not held back by
+ * that check, so a blob shorter than w4a16_packed_bytes(N, K) is still read
+ * out of bounds: such faults are not detectable here and surface at the
+ * caller's next synchronisation (w4a16_blob_check refuses such a blob on the
+ * host before upload).
  */
 w4a16_status w4a16_gemv(const void* x, const void* packed, float* y,
                         int32_t M, int32_t N, int32_t K, void* stream);
@@ -175,12 +223,20 @@ typedef struct w4a16_chain_entry {
 
 /* Bytes of the device workspace of w4a16_gemv_chain. */
 #define W4A16_CHAIN_WORKSPACE_BYTES 69632
-/* Byte offset in that workspace of the uint32 error word: nonzero once an
- * ordering wait of a chain launch gave up (that call's results are invalid;
- * zero-fill the workspace again before the next call). */
+/* Byte offset in that workspace of the uint32 error word, a set of the bits
+ * below, raised by a chain launch and never cleared by one. Any bit set:
+ * results of that call are invalid; zero-fill the workspace again before the
+ * next call. */
 #define W4A16_CHAIN_ERROR_OFFSET 256
+#define W4A16_CHAIN_ERR_WAIT 1u  /* an ordering wait gave up */
+#define W4A16_CHAIN_ERR_PLAN 2u  /* the plan's header does not match (count, M): nothing was written */
+#define W4A16_CHAIN_ERR_BLOB 4u  /* an entry's blob header does not match its (N, K): no y was written */
 
-/* Bytes of the plan for `count` entries (0 if count < 1 or too large). */
+/* Most entries of one chain plan. */
+#define W4A16_CHAIN_MAX_ENTRIES 1048576
+
+/* Bytes of the plan for `count` entries (0 if count < 1 or
+ * count > W4A16_CHAIN_MAX_ENTRIES). */
 size_t w4a16_chain_plan_bytes(int32_t count);
 
 /*
@@ -210,19 +266,24 @@ w4a16_status w4a16_chain_plan(const w4a16_chain_entry* entries, int32_t count, i
  *   workspace  device buffer of workspace_bytes >= W4A16_CHAIN_WORKSPACE_BYTES,
  *              16-byte aligned, zero-filled by the caller once before its first use;
  *              every call leaves its counters at zero again. The uint32 at
- *              byte offset 256 becomes nonzero if an ordering wait ever gave
- *              up (waits bound their spin so a starved launch cannot hang
- *              the GPU); results of such a call are invalid. Calls that
- *              share a workspace must not run concurrently.
+ *              W4A16_CHAIN_ERROR_OFFSET becomes nonzero if an ordering wait
+ *              ever gave up (waits bound their spin so a starved launch
+ *              cannot hang the GPU), the plan or a blob header did not
+ *              match; results of such a call are invalid. Calls that share
+ *              a workspace must not run concurrently.
  * The plan and workspace are owned by the caller. The call only enqueues.
  * The launch keeps all of its workgroups resident (grid sized from the
  * occupancy of the kernel); other work running concurrently on the device
  * can delay it but not deadlock it.
- * Errors (host side): NULL -> W4A16_ERR_NULL; count < 1 or M outside 1..8 ->
+ * Errors (host side): NULL -> W4A16_ERR_NULL; count outside
+ * 1..W4A16_CHAIN_MAX_ENTRIES or M outside 1..8 ->
  * W4A16_ERR_SHAPE; misaligned plan or workspace -> W4A16_ERR_ALIGN;
  * workspace_bytes too small -> W4A16_ERR_SIZE; launch rejected ->
- * W4A16_ERR_HIP. A plan whose header does not match (count, M)
- * is detected on the device: the kernel then writes nothing.
+ * W4A16_ERR_HIP. A plan whose header does not match (count, M) is detected
+ * on the device: the kernel then writes nothing and raises
+ * W4A16_CHAIN_ERR_PLAN. Every entry's blob header is checked against the
+ * entry (as w4a16_gemv checks it) at the start of the launch: if any does
+ * not match, the launch writes no y at all and raises W4A16_CHAIN_ERR_BLOB.
  */
 w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* workspace,
                               size_t workspace_bytes, void* stream);
@@ -453,7 +514,9 @@ w4a16_status w4a16_kv_attention_timed(int32_t bits, const void* q, const void* k
  * shape -> W4A16_ERR_SHAPE. */
 w4a16_status w4a16_kv_launch_shape(int32_t bits, int32_t T, int32_t Hq, int32_t Hkv, int32_t out[3]);
 
-/* Static, human-readable text for a status code (never NULL). */
+/* Static, human-readable text for a status code (never NULL): the reason a
+ * call was refused, as the contract table of the core-modules page (section
+ * 5.7) asks of a runtime that turns away an input it does not cover. */
 const char* w4a16_status_string(int32_t status);
 
 #ifdef __cplusplus

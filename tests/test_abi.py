@@ -36,8 +36,22 @@ def test_every_declared_symbol_is_exported(w4a16_lib):
     assert declared <= exported
 
 
+def test_python_constants_match_header():
+    """Every numeric #define and enum value of include/w4a16.h that the binding
+    mirrors has the same value there."""
+    text = open(os.path.join(ROOT, "include", "w4a16.h")).read()
+    defines = {m.group(1): int(m.group(2), 0) for m in re.finditer(r"#define (W4A16_\w+) (0x[0-9A-Fa-f]+|\d+)u?\b", text)}
+    enums = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(W4A16_\w+) = (\d+)", text)}
+    mirrored = {k: getattr(w4, k) for k in list(defines) + list(enums) if hasattr(w4, k)}
+    assert len(mirrored) >= 15
+    for k, v in mirrored.items():
+        assert v == defines.get(k, enums.get(k)), k
+    for name, cid in w4.CODEC_IDS.items():
+        assert enums["W4A16_CODEC_" + name.upper()] == cid
+
+
 def test_version_and_strings(w4a16_lib):
-    assert w4.w4a16_abi_version() == 5
+    assert w4.w4a16_abi_version() == 6
     for st in range(8):
         assert w4.w4a16_status_string(st) != "unknown status"
     assert w4.w4a16_status_string(99) == "unknown status"
@@ -51,8 +65,8 @@ def test_packed_bytes_rules(w4a16_lib):
     assert w4.w4a16_packed_bytes(4, 48) == 0
     assert w4.w4a16_packed_bytes(-1, 64) == 0
     assert w4.w4a16_packed_bytes(2**31 - 1, 2**16) == 0          # chunk index would overflow
-    assert w4.w4a16_packed_bytes(4096, 4096) == 4096 * 2048 + 1024 * 128 * 16
-    assert w4.w4a16_packed_bytes(3, 32) == 256 + 16
+    assert w4.w4a16_packed_bytes(4096, 4096) == 256 + 4096 * 2048 + 1024 * 128 * 16
+    assert w4.w4a16_packed_bytes(3, 32) == 256 + 256 + 16
 
 
 def test_pack_errors(w4a16_lib):
@@ -171,7 +185,8 @@ def _plan_fields(plan, count):
         raw = plan[64 + 64 * i: 128 + 64 * i]
         ptrs = raw[:32].view("<u8")
         ints = raw[32:56].view("<i4")
-        ents.append((*[int(p) for p in ptrs], *[int(v) for v in ints]))
+        blob = raw[56:64].view("<u8")
+        ents.append((*[int(p) for p in ptrs], *[int(v) for v in ints], int(blob[0])))
     return hdr, ents
 
 
@@ -187,20 +202,21 @@ def test_chain_plan_layout(w4a16_lib):
     assert plan.size == w4.w4a16_chain_plan_bytes(4) == 64 + 4 * 64
     hdr, ents = _plan_fields(plan, 4)
     shape = w4.chain_launch_shape(1)
-    assert (hdr[0], hdr[1], hdr[2], hdr[3]) == (0x48433457, 4, 4, 1)
+    assert (hdr[0], hdr[1], hdr[2], hdr[3]) == (0x48433457, 5, 4, 1)
     assert (hdr[4], hdr[5]) == (shape["ring"], shape["compute_waves"]) == (24, 8)
     for (x, p, y, N, K), e in zip(entries, ents):
-        ex, ecodes, esm, ey, eN, eG, eT, S, passes, xcoh = e
-        assert (ex, ecodes, ey, eN, eG, eT) == (x, p, y, N, K // 32, (N + 3) // 4)
-        assert esm == p + (N * K // 2 + 255) // 256 * 256
+        ex, ecodes, esm, ey, eN, eG, eT, S, passes, xcoh, pad = e
+        assert (ex, ecodes, ey, eN, eG, eT) == (x, p + 256, y, N, K // 32, (N + 3) // 4)
+        assert esm == p + 256 + (N * K // 2 + 255) // 256 * 256
         assert S * 64 >= K // 32 > (S - 1) * 64               # segments of 64 groups, one per lane
+    assert all(e[10] == 0 for e in ents)                   # padding
     # M = 1: 8 segments of activations per LDS pass; only the last x is written by an earlier entry
-    assert [e[7:] for e in ents] == [(2, 1, 0), (7, 1, 0), (14, 2, 0), (1, 1, 1)]
+    assert [e[7:10] for e in ents] == [(2, 1, 0), (7, 1, 0), (14, 2, 0), (1, 1, 1)]
     plan8 = w4.w4a16_chain_plan(entries[:2], 8)
     hdr8, e8 = _plan_fields(plan8, 2)
     assert (hdr8[3], hdr8[4]) == (8, w4.chain_launch_shape(8)["ring"])
     # M = 8: one segment of 8 activation rows per pass
-    assert [e[7:] for e in e8] == [(2, 2, 0), (7, 7, 0)]
+    assert [e[7:10] for e in e8] == [(2, 2, 0), (7, 7, 0)]
 
 
 def test_chain_plan_errors(w4a16_lib):
@@ -229,6 +245,7 @@ def test_chain_plan_errors(w4a16_lib):
     # a later entry reading an earlier entry's y is the allowed dependency
     assert plan([good, (B + 2**30, B + 2**25, B + 2**31, 64, 64)]) == w4.W4A16_OK
     assert L.w4a16_chain_plan_bytes(0) == 0 and L.w4a16_chain_plan_bytes(-3) == 0
+    assert L.w4a16_chain_plan_bytes(2**20) == 64 + 2**20 * 64 and L.w4a16_chain_plan_bytes(2**20 + 1) == 0
 
 
 def test_chain_call_rejects_before_any_hip_call(w4a16_lib):

@@ -7,7 +7,8 @@
 * agreement with separate w4a16_gemv launches (bitwise where the launch
   shapes coincide);
 * the workspace is left zeroed and error-free after every call;
-* a plan whose header does not match the call writes nothing;
+* a plan whose header does not match the call writes nothing and raises the
+  plan bit of the error word;
 * the chain captured in a HIP graph and replayed, with eager work and
   synchronisation between replays, matches the eager result every time.
 """
@@ -50,7 +51,7 @@ class Chain:
 
 def assert_workspace_clean(ch):
     ws = ch.workspace.cpu().numpy()
-    assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == 0, "an ordering wait gave up"
+    assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == 0, "the error word is raised"
     assert not ws.any(), f"counters or flags not reset: {np.flatnonzero(ws)[:8]}"
 
 
@@ -157,6 +158,14 @@ def test_chain_header_mismatch_writes_nothing(w4a16_lib):
     ch.run(M=2)                                             # plan says M = 1
     torch.cuda.synchronize()
     assert (ch.items[0]["y"].cpu().numpy() == -7.0).all()
+    ws = ch.workspace.cpu().numpy()
+    assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == w4.W4A16_CHAIN_ERR_PLAN
+    ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] = 0
+    assert not ws.any()                                     # no counter was touched
+    ch.workspace.zero_()
+    ch.run(M=1)                                             # the matching call still works
+    torch.cuda.synchronize()
+    assert np.isfinite(ch.items[0]["y"].cpu().numpy()).all() and (ch.items[0]["y"].cpu().numpy() != -7.0).any()
     assert_workspace_clean(ch)
 
 

@@ -15,6 +15,7 @@ import pytest
 
 import bit_weight_quantized_w4a16_amd as w4
 import workload
+from blob_header import HEADER_BYTES, strip_header
 
 
 def _round_up(v, a):
@@ -37,6 +38,7 @@ def _tiles(blob, off, T, G, entry):
 
 
 def decode_blob(codec, blob, N, K):
+    blob = strip_header(blob, w4.CODEC_IDS[codec], N, K)
     G, T = K // 32, (N + 3) // 4
     code_bytes = N * G * (32 if codec == "q8_sym" else 16)
     S = _round_up(code_bytes, 256)
@@ -107,16 +109,17 @@ def test_q5_fifth_bits_by_hand(w4a16_lib):
     codes = np.zeros((1, 32), np.uint8)
     codes[0, 5] = 16
     blob = w4.w4a16_codec_pack("q5", codes, np.ones((1, 1), np.float16), np.zeros((1, 1), np.float16))
-    word = int(blob[256:260].view("<u4")[0])
+    body = blob[HEADER_BYTES:]
+    word = int(body[256:260].view("<u4")[0])
     assert word == 1 << 24          # k = 5 = 8*0 + 2*(6 mod 4) + 6//4  ->  b = 4*6 + 0
-    assert not blob[:16].any()      # the low nibbles are all zero
+    assert not body[:16].any()      # the low nibbles are all zero
 
 
 def test_q8_bytes_by_hand(w4a16_lib):
     """k = 0..3 of the low half: bytes hold k = 0, 2, 1, 3 as q + 128."""
     codes = np.zeros((1, 32), np.int8)
     codes[0, :4] = [-128, 1, 2, 127]
-    blob = w4.w4a16_codec_pack("q8_sym", codes, np.ones((1, 1), np.float16))
+    blob = w4.w4a16_codec_pack("q8_sym", codes, np.ones((1, 1), np.float16))[HEADER_BYTES:]
     assert list(blob[:4]) == [0, 130, 129, 255]
     assert list(blob[4:32]) == [128] * 28   # the rest of both halves: q = 0
 
@@ -158,7 +161,7 @@ def test_codec_pack_errors(w4a16_lib):
                                           ("pal4", 16 / 32 + 32 / 4096)])
 def test_codec_bytes_per_weight(w4a16_lib, codec, expect):
     N, K = 4096, 4096
-    assert w4.w4a16_codec_packed_bytes(codec, N, K) == N * K * expect
+    assert w4.w4a16_codec_packed_bytes(codec, N, K) == HEADER_BYTES + N * K * expect
 
 
 def test_codec_gemv_rejects_before_any_hip_call(w4a16_lib):
