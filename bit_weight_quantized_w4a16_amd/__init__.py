@@ -55,6 +55,7 @@ EXPORTS = (
     "w4a16_kv_launch_shape",
     "w4a16_blob_check",
     "w4a16_blob_mismatches",
+    "w4a16_kv_attention_static",
 )
 
 W4A16_CHAIN_WORKSPACE_BYTES = 69632
@@ -67,6 +68,7 @@ W4A16_CHAIN_ERR_BLOB = 4        # an entry's blob header does not match its (N, 
 W4A16_BLOB_MAGIC = 0x36313457   # first four bytes of every packed weight blob
 W4A16_LAYOUT_VERSION = 6
 W4A16_BLOB_HEADER_BYTES = 256
+W4A16_KV_STATIC_WORKSPACE_BYTES = 8 << 20
 
 
 class ChainEntry(ctypes.Structure):
@@ -142,6 +144,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_status_string.argtypes = [c_i32]
     L.w4a16_blob_check.restype = c_i32
     L.w4a16_blob_check.argtypes = [c_vp, c_sz, c_i32, c_i32, c_i32]
+    L.w4a16_kv_attention_static.restype = c_i32
+    L.w4a16_kv_attention_static.argtypes = [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp]
     L.w4a16_blob_mismatches.restype = c_i32
     L.w4a16_blob_mismatches.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     _lib = L
@@ -518,6 +522,12 @@ def w4a16_kv_attention_timed_raw(bits: int, q_ptr: int, kv_ptr: int, o_ptr: int,
                                  ws_ptr: int, ws_bytes: int, stream: int, start_event: int, stop_event: int) -> int:
     return int(lib().w4a16_kv_attention_timed(int(bits), q_ptr, kv_ptr, o_ptr, int(T), int(Hq), int(Hkv), ws_ptr,
                                               int(ws_bytes), stream, start_event, stop_event))
+
+
+def w4a16_kv_attention_static_raw(bits: int, q_ptr: int, kv_ptr: int, o_ptr: int, T: int, Hq: int, Hkv: int,
+                                  stream: int = 0) -> int:
+    """w4a16_kv_attention_static with raw device pointers; returns the status code."""
+    return int(lib().w4a16_kv_attention_static(int(bits), q_ptr, kv_ptr, o_ptr, int(T), int(Hq), int(Hkv), stream))
 
 
 def w4a16_kv_attention(bits: int, q, kv, o, T: int, Hkv: int, workspace, stream=None) -> None:

@@ -606,6 +606,42 @@ extern "C" w4a16_status w4a16_kv_attention_timed(int32_t bits, const void* q, co
                     static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }
 
+namespace {
+
+// The partials of w4a16_kv_attention_static: a file-scope array that every
+// device holds its own copy of, for as long as the process lives. Its name
+// in host code is a host-side stand-in, never a device address: host code
+// uses only the per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[W4A16_KV_STATIC_WORKSPACE_BYTES / sizeof(float)];
+
+// Device address of `scratch` on device `dev`, looked up on the first call
+// on that device (which must be current) and kept; nullptr on failure.
+float* scratch_on(int dev) {
+  static std::atomic<float*> cache[w4a16_host::kMaxDevices];
+  if (dev < 0 || dev >= w4a16_host::kMaxDevices) return nullptr;
+  float* ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  cache[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" w4a16_status w4a16_kv_attention_static(int32_t bits, const void* q, const void* kv, float* o, int32_t T,
+                                                  int32_t Hq, int32_t Hkv, void* stream) {
+  if (!q || !kv || !o) return W4A16_ERR_NULL;
+  if (!shape_ok(bits, T, Hq, Hkv)) return W4A16_ERR_SHAPE;
+  if (w4a16_kv_workspace_bytes(T, Hq) > W4A16_KV_STATIC_WORKSPACE_BYTES) return W4A16_ERR_SIZE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  float* ptr = scratch_on(dev);
+  if (!ptr) return W4A16_ERR_HIP;
+  // every partial the merge reads is written by the split pass of the same
+  // call, so nothing has to be cleared first
+  return kv_enqueue(bits, q, kv, o, T, Hq, Hkv, ptr, W4A16_KV_STATIC_WORKSPACE_BYTES, stream, nullptr, nullptr);
+}
+
 extern "C" w4a16_status w4a16_kv_launch_shape(int32_t bits, int32_t T, int32_t Hq, int32_t Hkv, int32_t out[3]) {
   if (!out) return W4A16_ERR_NULL;
   if (!shape_ok(bits, T, Hq, Hkv)) return W4A16_ERR_SHAPE;

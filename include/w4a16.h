@@ -508,6 +508,30 @@ w4a16_status w4a16_kv_attention_timed(int32_t bits, const void* q, const void* k
                                       int32_t Hkv, void* workspace, size_t workspace_bytes, void* stream,
                                       void* start_event, void* stop_event);
 
+/* Bytes of the library's own partials array used by w4a16_kv_attention_static
+ * (one per device, held until the process ends): room for
+ * w4a16_kv_workspace_bytes(T, Hq) up to this size (8 MiB), e.g. T <= 129,024
+ * tokens at Hq = 32 and T <= 64,512 at Hq = 64. */
+#define W4A16_KV_STATIC_WORKSPACE_BYTES 8388608u
+
+/*
+ * w4a16_kv_attention_static - w4a16_kv_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation). The partials go to an array the library holds in each
+ * device's memory (W4A16_KV_STATIC_WORKSPACE_BYTES), whose device address is
+ * looked up on the first call on a device. The call itself allocates
+ * nothing. All calls on one device share that array and it keeps the last
+ * call's partials: calls that can overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller (one stream, say).
+ * Arguments, results (bitwise those of w4a16_kv_attention), ownership and
+ * errors are those of w4a16_kv_attention, plus: w4a16_kv_workspace_bytes(T,
+ * Hq) above W4A16_KV_STATIC_WORKSPACE_BYTES -> W4A16_ERR_SIZE (nothing
+ * enqueued); the array's address not found -> W4A16_ERR_HIP.
+ */
+w4a16_status w4a16_kv_attention_static(int32_t bits, const void* q, const void* kv, float* o, int32_t T, int32_t Hq,
+                                       int32_t Hkv, void* stream);
+
 /* Host only: out[0] = query heads per KV head (the kernel's template argument,
  * kv_attn_kernel<bits, out[0]>), out[1] = blocks per workgroup, out[2] =
  * workgroups per KV head on the current device. NULL -> W4A16_ERR_NULL; bad
