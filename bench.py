@@ -99,21 +99,23 @@ def gemv_bytes(M, N, K, codec="q4"):
 # a 1 GiB device copy; kept only while the kernel is unchanged since the
 # counters were taken.
 TRAFFIC = {
-    # (16,749.95 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_357_142,
-    # (2,137,225.4 KiB x 2.000 + 6,528.1 KiB x 1.000) per dispatch
-    ("llama8b_step", 1, "chain_kernel<1, 2, 4>"): 4_383_722_283,
-    # the 70B step: (65,466.21 KiB x 2.000 + 82.0 KiB x 1.000) per dispatch
-    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_148_314,
-    # weight-code variants: (15,083.47 / 20,096.30 / 28,412.23 KiB x 2.000 + 52.0 / 52.0 / 61.34 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_944_187,
-    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_210_474,
-    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_232_208,
-    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_903_370,
-    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_620_582,
-    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_570_565,
-    # palettised codes: (13,613.0 KiB x 2.000 + 52.0 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_932_673,
+    # (16,749.51 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_355_345,
+    # (2,137,104.19 KiB x 2.000 + 11,904.06 KiB x 1.000) per dispatch
+    ("llama8b_step", 1, "chain_kernel<1, 24, 8>"): 4_388_863_484,
+    # the 70B step: (65,464.86 KiB x 2.000 + 84.0 KiB x 1.000) per dispatch
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_154_508,
+    # weight-code variants: (15,088.73 / 20,100.57 / 28,413.19 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_954_150,
+    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_218_134,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_241_924,
+    # verify batches: (16,948.65 / 17,198.84 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
+    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_914_716,
+    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_631_895,
+    # the 70B step at M = 8: (63,844.62 KiB x 2.000 + 810.67 KiB x 1.000)
+    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_580_445,
+    # palettised codes: (13,617.75 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_941_656,
     # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
     ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_135_991,
     ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_667_525,
@@ -170,7 +172,9 @@ def build_inputs(torch, w4, M, dev, threads, codec="q4", wl=WORKLOAD, sets=1):
 
     out = []
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        for (layer, pi, p, m), x, blob in ex.map(make, items):
+        for i, ((layer, pi, p, m), x, blob) in enumerate(ex.map(make, items)):
+            if len(items) > 64 and (i + 1) % 64 == 0:
+                log(f"[bench] {i + 1} of {len(items)} GEMVs packed and uploaded")
             packed = w4.upload_packed(blob, dev)
             xd = torch.from_numpy(x).to(dev)
             y = torch.zeros((m, p.N), dtype=torch.float32, device=dev)
