@@ -508,6 +508,10 @@ def main():
             f"{forms['separate'] * 1e6:.1f} us/step")
     if args.only in (None, "chain"):
         forms["chain"] = time_loop(torch, stream, chain_step, args.warmup, args.steps)
+        # the error word is sticky: zero after the timed calls means every one was valid
+        st, bits = w4.w4a16_chain_status_raw(ws_p, ws_bytes, sh, False)
+        if st != w4.W4A16_OK:
+            raise w4.W4A16Error(st, f"timed chain calls (error word {bits:#x})")
         log(f"[bench] chain: {forms['chain'] * 1e6:.1f} us/step")
     form = min(forms, key=forms.get)
     sec = forms[form]

@@ -23,6 +23,7 @@ W4A16_ERR_SIZE = 4
 W4A16_ERR_OVERLAP = 5
 W4A16_ERR_HIP = 6
 W4A16_ERR_FORMAT = 7
+W4A16_ERR_WAIT = 8
 
 # weight-code variants (enum w4a16_codec)
 CODEC_IDS = {"q4": 0, "q4_sym": 1, "q5": 2, "q8_sym": 3, "pal4": 4}
@@ -56,6 +57,7 @@ EXPORTS = (
     "w4a16_blob_check",
     "w4a16_blob_mismatches",
     "w4a16_kv_attention_static",
+    "w4a16_chain_status",
 )
 
 W4A16_CHAIN_WORKSPACE_BYTES = 69632
@@ -118,6 +120,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemv_chain_timed.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp, c_vp]
     L.w4a16_gemv_chain.restype = c_i32
     L.w4a16_gemv_chain.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz, c_vp]
+    L.w4a16_chain_status.restype = c_i32
+    L.w4a16_chain_status.argtypes = [c_vp, c_sz, c_vp, ctypes.POINTER(ctypes.c_uint32), c_i32]
     L.w4a16_codec_packed_bytes.restype = c_sz
     L.w4a16_codec_packed_bytes.argtypes = [c_i32, c_i32, c_i32]
     L.w4a16_codec_pack.restype = c_i32
@@ -346,21 +350,51 @@ def w4a16_gemv_chain_timed_raw(plan_ptr: int, count: int, M: int, workspace_ptr:
                                             stream, start_event, stop_event))
 
 
-def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None) -> None:
-    """Enqueue a planned decode-step chain (plan and workspace are device tensors)."""
-    _device_tensors("w4a16_gemv_chain", plan=plan, workspace=workspace)
+def _stream_handle(stream) -> int:
     if stream is None:
         import torch
 
-        s = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        s = stream.cuda_stream
-    else:
-        s = int(stream)
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def w4a16_gemv_chain(plan, count: int, M: int, workspace, stream=None, check: bool = False) -> None:
+    """Enqueue a planned decode-step chain (plan and workspace are device tensors).
+
+    check=True waits for the call and raises W4A16Error (W4A16_ERR_WAIT or
+    W4A16_ERR_FORMAT) if it raised a bit of the workspace's error word; the
+    word is then cleared with the rest of the workspace."""
+    _device_tensors("w4a16_gemv_chain", plan=plan, workspace=workspace)
+    s = _stream_handle(stream)
     st = w4a16_gemv_chain_raw(_ptr(plan), count, M, _ptr(workspace),
                               workspace.numel() * workspace.element_size(), s)
     if st != W4A16_OK:
         raise W4A16Error(st, "w4a16_gemv_chain")
+    if check:
+        st, bits = w4a16_chain_status_raw(_ptr(workspace), workspace.numel() * workspace.element_size(), s, True)
+        if st != W4A16_OK:
+            raise W4A16Error(st, f"w4a16_gemv_chain (error word {bits:#x})")
+
+
+def w4a16_chain_status_raw(workspace_ptr: int, workspace_bytes: int, stream: int, clear: bool) -> tuple:
+    """w4a16_chain_status with raw pointers; returns (status code, error bits)."""
+    bits = ctypes.c_uint32(0)
+    st = int(lib().w4a16_chain_status(workspace_ptr, int(workspace_bytes), stream, ctypes.byref(bits), int(bool(clear))))
+    return st, int(bits.value)
+
+
+def w4a16_chain_status(workspace, stream=None, clear: bool = False) -> int:
+    """Wait for the chain calls enqueued on `stream` and return the error bits
+    of their workspace (0: every result valid); clear=True zero-fills the
+    workspace again when a bit was set. Raises W4A16Error on host errors."""
+    _device_tensors("w4a16_chain_status", workspace=workspace)
+    st, bits = w4a16_chain_status_raw(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream_handle(stream), clear)
+    if st not in (W4A16_OK, W4A16_ERR_WAIT, W4A16_ERR_FORMAT):
+        raise W4A16Error(st, "w4a16_chain_status")
+    return bits
 
 
 # ---------------------------------------------------------------------------

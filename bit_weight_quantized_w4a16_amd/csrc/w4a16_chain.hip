@@ -796,3 +796,25 @@ extern "C" w4a16_status w4a16_gemv_chain_timed(const void* plan, int32_t count, 
   return chain_enqueue(plan, count, M, workspace, workspace_bytes, stream, static_cast<hipEvent_t>(start_event),
                        static_cast<hipEvent_t>(stop_event));
 }
+
+extern "C" w4a16_status w4a16_chain_status(const void* workspace, size_t workspace_bytes, void* stream,
+                                           uint32_t* bits, int32_t clear) {
+  if (!workspace || !bits) return W4A16_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return W4A16_ERR_ALIGN;
+  if (workspace_bytes < W4A16_CHAIN_WORKSPACE_BYTES) return W4A16_ERR_SIZE;
+  *bits = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return W4A16_ERR_HIP;
+  uint32_t word = 0;
+  const uint8_t* at = static_cast<const uint8_t*>(workspace) + W4A16_CHAIN_ERROR_OFFSET;
+  if (hipMemcpy(&word, at, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return W4A16_ERR_HIP;
+  if (word && clear) {
+    // the stream is drained, so no chain call of this workspace is running
+    if (hipMemsetAsync(const_cast<void*>(workspace), 0, W4A16_CHAIN_WORKSPACE_BYTES, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return W4A16_ERR_HIP;
+  }
+  *bits = word;
+  if (!word) return W4A16_OK;
+  return (word & W4A16_CHAIN_ERR_WAIT) ? W4A16_ERR_WAIT : W4A16_ERR_FORMAT;
+}

@@ -581,12 +581,6 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
 
 }  // namespace
 
-extern "C" size_t w4a16_kv_packed_bytes(int32_t bits, int32_t T, int32_t Hkv) {
-  if ((bits != 8 && bits != 4) || T < 1 || T > kMaxT || Hkv < 1 || Hkv > 4096) return 0;
-  const int64_t nb = (int64_t(T) + kBlockTokens - 1) / kBlockTokens;
-  return size_t(int64_t(Hkv) * nb * record_bytes(bits));
-}
-
 extern "C" size_t w4a16_kv_workspace_bytes(int32_t T, int32_t Hq) {
   if (T < 1 || T > kMaxT || Hq < 1 || Hq > 4096) return 0;
   return size_t(max_partials(T, Hq)) * kPartFloats * sizeof(float);

@@ -299,6 +299,20 @@ extern "C" w4a16_status w4a16_codec_pack(int32_t codec, const uint8_t* codes, co
 // Quantised KV cache (format in include/w4a16.h)
 // ---------------------------------------------------------------------------
 
+// One record holds 64 tokens of one KV head: 17408 bytes at INT8, 10240 at
+// INT4. The attention kernels' record structs carry the same sizes; the size
+// tests and the KV parity tests fail if the two ever differ.
+namespace {
+constexpr int64_t kKvTok = 64;
+constexpr int64_t kv_record_bytes(int32_t bits) { return bits == 8 ? 17408 : 10240; }
+}  // namespace
+
+extern "C" size_t w4a16_kv_packed_bytes(int32_t bits, int32_t T, int32_t Hkv) {
+  if ((bits != 8 && bits != 4) || T < 1 || T > (1 << 24) || Hkv < 1 || Hkv > 4096) return 0;
+  const int64_t nb = (int64_t(T) + kKvTok - 1) / kKvTok;
+  return size_t(int64_t(Hkv) * nb * kv_record_bytes(bits));
+}
+
 extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, const uint16_t* k_scale,
                                       const uint16_t* k_min, const uint8_t* v_codes, const uint16_t* v_scale,
                                       const uint16_t* v_min, int32_t T, int32_t Hkv, void* out, size_t out_bytes) {
@@ -308,9 +322,9 @@ extern "C" w4a16_status w4a16_kv_pack(int32_t bits, const uint8_t* k_codes, cons
   const size_t need = w4a16_kv_packed_bytes(bits, T, Hkv);
   if (need == 0) return W4A16_ERR_SHAPE;
   if (out_bytes < need) return W4A16_ERR_SIZE;
-  constexpr int64_t kD = 128, kTok = 64;
+  constexpr int64_t kD = 128, kTok = kKvTok;
   const int64_t nb = (int64_t(T) + kTok - 1) / kTok;
-  const int64_t R = bits == 8 ? 17408 : 10240;
+  const int64_t R = kv_record_bytes(bits);
   const int64_t cb = bits == 8 ? kD : kD / 2;  // canonical code bytes per (token, head)
   uint8_t* o = static_cast<uint8_t*>(out);
   parallel_rows(int64_t(Hkv) * nb, R, [&](int64_t r0, int64_t r1) {
@@ -397,6 +411,7 @@ extern "C" const char* w4a16_status_string(int32_t status) {
     case W4A16_ERR_OVERLAP: return "y overlaps x or the packed weights";
     case W4A16_ERR_HIP: return "the HIP runtime reported an error";
     case W4A16_ERR_FORMAT: return "unknown codec, a code outside its codec's range, or a blob header that does not match";
+    case W4A16_ERR_WAIT: return "a chain launch's ordering wait gave up; its results are invalid";
     default: return "unknown status";
   }
 }

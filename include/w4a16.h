@@ -71,8 +71,9 @@ typedef enum w4a16_status {
   W4A16_ERR_SIZE = 4,     /* an output buffer is smaller than required */
   W4A16_ERR_OVERLAP = 5,  /* y overlaps x or the packed weights */
   W4A16_ERR_HIP = 6,      /* the HIP runtime reported an error */
-  W4A16_ERR_FORMAT = 7    /* unknown codec, a code outside its codec's range, or a
+  W4A16_ERR_FORMAT = 7,   /* unknown codec, a code outside its codec's range, or a
                              blob header that does not match the call */
+  W4A16_ERR_WAIT = 8      /* a chain launch's ordering wait gave up: its results are invalid */
 } w4a16_status;
 
 /* First four bytes of every packed weight blob ("W416" in ASCII). */
@@ -295,6 +296,26 @@ w4a16_status w4a16_gemv_chain(const void* plan, int32_t count, int32_t M, void* 
  */
 w4a16_status w4a16_gemv_chain_timed(const void* plan, int32_t count, int32_t M, void* workspace,
                                     size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
+/*
+ * w4a16_chain_status - host, blocking: the outcome of the chain calls enqueued
+ * so far on `stream` with this workspace. Waits until the stream has drained,
+ * reads the error word at W4A16_CHAIN_ERROR_OFFSET into *bits and, if `clear`
+ * is nonzero and a bit was set, zero-fills the first
+ * W4A16_CHAIN_WORKSPACE_BYTES of the workspace again (on `stream`, waited
+ * for) so it can serve the next call.
+ *   workspace, workspace_bytes, stream   as given to w4a16_gemv_chain
+ * Returns W4A16_OK if the word is zero; W4A16_ERR_WAIT if
+ * W4A16_CHAIN_ERR_WAIT is set; else W4A16_ERR_FORMAT (plan or blob header
+ * mismatch). Host errors: NULL workspace or bits -> W4A16_ERR_NULL (bits
+ * untouched); misaligned workspace -> W4A16_ERR_ALIGN; workspace_bytes too
+ * small -> W4A16_ERR_SIZE; a failing wait or copy -> W4A16_ERR_HIP (*bits = 0).
+ * Synchronises, so it is not for use under stream capture; the bits are
+ * sticky across calls until cleared, so check after the last call of a
+ * batch, or after every call when each result matters.
+ */
+w4a16_status w4a16_chain_status(const void* workspace, size_t workspace_bytes, void* stream, uint32_t* bits,
+                                int32_t clear);
 
 /*
  * w4a16_chain_launch_shape - host only: the three template arguments of the

@@ -52,7 +52,7 @@ def test_python_constants_match_header():
 
 def test_version_and_strings(w4a16_lib):
     assert w4.w4a16_abi_version() == 6
-    for st in range(8):
+    for st in range(9):
         assert w4.w4a16_status_string(st) != "unknown status"
     assert w4.w4a16_status_string(99) == "unknown status"
     assert w4.w4a16_max_k(0) == 0 and w4.w4a16_max_k(9) == 0
@@ -262,6 +262,21 @@ def test_chain_call_rejects_before_any_hip_call(w4a16_lib):
     assert L.w4a16_gemv_chain(B, 1, 1, B + 4096, 256, None) == w4.W4A16_ERR_SIZE
 
 
+def test_chain_status_rejects_before_any_hip_call(w4a16_lib):
+    import ctypes
+
+    L = w4a16_lib
+    B = 0x7F0000000000
+    W = w4.W4A16_CHAIN_WORKSPACE_BYTES
+    bits = ctypes.c_uint32(77)
+    assert L.w4a16_chain_status(None, W, None, ctypes.byref(bits), 0) == w4.W4A16_ERR_NULL
+    assert L.w4a16_chain_status(B, W, None, None, 0) == w4.W4A16_ERR_NULL
+    assert bits.value == 77                                  # untouched on NULL
+    assert L.w4a16_chain_status(B + 4, W, None, ctypes.byref(bits), 1) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_chain_status(B, W - 1, None, ctypes.byref(bits), 1) == w4.W4A16_ERR_SIZE
+    assert L.w4a16_chain_status(B, 256, None, ctypes.byref(bits), 0) == w4.W4A16_ERR_SIZE
+
+
 # ------------------------------------------------------ binding argument checks
 def test_binding_refuses_host_and_strided_tensors_before_any_gpu_call(w4a16_lib):
     """The library takes bare device addresses: the binding refuses host
@@ -280,6 +295,8 @@ def test_binding_refuses_host_and_strided_tensors_before_any_gpu_call(w4a16_lib)
         w4.w4a16_codec_gemv("q8_sym", x, packed, y)
     with pytest.raises(ValueError, match="not on a GPU"):
         w4.w4a16_gemv_chain(packed, 1, 1, torch.zeros(16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w4.w4a16_chain_status(torch.zeros(16, dtype=torch.int32))
     q = torch.zeros((4, 128), dtype=torch.float16)
     o = torch.zeros((4, 128), dtype=torch.float32)
     with pytest.raises(ValueError, match="not on a GPU"):

@@ -111,17 +111,18 @@ def test_chain_with_a_mismatched_blob_writes_nothing(w4a16_lib, bad_at):
         ws = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4, dtype=torch.int32, device=DEV)
         w4.w4a16_gemv_chain(plan, len(entries), M, ws)
         torch.cuda.synchronize()
-        return ws.cpu().numpy()
+        return ws.cpu().numpy(), w4.w4a16_chain_status_raw(ws.data_ptr(), ws.numel() * 4, 0, False)
 
     print(f"[blob] chain of 3, entry {bad_at} mismatched", flush=True)
-    w = run(order)
+    w, status = run(order)
     for it in order:
         assert (it["y"].cpu().numpy() == FILL).all()
     assert w[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == w4.W4A16_CHAIN_ERR_BLOB
+    assert status == (w4.W4A16_ERR_FORMAT, w4.W4A16_CHAIN_ERR_BLOB)
     w[w4.W4A16_CHAIN_ERROR_OFFSET // 4] = 0
     assert not w.any()
-    w = run(items)
-    assert not w.any()
+    w, status = run(items)
+    assert not w.any() and status == (w4.W4A16_OK, 0)
     for it, (x, codes, scale, mn) in zip(items, (p0, p2)):
         y_ref, B = oracle.gemv(x, codes, scale, mn)
         check(it["y"].cpu().numpy().astype(np.float64), y_ref, B, f"chain entry N={it['N']}",

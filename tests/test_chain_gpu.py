@@ -8,7 +8,8 @@
   shapes coincide);
 * the workspace is left zeroed and error-free after every call;
 * a plan whose header does not match the call writes nothing and raises the
-  plan bit of the error word;
+  plan bit of the error word, which w4a16_chain_status reports (and clears);
+* w4a16_chain_status maps each error bit to its status;
 * the chain captured in a HIP graph and replayed, with eager work and
   synchronisation between replays, matches the eager result every time.
 """
@@ -45,8 +46,9 @@ class Chain:
         self.plan_dev = torch.from_numpy(host).to(DEV)
         return self.plan_dev
 
-    def run(self, stream=None, M=None):
-        w4.w4a16_gemv_chain(self.plan_dev, len(self.items), self.M if M is None else M, self.workspace, stream)
+    def run(self, stream=None, M=None, check=False):
+        w4.w4a16_gemv_chain(self.plan_dev, len(self.items), self.M if M is None else M, self.workspace, stream,
+                            check=check)
 
 
 def assert_workspace_clean(ch):
@@ -162,11 +164,46 @@ def test_chain_header_mismatch_writes_nothing(w4a16_lib):
     assert ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] == w4.W4A16_CHAIN_ERR_PLAN
     ws[w4.W4A16_CHAIN_ERROR_OFFSET // 4] = 0
     assert not ws.any()                                     # no counter was touched
-    ch.workspace.zero_()
-    ch.run(M=1)                                             # the matching call still works
-    torch.cuda.synchronize()
+    ws_bytes = ch.workspace.numel() * 4
+    st, bits = w4.w4a16_chain_status_raw(ch.workspace.data_ptr(), ws_bytes, 0, False)
+    assert (st, bits) == (w4.W4A16_ERR_FORMAT, w4.W4A16_CHAIN_ERR_PLAN)
+    assert w4.w4a16_chain_status(ch.workspace) == w4.W4A16_CHAIN_ERR_PLAN   # sticky until cleared
+    assert w4.w4a16_chain_status(ch.workspace, clear=True) == w4.W4A16_CHAIN_ERR_PLAN
+    assert not ch.workspace.cpu().numpy().any()
+    with pytest.raises(w4.W4A16Error) as e:
+        ch.run(M=2, check=True)
+    assert e.value.status == w4.W4A16_ERR_FORMAT
+    assert not ch.workspace.cpu().numpy().any()             # check=True cleared it
+    ch.run(M=1, check=True)                                 # the matching call still works
     assert np.isfinite(ch.items[0]["y"].cpu().numpy()).all() and (ch.items[0]["y"].cpu().numpy() != -7.0).any()
     assert_workspace_clean(ch)
+    assert w4.w4a16_chain_status_raw(ch.workspace.data_ptr(), ws_bytes, 0, True) == (w4.W4A16_OK, 0)
+
+
+def test_chain_status_maps_each_bit(w4a16_lib):
+    """The error word is the only input of w4a16_chain_status: set from the
+    host, each combination of bits maps to its status (the wait bit wins), and
+    clearing zero-fills the whole workspace. No chain kernel is launched."""
+    ws = torch.zeros(w4.W4A16_CHAIN_WORKSPACE_BYTES // 4 + 8, dtype=torch.int32, device=DEV)
+    at = w4.W4A16_CHAIN_ERROR_OFFSET // 4
+    cases = [(0, w4.W4A16_OK), (w4.W4A16_CHAIN_ERR_WAIT, w4.W4A16_ERR_WAIT),
+             (w4.W4A16_CHAIN_ERR_PLAN, w4.W4A16_ERR_FORMAT), (w4.W4A16_CHAIN_ERR_BLOB, w4.W4A16_ERR_FORMAT),
+             (w4.W4A16_CHAIN_ERR_WAIT | w4.W4A16_CHAIN_ERR_BLOB, w4.W4A16_ERR_WAIT)]
+    s = torch.cuda.Stream()
+    for word, status in cases:
+        ws.fill_(0)
+        ws[at] = word
+        ws[1] = 5                                           # a stale counter beside the word
+        ws[-1] = 9                                          # past the workspace: never touched
+        torch.cuda.synchronize()
+        st, bits = w4.w4a16_chain_status_raw(ws.data_ptr(), ws.numel() * 4, s.cuda_stream, True)
+        assert (st, bits) == (status, word), word
+        h = ws.cpu().numpy()
+        assert h[-1] == 9
+        if word:
+            assert not h[:-8].any(), word                   # cleared: counters too
+        else:
+            assert h[1] == 5                                # nothing set: nothing cleared
 
 
 def test_chain_graph_replays_match_eager(w4a16_lib):
