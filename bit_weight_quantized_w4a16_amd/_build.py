@@ -32,6 +32,10 @@ HIP_FLAGS = [
     "-fPIC",
     # no packed-fp32 VALU forms anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 dwords of explicit kernel arguments arrive in scalar
+    # registers when a wave starts, instead of by scalar loads from the
+    # argument segment (a memory round trip before the first weight load)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

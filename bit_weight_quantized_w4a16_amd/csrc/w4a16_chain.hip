@@ -285,7 +285,7 @@ __device__ __forceinline__ bool ring_steps(Step& step) {
 
 template <int M, int RING, int NCW>
 __global__ void __launch_bounds__(64 * (chain_loader_waves(M) + NCW))
-chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int count) {
+chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int count, int nwg) {
   static_assert(RING == kRing && NCW == chain_compute_waves(M), "one ring; the compute waves of M");
   constexpr int XS = chain_pass_segs(M);
   constexpr int XG = XS * kSeg;  // groups of one LDS pass
@@ -293,7 +293,8 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   constexpr int NL = chain_loader_waves(M);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwg = gridDim.x;
+  // nwg (the launch's workgroup count) is an argument: every explicit
+  // argument arrives preloaded in scalar registers, gridDim.x would be a load
   const int wg = blockIdx.x;
   if (hdr->magic != kChainMagic || hdr->version != kChainVersion || hdr->count != count || hdr->M != M ||
       hdr->ring != RING || hdr->compute_waves != NCW) {
@@ -305,8 +306,9 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   const unsigned inv = __builtin_amdgcn_readfirstlane(nwg > 1 ? 0xFFFFFFFFu / unsigned(nwg) + 1u : 0u);
 
   __shared__ ChainLds L;
-  for (int i = threadIdx.x; i < kRing; i += blockDim.x) L.ready[i] = L.consumed[i] = 0;
-  for (int i = threadIdx.x; i < kMaxBlockTiles; i += blockDim.x) L.tile_cnt[i] = 0;
+  constexpr int kThreads = 64 * (chain_loader_waves(M) + NCW);
+  for (int i = threadIdx.x; i < kRing; i += kThreads) L.ready[i] = L.consumed[i] = 0;
+  for (int i = threadIdx.x; i < kMaxBlockTiles; i += kThreads) L.tile_cnt[i] = 0;
   if (threadIdx.x == 0) L.done = L.go = L.staged = L.abort = L.bad_blob = 0;
   __syncthreads();  // the only workgroup barrier: nothing is in flight yet
 
@@ -648,7 +650,7 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   }
 }
 
-typedef void (*chain_fn)(const ChainHeader*, unsigned*, int);
+typedef void (*chain_fn)(const ChainHeader*, unsigned*, int, int);
 
 template <int M>
 constexpr chain_fn chain_instance() {
@@ -773,8 +775,8 @@ w4a16_status chain_enqueue(const void* plan, int32_t count, int32_t M, void* wor
   const int grid = w4a16_host::cu_count(dev) * occ;
   const ChainHeader* hp = static_cast<const ChainHeader*>(plan);
   unsigned* wp = static_cast<unsigned*>(workspace);
-  int n_arg = count;
-  void* args[] = {&hp, &wp, &n_arg};
+  int n_arg = count, g_arg = grid;
+  void* args[] = {&hp, &wp, &n_arg, &g_arg};
   const int block = 64 * (chain_loader_waves(M) + chain_compute_waves(M));
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), args, 0,
                          static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)

@@ -51,9 +51,9 @@ __device__ unsigned blob_mismatch_count;
 template <int CODEC, int M, int GPL, int MODE>
 __global__ void __launch_bounds__(64 * max_waves_of<Codec>(M, GPL))
 codec_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ aux,
-             const void* __restrict__ side, float* __restrict__ y, int N, int G, int T, int nchunks, int tpb,
+             const void* __restrict__ side, float* __restrict__ y, int N, int G, int T, int nchunks, int tpb_grid,
              int nwaves) {
-  gemv_body<Codec, M, GPL, MODE>(x, WeightPtrs{codes, aux, side}, y, N, G, T, nchunks, tpb, nwaves,
+  gemv_body<Codec, M, GPL, MODE>(x, WeightPtrs{codes, aux, side}, y, N, G, T, nchunks, tpb_grid, nwaves,
                                  &blob_mismatch_count);
 }
 
@@ -145,7 +145,9 @@ w4a16_status enqueue(const w4a16_codecs::Launch& l, const w4a16_codecs::Regions&
   const u32x4* ap = reg.aux ? reinterpret_cast<const u32x4*>(base + reg.aux) : nullptr;
   const void* sp = base + reg.side;
   float* y = l.y;
-  int n_arg = l.N, g_arg = G, t_arg = T, c_arg = s.nchunks, b_arg = tpb, w_arg = s.waves;
+  int n_arg = l.N, g_arg = G, t_arg = T, c_arg = s.nchunks, b_arg = w4a16_host::tpb_grid_arg(tpb, grid),
+      w_arg = s.waves;
+  if (b_arg == 0) return W4A16_ERR_HIP;
   void* args[] = {&xp, &cp, &ap, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg, &w_arg};
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * s.waves), args,
                          dynamic_lds(s.waves), l.stream, l.start, l.stop, 0) != hipSuccess)

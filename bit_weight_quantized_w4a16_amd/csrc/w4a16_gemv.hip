@@ -54,8 +54,8 @@ __device__ unsigned blob_mismatch_count;
 template <int M, int GPL, int MODE>
 __global__ void __launch_bounds__(64 * max_waves_of<CodecQ4>(M, GPL))
 gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ codes, const u32x4* __restrict__ sm,
-            float* __restrict__ y, int N, int G, int T, int nchunks, int tpb, int nwaves) {
-  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb, nwaves,
+            float* __restrict__ y, int N, int G, int T, int nchunks, int tpb_grid, int nwaves) {
+  gemv_body<CodecQ4, M, GPL, MODE>(x, WeightPtrs{codes, nullptr, sm}, y, N, G, T, nchunks, tpb_grid, nwaves,
                                    &blob_mismatch_count);
 }
 
@@ -171,7 +171,9 @@ w4a16_status gemv_enqueue(const void* x, const void* packed, float* y, int32_t M
   const u32x4* xp = static_cast<const u32x4*>(x);
   const u32x4* cp = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES);
   const u32x4* sp = reinterpret_cast<const u32x4*>(base + W4A16_BLOB_HEADER_BYTES + codes_region);
-  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = tpb, w_arg = shape.waves;
+  int n_arg = N, g_arg = G, t_arg = T, c_arg = shape.nchunks, b_arg = w4a16_host::tpb_grid_arg(tpb, grid),
+      w_arg = shape.waves;
+  if (b_arg == 0) return W4A16_ERR_HIP;
   void* args[] = {&xp, &cp, &sp, &y, &n_arg, &g_arg, &t_arg, &c_arg, &b_arg, &w_arg};
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(64 * shape.waves), args, 0,
                          static_cast<hipStream_t>(stream), start, stop, 0) != hipSuccess)

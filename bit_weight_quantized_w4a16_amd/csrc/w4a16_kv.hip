@@ -112,7 +112,7 @@ __device__ __forceinline__ f4 mfma4(h4 a, h4 b, f4 c) { return __builtin_amdgcn_
 template <int BITS, int GQ>
 __global__ void __launch_bounds__(64 * waves_of(BITS))
 kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__ kv, float* __restrict__ part, int T,
-               int nb, int bpw, float scale_log2) {
+               int nb, int bpw, float scale_log2, int S) {
   using R = Rec<BITS>;
   constexpr int kWaves = waves_of(BITS);
   constexpr int HG = (GQ + 3) / 4;       // groups of four query heads: the rows of one MFMA
@@ -121,7 +121,8 @@ kv_attn_kernel(const uint32_t* __restrict__ q_pairs, const uint8_t* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.y;           // KV head
   const int split = blockIdx.x;
-  const int S = gridDim.x;
+  // S (splits per KV head, the grid's x extent) is an argument: explicit
+  // arguments arrive preloaded in scalar registers, gridDim.x would be a load
   const int b0 = split * bpw;
   const int b1 = min(b0 + bpw, nb);
 
@@ -467,7 +468,7 @@ __global__ void __launch_bounds__(kMergeThreads) kv_combine_kernel(const float* 
   if (k == 0) o[size_t(h) * kD + d] = ((accs[0][d] + accs[1][d]) + (accs[2][d] + accs[3][d])) / den;
 }
 
-typedef void (*attn_fn)(const uint32_t*, const uint8_t*, float*, int, int, int, float);
+typedef void (*attn_fn)(const uint32_t*, const uint8_t*, float*, int, int, int, float, int);
 typedef void (*comb_fn)(const float*, float*, int);
 
 template <int BITS>
@@ -565,7 +566,7 @@ w4a16_status kv_enqueue(int32_t bits, const void* q, const void* kv, float* o, i
   float* pp = static_cast<float*>(workspace);
   int t_arg = T, nb_arg = nb, bpw_arg = bpw, s_arg = S;
   float sc_arg = scale_log2;
-  void* a1[] = {&qp, &kp, &pp, &t_arg, &nb_arg, &bpw_arg, &sc_arg};
+  void* a1[] = {&qp, &kp, &pp, &t_arg, &nb_arg, &bpw_arg, &sc_arg, &s_arg};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // the events (if any) bracket the split attention pass, the dominant kernel
   if (hipExtLaunchKernel(reinterpret_cast<const void*>(fa), dim3(S, Hkv), dim3(64 * waves_of(bits)), a1, 0, st,

@@ -420,7 +420,12 @@ __host__ __device__ constexpr int max_waves_of(int M, int GPL) {
 // nwaves is the workgroup's wave count, passed by the host: the device-side
 // workgroup size (blockDim.x) is a vector load from the dispatch packet, and
 // every wave would wait for it, a full memory latency, before it could issue
-// its activation loads.
+// its activation loads. For the same reason the launch's workgroup count
+// comes in the high 16 bits of tpb_grid (tiles per workgroup in the low 16):
+// gridDim.x is a load from the kernel argument segment's implicit part,
+// while every explicit argument arrives preloaded in scalar registers (the
+// library is built with kernel-argument preloading; at most 64 bytes of
+// explicit arguments preload, and these kernels use 56 or 64).
 //
 // The packed blob's header sits just before its code region (wp.codes). Its
 // first 16 bytes (one scalar load at the start) are compared where results
@@ -432,20 +437,21 @@ __host__ __device__ constexpr int max_waves_of(int M, int GPL) {
 // and the kernel arguments are those of a kernel without the check.
 template <class C, int M, int GPL, int MODE>
 __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const WeightPtrs& wp, float* __restrict__ y,
-                                          int N, int G, int T, int nchunks, int tpb, int nwaves,
+                                          int N, int G, int T, int nchunks, int tpb_grid, int nwaves,
                                           unsigned* __restrict__ mismatch) {
   const int lane = threadIdx.x & 63;
   // wave-uniform values kept in scalar registers, so every load address is a
   // scalar base plus the one per-lane offset `lane`
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk_groups = nwaves * 64 * GPL;  // groups covered by one pass over K
+  const int tpb = tpb_grid & 0xFFFF, grid = tpb_grid >> 16;
   const int nblocks = (T + tpb - 1) / tpb;
   if (int(blockIdx.x) >= nblocks) return;
   // Every kernel argument is in registers before the header's scalar load
   // goes out: scalar loads complete out of order, so the wait for an
   // argument loaded after it would wait for the header as well.
   asm volatile("" ::"s"(x), "s"(wp.codes), "s"(wp.aux), "s"(wp.side), "s"(y), "s"(N), "s"(G), "s"(T), "s"(nchunks),
-               "s"(tpb), "s"(nwaves));
+               "s"(tpb_grid), "s"(nwaves));
   const BlobHead head = read_head(reinterpret_cast<const uint8_t*>(wp.codes) - W4A16_BLOB_HEADER_BYTES);
   auto head_ok = [&]() { return head_matches(head, C::kCodec, N, G * kGroup); };
   // after the last store: one count per launch whose header did not match
@@ -498,7 +504,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
     // computed, as in the single-pass loop below; the 128-register budget of
     // wider workgroups has no room for the second buffer.
     constexpr bool kPrefetch = GPL == 1 && max_waves_of<C>(M, GPL) <= 8;
-    for (int b = blockIdx.x; b < nblocks; b += gridDim.x) {
+    for (int b = blockIdx.x; b < nblocks; b += grid) {
       const int ntiles = min(tpb, T - b * tpb);
       for (int c = 0; c < nchunks; ++c) {
         int g0[GPL];
@@ -557,11 +563,11 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
     // flight); tiles past T (in the matrix's last block only) fetch a clamped
     // tile and are skipped. A scheduling barrier after each fetch keeps the
     // next tile's loads ahead of the current tile's compute.
-    const int my_blocks = (nblocks - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+    const int my_blocks = (nblocks - int(blockIdx.x) + grid - 1) / grid;
     const int n_items = my_blocks * tpb;
     int g0[GPL];
     bases(0, g0);
-    auto tile_of = [&](int e) { return (int(blockIdx.x) + (e / tpb) * int(gridDim.x)) * tpb + e % tpb; };
+    auto tile_of = [&](int e) { return (int(blockIdx.x) + (e / tpb) * grid) * tpb + e % tpb; };
     auto fetch = [&](int e, Loads& L) {
       const int t = tile_of(e);
       C::template fetch<GPL>(wp, N, G, t < T ? t : T - 1, g0, lane, L);
@@ -582,7 +588,7 @@ __device__ __forceinline__ void gemv_body(const u32x4* __restrict__ x, const Wei
         }
       }
       if constexpr (MODE == kBlock) {
-        if (e % tpb == tpb - 1) reduce_block(int(blockIdx.x) + (e / tpb) * int(gridDim.x));
+        if (e % tpb == tpb - 1) reduce_block(int(blockIdx.x) + (e / tpb) * grid);
       }
     };
 
@@ -743,6 +749,13 @@ inline void grid_of(int T, int M, int waves, bool direct, int cus, int occ, int&
   }
   const int blocks = cdiv(T, tpb);
   grid = blocks < max_grid ? blocks : max_grid;
+}
+
+// The kernels' tpb_grid argument: tiles per workgroup in the low 16 bits, the
+// launch's workgroup count in the high 16 (0 if either does not fit; the
+// caller then refuses the launch).
+inline int tpb_grid_arg(int tpb, int grid) {
+  return tpb >= 1 && tpb < (1 << 16) && grid >= 1 && grid < (1 << 15) ? tpb | (grid << 16) : 0;
 }
 
 }  // namespace w4a16_host
