@@ -99,26 +99,26 @@ def gemv_bytes(M, N, K, codec="q4"):
 # a 1 GiB device copy; kept only while the kernel is unchanged since the
 # counters were taken.
 TRAFFIC = {
-    # (16,749.51 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_355_345,
-    # (2,137,104.19 KiB x 2.000 + 11,904.06 KiB x 1.000) per dispatch
-    ("llama8b_step", 1, "chain_kernel<1, 24, 8>"): 4_388_863_484,
-    # the 70B step: (65,464.86 KiB x 2.000 + 84.0 KiB x 1.000) per dispatch
-    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_154_508,
-    # weight-code variants: (15,088.73 / 20,100.57 / 28,413.19 KiB x 2.000 + 52.0 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_954_150,
-    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_218_134,
-    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_241_924,
-    # verify batches: (16,948.65 / 17,198.84 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
-    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_914_716,
-    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_631_895,
-    # the 70B step at M = 8: (63,844.62 KiB x 2.000 + 810.67 KiB x 1.000)
-    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_580_445,
-    # palettised codes: (13,617.75 KiB x 2.000 + 52.0 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_941_656,
-    # KV-cache attention, split pass: (41,441.09 / 48,739.69 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
-    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_135_991,
-    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_667_525,
+    # (16,752.39 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_361_216,
+    # (2,137,331.94 KiB x 2.000 + 11,904.06 KiB x 1.000) per dispatch
+    ("llama8b_step", 1, "chain_kernel<1, 24, 8>"): 4_389_327_294,
+    # the 70B step: (65,464.47 KiB x 2.000 + 84.0 KiB x 1.000) per dispatch
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_153_625,
+    # weight-code variants: (15,086.10 / 20,092.59 / 28,408.95 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_948_753,
+    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_201_770,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_233_211,
+    # verify batches: (16,941.37 / 17,198.15 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
+    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_899_792,
+    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_630_460,
+    # the 70B step at M = 8: (63,845.30 KiB x 2.000 + 810.67 KiB x 1.000)
+    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_775,
+    # palettised codes: (13,616.53 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_939_140,
+    # KV-cache attention, split pass: (41,447.22 / 48,741.68 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
+    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_146_262,
+    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_668_894,
 }
 
 

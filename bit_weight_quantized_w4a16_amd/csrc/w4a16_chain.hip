@@ -296,8 +296,12 @@ chain_kernel(const ChainHeader* __restrict__ hdr, unsigned* __restrict__ ws, int
   // nwg (the launch's workgroup count) is an argument: every explicit
   // argument arrives preloaded in scalar registers, gridDim.x would be a load
   const int wg = blockIdx.x;
-  if (hdr->magic != kChainMagic || hdr->version != kChainVersion || hdr->count != count || hdr->M != M ||
-      hdr->ring != RING || hdr->compute_waves != NCW) {
+  // the header's six words in one go (a chain of || would load and wait for
+  // them one at a time)
+  const uint32_t h_magic = hdr->magic, h_version = hdr->version;
+  const int32_t h_count = hdr->count, h_m = hdr->M, h_ring = hdr->ring, h_cw = hdr->compute_waves;
+  if ((h_magic != kChainMagic) | (h_version != kChainVersion) | (h_count != count) | (h_m != M) | (h_ring != RING) |
+      (h_cw != NCW)) {
     // every workgroup sees the same header, so all leave together
     if (wg == 0 && threadIdx.x == 0) or_coherent(ws + kErrorWord, W4A16_CHAIN_ERR_PLAN);
     return;
