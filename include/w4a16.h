@@ -320,8 +320,8 @@ w4a16_status w4a16_chain_status(const void* workspace, size_t workspace_bytes, v
 /*
  * w4a16_chain_launch_shape - host only: the three template arguments of the
  * kernel w4a16_gemv_chain launches for M, as profilers print its name
- * chain_kernel<out[0], out[1], out[2]>: activation rows, groups of 32 weights
- * per lane, units of work whose weight loads each compute wave keeps in flight.
+ * chain_kernel<out[0], out[1], out[2]>: activation rows, slots of the
+ * workgroup's LDS ring of weight units, compute waves per workgroup.
  * Errors: NULL out -> W4A16_ERR_NULL; M outside 1..8 -> W4A16_ERR_SHAPE.
  */
 w4a16_status w4a16_chain_launch_shape(int32_t M, int32_t out[3]);
