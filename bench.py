@@ -143,6 +143,33 @@ def copy_calibration(torch, dev):
     log("[bench] copy calibration: 3 copies of 1 GiB done")
 
 
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def system_info(torch, w4, dev):
+    """What the line was measured on: device, runtime and library versions, host CPU."""
+    props = torch.cuda.get_device_properties(dev)
+    return {
+        "device": props.name,
+        "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "hip": torch.version.hip,
+        "torch": torch.__version__,
+        "library_abi": w4.w4a16_abi_version(),
+        "host_cpu": host_cpu_model(),
+        "host_threads": len(os.sched_getaffinity(0)),
+    }
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -234,6 +261,7 @@ def cpu_baseline(budget_s=12.0, codec="q4", wl=WORKLOAD, M=1):
         "value": round(done_bytes / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "host_cpu": host_cpu_model(),
         "kind": "oracle",
         "sample": f"fp64 oracle on the first {len(done)} of the step's {len(step)} GEMVs (layer order, "
                   f"{done[0]} .. {done[-1]}), "
@@ -279,6 +307,7 @@ def kv_cpu_baseline(bits, T, budget_s):
         "value": round(nbytes / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "host_cpu": host_cpu_model(),
         "kind": "oracle",
         "sample": f"fp64 attention oracle (numpy) on the first {done} of the step's {workload.KV_LAYERS} layers "
                   f"(T = {T}), {nbytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s wall, one thread",
@@ -377,6 +406,7 @@ def main_kv(args, torch, w4, dev):
             "launch": f"{L} w4a16_kv_attention calls per step ({kernel} + {shape['merge_kernel']}), "
                       f"replayed from a HIP graph",
         },
+        "system": system_info(torch, w4, dev),
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
@@ -602,6 +632,7 @@ def main():
                                       if sets > 1 else "")}[form],
             "us_per_step_by_launch_form": {k: round(v * 1e6, 2) for k, v in forms.items()},
         },
+        "system": system_info(torch, w4, dev),
         "roofline": {
             "bound": "alu" if alu_bound else "hbm",
             "kernel": kernel,
