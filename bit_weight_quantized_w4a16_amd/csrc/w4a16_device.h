@@ -37,6 +37,16 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
+// a.b + 0 in one VOP3P instruction with the inline constant 0 as its
+// accumulator. Written with fdot2(a, b, 0), the compiler picks the
+// two-address v_dot2c form and zeroes its destination with a v_mov first: one
+// extra VALU operation per partial sum started, 2M per (row, group).
+__device__ __forceinline__ float dot2_from_zero(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float,
@@ -318,8 +328,13 @@ __device__ __forceinline__ void compute_tile(const TileLoads<GPL>& L, const XA& 
           const uint32_t pd = w8 & 0x00F000F0u;  // k = 8d+6, 8d+7  -> q * 2^-20
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            lo[r][m] = dot2(pa, elem(xq[m], 0), lo[r][m]);
-            hi[r][m] = dot2(pb, elem(xq[m], 1), hi[r][m]);
+            if (d == 0) {  // each (row, group) chain starts from 0
+              lo[r][m] = dot2_from_zero(pa, elem(xq[m], 0));
+              hi[r][m] = dot2_from_zero(pb, elem(xq[m], 1));
+            } else {
+              lo[r][m] = dot2(pa, elem(xq[m], 0), lo[r][m]);
+              hi[r][m] = dot2(pb, elem(xq[m], 1), hi[r][m]);
+            }
             lo[r][m] = dot2(pc, elem(xq[m], 2), lo[r][m]);
             hi[r][m] = dot2(pd, elem(xq[m], 3), hi[r][m]);
           }

@@ -101,10 +101,11 @@ struct CodecQ4 {
 // x (as in compute_tile): lo gathers q * 2^-24 terms, hi gathers q * 2^-20.
 // `five` adds a fifth code bit below each nibble's plane (0 for 4-bit codes):
 // bits 4/20 of fa and 8/24 of fa for the first two pairs, of fb for the last
-// two, already shifted into place by the caller.
+// two, already shifted into place by the caller. `first`: the chunk starts
+// lo and hi (from 0) instead of adding to them.
 template <int M, bool FIVE>
 __device__ __forceinline__ void nibble_dots(uint32_t w, uint32_t fa, uint32_t fb, const u32x4 (&xq)[M],
-                                            float (&lo)[M], float (&hi)[M]) {
+                                            float (&lo)[M], float (&hi)[M], bool first) {
   const uint32_t w8 = w >> 8;
   uint32_t pa = w & 0x000F000Fu, pb = w & 0x00F000F0u, pc = w8 & 0x000F000Fu, pd = w8 & 0x00F000F0u;
   if constexpr (FIVE) {
@@ -115,8 +116,13 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, uint32_t fa, uint32_t fb
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    lo[m] = dot2(pa, elem(xq[m], 0), lo[m]);
-    hi[m] = dot2(pb, elem(xq[m], 1), hi[m]);
+    if (first) {
+      lo[m] = dot2_from_zero(pa, elem(xq[m], 0));
+      hi[m] = dot2_from_zero(pb, elem(xq[m], 1));
+    } else {
+      lo[m] = dot2(pa, elem(xq[m], 0), lo[m]);
+      hi[m] = dot2(pb, elem(xq[m], 1), hi[m]);
+    }
     lo[m] = dot2(pc, elem(xq[m], 2), lo[m]);
     hi[m] = dot2(pd, elem(xq[m], 3), hi[m]);
   }
@@ -161,7 +167,7 @@ struct CodecQ4Sym {
       tile_walk<M>(
           xa, j,
           [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
-            nibble_dots<M, false>(elem(L.code[r][j], d), 0u, 0u, xq, lo[r], hi[r]);
+            nibble_dots<M, false>(elem(L.code[r][j], d), 0u, 0u, xq, lo[r], hi[r], d == 0);
           },
           [&](int r) __attribute__((always_inline)) {
             const float s = half_of(L.sc[j], r);
@@ -224,7 +230,7 @@ struct CodecQ5 {
           xa, j,
           [&](int r, int d, const u32x4(&xq)[M]) __attribute__((always_inline)) {
             const uint32_t h = elem(L.hb[j], r);
-            nibble_dots<M, true>(elem(L.code[r][j], d), h << (4 - d), h >> (4 + d), xq, lo[r], hi[r]);
+            nibble_dots<M, true>(elem(L.code[r][j], d), h << (4 - d), h >> (4 + d), xq, lo[r], hi[r], d == 0);
           },
           [&](int r) __attribute__((always_inline)) {
             const f16x2 hm = __builtin_bit_cast(f16x2, elem(L.sm[j], r));
@@ -295,8 +301,13 @@ struct CodecQ8Sym {
               const uint32_t p0 = w & 0x00FF00FFu, p1 = (w >> 8) & 0x00FF00FFu;
 #pragma unroll
               for (int m = 0; m < M; ++m) {
-                lo[r][m] = dot2(p0, elem(xq[m], 2 * i), lo[r][m]);
-                hi[r][m] = dot2(p1, elem(xq[m], 2 * i + 1), hi[r][m]);
+                if (d == 0 && i == 0) {  // each (row, group) chain starts from 0
+                  lo[r][m] = dot2_from_zero(p0, elem(xq[m], 0));
+                  hi[r][m] = dot2_from_zero(p1, elem(xq[m], 1));
+                } else {
+                  lo[r][m] = dot2(p0, elem(xq[m], 2 * i), lo[r][m]);
+                  hi[r][m] = dot2(p1, elem(xq[m], 2 * i + 1), hi[r][m]);
+                }
               }
             }
           },
@@ -396,7 +407,9 @@ struct CodecPal4 {
           for (int i = 0; i < 4; ++i) {
             const uint32_t pair = tab[r * 256 + ((w >> (8 * i)) & 0xFFu)];  // (w_k, w_k+1), k = 8d + 2i
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = dot2(pair, elem(xa.x(m, j, d), i), acc[r][m]);
+            for (int m = 0; m < M; ++m)
+              acc[r][m] = (j == 0 && d == 0 && i == 0) ? dot2_from_zero(pair, elem(xa.x(m, j, d), i))
+                                                       : dot2(pair, elem(xa.x(m, j, d), i), acc[r][m]);
           }
         }
       }
