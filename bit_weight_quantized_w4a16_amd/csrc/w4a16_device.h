@@ -81,18 +81,31 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Maximum over the 64 lanes of a wave, by the same exchanges as wave_sum;
-// every lane ends with the same value.
+// every lane ends with the same value. The exchanges compare order keys: the
+// bits of a float, with the magnitude bits flipped when the sign is set,
+// order as signed integers the way the floats do (NaN aside), and an integer
+// max needs no NaN quieting, so each DPP exchange and its max issue as one
+// v_max_i32 with a DPP operand (fmaxf costs a move, a canonicalising max and
+// the max per exchange).
+__device__ __forceinline__ int order_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_order_key(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  const unsigned b = __builtin_bit_cast(unsigned, v);
-  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  v = fmaxf(__builtin_bit_cast(float, unsigned(p[0])), __builtin_bit_cast(float, unsigned(p[1])));
-  const unsigned c = __builtin_bit_cast(unsigned, v);
-  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return fmaxf(__builtin_bit_cast(float, unsigned(q[0])), __builtin_bit_cast(float, unsigned(q[1])));
+  int k = order_key(v);
+  k = max(k, dpp_i<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = max(k, dpp_i<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = max(k, dpp_i<0x141>(k));  // row_half_mirror
+  k = max(k, dpp_i<0x140>(k));  // row_mirror
+  const auto p = __builtin_amdgcn_permlane16_swap(unsigned(k), unsigned(k), false, false);
+  k = max(int(p[0]), int(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(unsigned(k), unsigned(k), false, false);
+  return from_order_key(max(int(q[0]), int(q[1])));
 }
 
 // Loads of one 4-row tile for this lane: GPL scale/min entries, 4*GPL chunks.
