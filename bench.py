@@ -511,9 +511,15 @@ def main():
         separate = [g["y"].clone() for g in gemvs]
         for g in gemvs:
             g["y"].fill_(float("nan"))
+        # the plan and workspace uploads, the clones and the NaN fills ran on
+        # the current stream; the chain runs on `stream`
+        torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             chain_step()
         stream.synchronize()
+        st, bits = w4.w4a16_chain_status_raw(ws_p, ws_bytes, sh, False)
+        if st != w4.W4A16_OK:
+            raise w4.W4A16Error(st, f"first chain call (error word {bits:#x})")
         spot_check(w4, gemvs, torch)
         worst = max(float(((g["y"] - r).abs() / (r.abs() + 1e-3)).max()) for g, r in zip(gemvs, separate))
         if workspace.cpu().numpy().any():

@@ -212,6 +212,7 @@ def test_chain_graph_replays_match_eager(w4a16_lib):
     ch = Chain(problems, 1)
     ch.plan()
     s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())  # the plan and workspace uploads ran on the current stream
     with torch.cuda.stream(s):
         ch.run(s)
     s.synchronize()

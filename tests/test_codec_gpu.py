@@ -151,6 +151,7 @@ def test_codec_timed_matches_untimed(w4a16_lib, codec):
     y0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.wait_stream(torch.cuda.current_stream())  # the uploads and the NaN fill ran on the current stream
     with torch.cuda.stream(s):
         a.record(s)      # creates the events before their handles are passed on
         b.record(s)

@@ -137,6 +137,7 @@ def test_bitwise_repeatable_and_stream_ordered(w4a16_lib):
     x, codes, scale, mn = workload.random_problem(15, M, N, K, outliers=True)
     xd, packed = _device_inputs(x, codes, scale, mn)
     s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())  # the uploads ran on the current stream
     ys = []
     with torch.cuda.stream(s):
         for _ in range(3):
@@ -159,6 +160,7 @@ def test_timed_launch_matches_and_times_the_kernel(w4a16_lib):
     y0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     y1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.wait_stream(torch.cuda.current_stream())  # the uploads and the NaN fill ran on the current stream
     with torch.cuda.stream(s):
         a.record(s)
         b.record(s)

@@ -137,6 +137,7 @@ def test_kv_timed_matches_untimed(w4a16_lib):
     o1 = torch.full((Hq, 128), float("nan"), dtype=torch.float32, device=DEV)
     s = torch.cuda.Stream(device=DEV)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.wait_stream(torch.cuda.current_stream())  # the uploads and the NaN fill ran on the current stream
     with torch.cuda.stream(s):
         a.record(s)
         b.record(s)
