@@ -99,26 +99,26 @@ def gemv_bytes(M, N, K, codec="q4"):
 # a 1 GiB device copy; kept only while the kernel is unchanged since the
 # counters were taken.
 TRAFFIC = {
-    # (16,752.39 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
-    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_361_216,
-    # (2,137,331.94 KiB x 2.000 + 11,904.06 KiB x 1.000) per dispatch
-    ("llama8b_step", 1, "chain_kernel<1, 24, 8>"): 4_389_327_294,
-    # the 70B step: (65,464.47 KiB x 2.000 + 84.0 KiB x 1.000) per dispatch
-    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_153_625,
-    # weight-code variants: (15,086.10 / 20,092.59 / 28,408.95 KiB x 2.000 + 52.0 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_948_753,
-    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_201_770,
-    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_233_211,
-    # verify batches: (16,941.37 / 17,198.15 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
-    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_899_792,
-    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_630_460,
-    # the 70B step at M = 8: (63,845.30 KiB x 2.000 + 810.67 KiB x 1.000)
-    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_775,
-    # palettised codes: (13,616.53 KiB x 2.000 + 52.0 KiB x 1.000)
-    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_939_140,
-    # KV-cache attention, split pass: (41,447.22 / 48,741.68 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
-    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_146_262,
-    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_668_894,
+    # (16,750.70 KiB FETCH_SIZE x 2.000 + 52.0 KiB WRITE_SIZE x 1.000) per dispatch
+    ("llama8b_step", 1, "gemv_kernel<1, 1, 1>"): 34_358_684,
+    # (2,137,088.35 KiB x 2.000 + 11,904.06 KiB x 1.000) per dispatch
+    ("llama8b_step", 1, "chain_kernel<1, 24, 8>"): 4_388_946_709,
+    # the 70B step: (65,464.03 KiB x 2.000 + 84.0 KiB x 1.000) per dispatch
+    ("llama70b_step", 1, "gemv_kernel<1, 1, 1>"): 134_156_358,
+    # weight-code variants: (15,084.23 / 20,094.84 / 28,408.95 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<1, 1, 1, 1>"): 30_945_743,
+    ("llama8b_step", 1, "codec_kernel<2, 1, 1, 1>"): 41_207_479,
+    ("llama8b_step", 1, "codec_kernel<3, 1, 1, 1>"): 58_234_777,
+    # verify batches: (16,946.12 / 17,196.90 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
+    ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_910_459,
+    ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_628_853,
+    # the 70B step at M = 8: (63,843.49 KiB x 2.000 + 810.67 KiB x 1.000)
+    ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_595,
+    # palettised codes: (13,617.78 KiB x 2.000 + 52.0 KiB x 1.000)
+    ("llama8b_step", 1, "codec_kernel<4, 1, 1, 1>"): 27_942_458,
+    # KV-cache attention, split pass: (41,442.61 / 48,739.67 KiB x 2.000 + 1,235.0 / 828.75 KiB x 1.000)
+    ("llama8b_kv_int8", 1, "kv_attn_kernel<8, 4>"): 86_139_115,
+    ("llama8b_kv_int4", 1, "kv_attn_kernel<4, 4>"): 100_667_484,
 }
 
 
