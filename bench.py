@@ -73,6 +73,8 @@ WORKLOAD_TEXT = {
                       "plain N(0,1) activations",
     "llama70b_step": "llama70b_step: 80 Llama-3-70B-shaped layers x (qkv 8192->10240, o 8192->8192, "
                      "gate_up 8192->57344, down 28672->8192)",
+    "llama70b_tp8": "llama70b_tp8: one GPU's share of the 80-layer 70B step under 8-way tensor parallelism "
+                    "(qkv 8192->1280, o 1024->8192, gate_up 8192->7168, down 3584->8192)",
 }
 
 
@@ -112,6 +114,8 @@ TRAFFIC = {
     # verify batches: (16,946.12 / 17,196.90 KiB x 2.000 + 200.0 / 400.0 KiB x 1.000)
     ("llama8b_verify", 4, "gemv_kernel<4, 1, 1>"): 34_910_459,
     ("llama8b_verify", 8, "gemv_kernel<8, 1, 1>"): 35_628_853,
+    # one GPU's share of the 70B step at 8-way tensor parallelism: (10,126.34 KiB x 2.000 + 35.33 KiB x 1.000)
+    ("llama70b_tp8", 1, "gemv_kernel<1, 1, 1>"): 20_774_930,
     # the 70B step at M = 8: (63,843.49 KiB x 2.000 + 810.67 KiB x 1.000)
     ("llama70b_step", 8, "gemv_kernel<8, 1, 1>"): 131_581_595,
     # palettised codes: (13,617.78 KiB x 2.000 + 52.0 KiB x 1.000)

@@ -257,6 +257,18 @@ def test_llama8b_step_sampled(w4a16_lib, layer, proj):
     check(y[:, rows], y_ref, B, f"llama8b_step layer {layer} proj {proj}", inputs=(x, codes, scale, mn), rows=rows)
 
 
+@pytest.mark.parametrize("layer", [0, 79])
+@pytest.mark.parametrize("proj", [0, 1, 2, 3])
+def test_llama70b_tp8_shard(w4a16_lib, layer, proj):
+    """One GPU's share of the 70B layer at 8-way tensor parallelism, in the
+    launch the bench times: o's K of 1024 is 32 groups, half a wave's lanes."""
+    x, codes, scale, mn = workload.gemv_inputs("llama70b_tp8", layer, proj, 1)
+    print(f"[shape] llama70b_tp8 layer={layer} proj={proj} N={codes.shape[0]} K={x.shape[1]}", flush=True)
+    y = run_gpu(x, codes, scale, mn)
+    y_ref, B = oracle.gemv(x, codes, scale, mn, threads=8)
+    check(y, y_ref, B, f"llama70b_tp8 layer {layer} proj {proj}", inputs=(x, codes, scale, mn))
+
+
 @pytest.mark.parametrize("M", [1, 8])
 @pytest.mark.parametrize("proj", [0, 1, 2, 3])
 def test_llama70b_sampled(w4a16_lib, M, proj):

@@ -48,7 +48,7 @@ def test_outlier_count_per_row(K):
 
 def test_named_workloads():
     names = list(workload.WORKLOADS)
-    assert names == ["gemv4096", "llama8b_layer", "llama8b_step", "llama8b_verify", "llama70b_step"]
+    assert names == ["gemv4096", "llama8b_layer", "llama8b_step", "llama8b_verify", "llama70b_step", "llama70b_tp8"]
     step = list(workload.workload_gemvs("llama8b_step"))
     assert len(step) == 128
     nweights = sum(p.N * p.K for _, _, p, _ in step)
@@ -56,6 +56,14 @@ def test_named_workloads():
     big = list(workload.workload_gemvs("llama70b_step", M=1))
     assert len(big) == 320
     assert sum(p.N * p.K for _, _, p, _ in big) == 68_451_041_280
+    # 8-way tensor parallelism: every matrix of the 70B layer is split eight ways,
+    # qkv and gate_up along N, o and down along K
+    shard = list(workload.workload_gemvs("llama70b_tp8", M=1))
+    assert len(shard) == 320
+    assert sum(p.N * p.K for _, _, p, _ in shard) * 8 == 68_451_041_280
+    for full, part in zip(workload.LLAMA70B_LAYER, workload.LLAMA70B_TP8_SHARD):
+        assert full.name == part.name
+        assert (part.N * 8, part.K) == (full.N, full.K) or (part.N, part.K * 8) == (full.N, full.K)
 
 
 def test_gemv_inputs_shapes():

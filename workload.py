@@ -54,6 +54,18 @@ LLAMA70B_LAYER = (
 )
 
 
+# One GPU's share of the 70B layer under 8-way tensor parallelism: the fused
+# qkv and gate_up matrices split along their output rows (column-parallel),
+# o and down along their input features (row-parallel, each GPU a 1/8 slice
+# of K, summed across GPUs afterwards).
+LLAMA70B_TP8_SHARD = (
+    Proj("qkv", 8192, 1280),
+    Proj("o", 1024, 8192),
+    Proj("gate_up", 8192, 7168),
+    Proj("down", 3584, 8192),
+)
+
+
 @dataclass(frozen=True)
 class Workload:
     wid: int             # numeric id used in the seed key
@@ -75,6 +87,8 @@ WORKLOADS = {
     "llama8b_verify": Workload(3, "llama8b_verify", 1, LLAMA8B_LAYER, (4, 8), False),
     # 80 Llama-3-70B-shaped layers, M = 1 and M = 8, with activation outliers
     "llama70b_step": Workload(4, "llama70b_step", 80, LLAMA70B_LAYER, (1, 8), True),
+    # one GPU's share of that step under 8-way tensor parallelism, M = 1
+    "llama70b_tp8": Workload(5, "llama70b_tp8", 80, LLAMA70B_TP8_SHARD, (1,), True),
 }
 
 
